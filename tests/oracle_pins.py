@@ -1,0 +1,431 @@
+"""Pins of the CPU oracle to facts outside the oracle itself.
+
+Each pin is a function ``pin(o)`` that raises AssertionError when the oracle
+``o`` disagrees with something the pages or the mathematics fix: exact sums
+and products with ``fractions.Fraction`` or Python integers on small inputs,
+closed forms, the worked examples in ``tests/golden/`` (derived by hand from
+the TVM TIRx page "reduction -> sm100_packed", section "Algorithm"),
+special values, and exhaustive checks of the 16-bit decoders against numpy's
+binary16 and torch's bfloat16.
+
+The same pins run against the real oracle (test_oracle.py) and against
+deliberately broken copies of it (test_oracle_mutants.py), which shows each
+plausible mistake fails at least one of them.
+"""
+from __future__ import annotations
+
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+U32 = 1 << 32
+
+
+def f32(v) -> np.float32:
+    return np.float32(v)
+
+
+def bits(v) -> int:
+    return int(np.array([v], dtype=np.float32).view(np.uint32)[0])
+
+
+def exact_sum(values) -> Fraction:
+    return sum((Fraction(float(v)) for v in values), Fraction(0))
+
+
+def exact_prod(values) -> Fraction:
+    p = Fraction(1)
+    for v in values:
+        p *= Fraction(float(v))
+    return p
+
+
+def load_page_order_cases():
+    """Parse tests/golden/page_order_sum.txt into dict records."""
+    cases = []
+    with open(os.path.join(GOLDEN, "page_order_sum.txt")) as fh:
+        for line in fh:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            name, n, entries, accum, old, expected, why = (
+                p.strip() for p in line.split(";", 6))
+            x = np.zeros(int(n), np.float32)
+            for e in entries.split():
+                i, v = e.split("=")
+                x[int(i)] = np.float32(float(v))
+            cases.append(dict(name=name, x=x, accum=bool(int(accum)),
+                              old=float(old), expected=np.float32(float(expected)),
+                              why=why))
+    return cases
+
+
+# ---------------------------------------------------------------------------
+# sum
+# ---------------------------------------------------------------------------
+
+def pin_sum_bruteforce(o):
+    """S and A against exact rational sums on small random inputs."""
+    rng = np.random.default_rng(11)
+    for n in (1, 2, 3, 7, 8, 9, 31, 32, 33, 64, 257):
+        mag = 10.0 ** rng.uniform(-3, 3, n)
+        x = (rng.uniform(-1, 1, n) * mag).astype(np.float32)
+        old = float(np.float32(rng.uniform(-10, 10)))
+        for accum in (False, True):
+            terms = list(x) + ([np.float32(old)] if accum else [])
+            ex = exact_sum(terms)
+            ab = sum((abs(Fraction(float(v))) for v in terms), Fraction(0))
+            s, a = o.sum_f32(x, accum, old)
+            assert abs(Fraction(s) - ex) <= Fraction(1, 10**15) * ab, (n, s, ex)
+            assert abs(Fraction(a) - ab) <= Fraction(1, 10**15) * ab, (n, a, ab)
+
+
+def pin_sum_integer_exact(o):
+    """Integer-valued inputs: every partial sum is exact, so S is exact."""
+    rng = np.random.default_rng(12)
+    x = rng.integers(-1000, 1001, 5000).astype(np.float32)
+    s, a = o.sum_f32(x)
+    assert s == float(np.sum(x.astype(np.int64)))
+    assert a == float(np.sum(np.abs(x.astype(np.int64))))
+
+
+def pin_sum_arithmetic_series(o):
+    """1 + 2 + ... + n = n (n + 1) / 2."""
+    for n in (1, 8, 32, 4096, 100000):
+        x = np.arange(1, n + 1, dtype=np.float32)
+        s, a = o.sum_f32(x)
+        assert s == n * (n + 1) / 2 and a == s, (n, s)
+
+
+def pin_sum_cancellation(o):
+    """The compensation must recover a term a plain double sum loses."""
+    big = float(2 ** 60)
+    for x in ([big, 1.0, -big], [1.0, big, -big], [-big, 1.0, big]):
+        s, a = o.sum_f32(np.array(x, np.float32))
+        assert s == 1.0, (x, s)
+        assert a == 2 * big + 1.0 or a == 2 * big  # A needs no compensation
+
+
+def pin_sum_accum(o):
+    """accum folds the old dst into the result and into A."""
+    s, a = o.sum_f32(np.array([1.0, 2.0], np.float32), True, 3.25)
+    assert (s, a) == (6.25, 6.25)
+    s, a = o.sum_f32(np.array([1.0, 2.0], np.float32), True, -3.25)
+    assert (s, a) == (-0.25, 6.25)
+    s, a = o.sum_f32(np.array([1.0, 2.0], np.float32), False, 100.0)
+    assert (s, a) == (3.0, 3.0)
+
+
+def pin_sum_empty(o):
+    """An empty vector computes nothing, even under accum."""
+    assert o.sum_f32(np.zeros(0, np.float32)) is None
+    assert o.sum_f32(np.zeros(0, np.float32), True, 3.25) is None
+
+
+def pin_sum_nonfinite(o):
+    """IEEE classes propagate: inf + 1 = inf, inf + -inf = NaN."""
+    inf = float("inf")
+    assert o.sum_f32(np.array([inf, 1], np.float32))[0] == inf
+    assert o.sum_f32(np.array([-inf, 5], np.float32))[0] == -inf
+    assert math.isnan(o.sum_f32(np.array([inf, -inf], np.float32))[0])
+    assert math.isnan(o.sum_f32(np.array([float("nan"), 1], np.float32))[0])
+
+
+def pin_sum_subnormal(o):
+    """Subnormals are not flushed: 2^-149 + 2^-149 + 2^-148 = 2^-147."""
+    x = np.array([2.0 ** -149, 2.0 ** -149, 2.0 ** -148], np.float32)
+    assert x[0] != 0
+    s, _ = o.sum_f32(x)
+    assert s == 2.0 ** -147
+
+
+# ---------------------------------------------------------------------------
+# max / min
+# ---------------------------------------------------------------------------
+
+def pin_maxmin_bruteforce(o):
+    """Against Python's max / min, with the extreme at the ends and inside."""
+    rng = np.random.default_rng(13)
+    for n in (1, 2, 7, 8, 9, 33, 1000):
+        for where in {0, n // 2, n - 1}:
+            x = rng.uniform(-1, 1, n).astype(np.float32)
+            x[where] = 7.5
+            assert o.max_f32(x) == max(x.tolist()) == 7.5
+            x[where] = -7.5
+            assert o.min_f32(x) == min(x.tolist()) == -7.5
+            y = rng.uniform(-1, 1, n).astype(np.float32)
+            assert o.max_f32(y) == max(y.tolist())
+            assert o.min_f32(y) == min(y.tolist())
+
+
+def pin_maxmin_nan_policy(o):
+    """maxNum / minNum: NaN is ignored unless every operand is NaN."""
+    nan = float("nan")
+    assert o.max_f32(np.array([nan, 1, nan], np.float32)) == 1
+    assert o.min_f32(np.array([1, nan, -3], np.float32)) == -3
+    assert o.max_f32(np.array([nan, -2], np.float32)) == -2
+    assert math.isnan(o.max_f32(np.array([nan, nan], np.float32)))
+    assert math.isnan(o.min_f32(np.array([nan], np.float32)))
+    assert o.max_f32(np.array([nan], np.float32), True, 2.0) == 2
+    assert o.min_f32(np.array([4.0], np.float32), True, nan) == 4
+
+
+def pin_maxmin_accum(o):
+    """accum includes the old dst: max(3.25, x) over x in [-1, 1] is 3.25."""
+    rng = np.random.default_rng(14)
+    x = rng.uniform(-1, 1, 100).astype(np.float32)
+    assert o.max_f32(x, True, 3.25) == np.float32(3.25)
+    assert o.min_f32(x, True, 3.25) == min(x.tolist())
+    assert o.min_f32(x, True, -5.0) == -5.0
+    assert o.max_f32(x, False, 3.25) == max(x.tolist())
+
+
+def pin_maxmin_empty(o):
+    """n == 0 leaves the destination untouched, even under accum."""
+    e = np.zeros(0, np.float32)
+    assert o.max_f32(e, False, 42.0) == 42.0
+    assert o.min_f32(e, True, -42.0) == -42.0
+
+
+def pin_maxmin_special(o):
+    """Subnormals survive bit-exactly; infinities order normally."""
+    t = 2.0 ** -149
+    x = np.array([t, -t, 0.0], np.float32)
+    assert bits(o.max_f32(x)) == bits(t)
+    assert bits(o.min_f32(x)) == bits(-t)
+    inf = float("inf")
+    x = np.array([-inf, 1, 0.5], np.float32)
+    assert o.max_f32(x) == 1 and o.min_f32(x) == -inf
+    assert o.max_f32(np.array([inf], np.float32)) == inf
+    assert o.max_f32(np.array([0.25], np.float32)) == np.float32(0.25)
+
+
+# ---------------------------------------------------------------------------
+# the page's single-precision summation order
+# ---------------------------------------------------------------------------
+
+def pin_page_sum_golden(o):
+    """Hand-derived worked examples of the page's order (tests/golden)."""
+    for c in load_page_order_cases():
+        got = o.page_sum_f32(c["x"], c["accum"], c["old"])
+        assert bits(got) == bits(c["expected"]), (c["name"], got, c["expected"])
+
+
+def pin_page_sum_integer_exact(o):
+    """Small integers: every order is exact, so the result is the exact sum."""
+    rng = np.random.default_rng(15)
+    for n in (1, 5, 8, 9, 16, 17, 31, 32, 33, 100, 1000):
+        x = rng.integers(-100, 101, n).astype(np.float32)
+        assert o.page_sum_f32(x) == float(np.sum(x.astype(np.int64))), n
+        assert o.page_sum_f32(x, True, 7.0) == 7.0 + float(np.sum(x.astype(np.int64)))
+
+
+def pin_page_sum_error_bound(o):
+    """Random data: within the worst-case bound of an order of depth n/8 + 4."""
+    rng = np.random.default_rng(16)
+    for n in (8, 9, 15, 64, 100, 1000, 4099):
+        x = rng.uniform(-1, 1, n).astype(np.float32)
+        ex = exact_sum(x)
+        ab = sum(abs(Fraction(float(v))) for v in x)
+        depth = n // 8 + 4
+        got = o.page_sum_f32(x)
+        assert abs(Fraction(float(got)) - ex) <= depth * Fraction(1, 2**24) * ab
+
+
+# ---------------------------------------------------------------------------
+# rows
+# ---------------------------------------------------------------------------
+
+def pin_rows_bruteforce(o):
+    """Each row of an ld-padded matrix reduces to its own brute-force value;
+    the NaN padding between n and ld never enters."""
+    rng = np.random.default_rng(17)
+    rows, n, ld = 5, 13, 16
+    m = np.full((rows, ld), np.nan, np.float32)
+    m[:, :n] = rng.uniform(-1, 1, (rows, n)).astype(np.float32)
+    old = rng.uniform(-1, 1, rows).astype(np.float32)
+    s, a = o.rows_sum_f32(m, rows, n, ld)
+    s2, _ = o.rows_sum_f32(m, rows, n, ld, True, old)
+    mx = o.rows_max_f32(m, rows, n, ld)
+    mn = o.rows_min_f32(m, rows, n, ld, True, old)
+    for r in range(rows):
+        row = m[r, :n]
+        ex = exact_sum(row)
+        ab = sum(abs(Fraction(float(v))) for v in row)
+        assert abs(Fraction(s[r]) - ex) <= Fraction(1, 10**15) * ab
+        assert abs(Fraction(a[r]) - ab) <= Fraction(1, 10**15) * ab
+        ex2 = ex + Fraction(float(old[r]))
+        assert abs(Fraction(s2[r]) - ex2) <= Fraction(1, 10**14) * (ab + 1)
+        assert mx[r] == max(row.tolist())
+        assert mn[r] == min(row.tolist() + [float(old[r])])
+
+
+def pin_rows_page_golden(o):
+    """Rows reproduce the golden page-order cases row by row, with ld > n."""
+    cases = [c for c in load_page_order_cases() if c["x"].size == 8
+             and not c["accum"]]
+    ld = 11
+    m = np.full((len(cases), ld), np.nan, np.float32)
+    for r, c in enumerate(cases):
+        m[r, :8] = c["x"]
+    got = o.rows_page_sum_f32(m, len(cases), 8, ld)
+    for r, c in enumerate(cases):
+        assert bits(got[r]) == bits(c["expected"]), c["name"]
+
+
+def pin_rows_empty(o):
+    """rows == 0 or n == 0 leaves every destination untouched."""
+    m = np.ones((3, 4), np.float32)
+    sentinel = np.full(3, 9.5, np.float32)
+    assert o.rows_sum_f32(m, 3, 0, 4) is None
+    assert o.rows_sum_f32(m, 0, 4, 4) is None
+    assert (o.rows_max_f32(m, 3, 0, 4, dst=sentinel) == 9.5).all()
+    assert (o.rows_min_f32(m, 3, 0, 4, True, dst=sentinel) == 9.5).all()
+    assert (o.rows_page_sum_f32(m, 3, 0, 4, dst=sentinel) == 9.5).all()
+
+
+# ---------------------------------------------------------------------------
+# colprod
+# ---------------------------------------------------------------------------
+
+def pin_colprod_f32_bruteforce(o):
+    """The TCOLPROD example shape (16 x 16 -> 1 x 16) against exact products,
+    plus a non-square ld-padded tile (R != C catches a transposed index)."""
+    rng = np.random.default_rng(18)
+    t = rng.uniform(0.5, 1.5, (16, 16)).astype(np.float32)
+    got = o.colprod_f32(t, 16, 16, 16)
+    for j in range(16):
+        ex = exact_prod(t[:, j])
+        assert abs(Fraction(got[j]) - ex) <= Fraction(1, 10**14) * abs(ex)
+    R, C, ld = 5, 7, 9
+    m = np.full((R, ld), np.nan, np.float32)
+    m[:, :C] = rng.uniform(-2, 2, (R, C)).astype(np.float32)
+    got = o.colprod_f32(m, R, C, ld)
+    for j in range(C):
+        ex = exact_prod(m[:, j])
+        assert abs(Fraction(got[j]) - ex) <= Fraction(1, 10**14) * abs(ex)
+
+
+def pin_colprod_f32_closed_forms(o):
+    """Ones give exactly 1; powers of two are exact; zeros carry the XOR of
+    the signs."""
+    assert (o.colprod_f32(np.ones((100, 3), np.float32), 100, 3, 3) == 1).all()
+    e = np.array([[2.0, 0.5, -4.0], [2.0, 0.25, 8.0], [-2.0, 4.0, 0.125]],
+                 np.float32)
+    assert o.colprod_f32(e, 3, 3, 3).tolist() == [-8.0, 0.5, -4.0]
+    z = np.array([[-1.0, -1.0], [0.0, -0.0], [2.0, 3.0]], np.float32)
+    got = o.colprod_f32(z, 3, 2, 2)
+    assert got[0] == 0 and math.copysign(1, got[0]) == -1
+    assert got[1] == 0 and math.copysign(1, got[1]) == 1
+
+
+def pin_colprod_empty(o):
+    """R == 0 or C == 0: early return, dst untouched (no empty product 1)."""
+    t = np.ones((4, 4), np.float32)
+    for (R, C) in ((0, 4), (4, 0), (0, 0)):
+        d = o.colprod_f32(t, R, C, 4, dst=np.full(4, 7.0))
+        assert (d == 7.0).all(), (R, C)
+        d = o.colprod_i32(t.astype(np.int32), R, C, 4,
+                          dst=np.full(4, 7, np.int32))
+        assert (d == 7).all(), (R, C)
+        h = t.astype(np.float16).view(np.uint16)
+        assert (o.colprod_f16(h, R, C, 4, dst=np.full(4, 7.0)) == 7.0).all()
+        assert (o.colprod_bf16(h, R, C, 4, dst=np.full(4, 7.0)) == 7.0).all()
+
+
+def _same_float(a: float, b: float) -> bool:
+    if math.isnan(a) or math.isnan(b):
+        return math.isnan(a) and math.isnan(b)
+    return a == b and math.copysign(1, a) == math.copysign(1, b)
+
+
+def pin_f16_decode_exhaustive(o):
+    """All 65536 binary16 patterns decode as numpy's float16 does."""
+    allbits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ref = allbits.view(np.float16).astype(np.float64)
+    for b in range(0, 65536):
+        assert _same_float(o.f16_to_f64(b), float(ref[b])), hex(b)
+
+
+def pin_bf16_decode_exhaustive(o):
+    """All 65536 bfloat16 patterns decode as torch's bfloat16 does, and a
+    few values known from the format's definition."""
+    import torch
+    allbits = torch.arange(65536, dtype=torch.int32).to(torch.int16)
+    ref = allbits.view(torch.bfloat16).to(torch.float64).tolist()
+    for b in range(0, 65536):
+        assert _same_float(o.bf16_to_f64(b), ref[b]), hex(b)
+    known = {0x3F80: 1.0, 0xC000: -2.0, 0x4049: 3.140625, 0x0000: 0.0,
+             0x7F80: float("inf"), 0x0001: 2.0 ** -133,
+             0x7F7F: (2 - 2.0 ** -7) * 2.0 ** 127}
+    for b, v in known.items():
+        assert o.bf16_to_f64(b) == v, hex(b)
+
+
+def pin_colprod_16bit_bruteforce(o):
+    """fp16 / bf16 tiles against exact products of independently decoded
+    values (numpy float16, torch bfloat16)."""
+    import torch
+    rng = np.random.default_rng(19)
+    v = rng.uniform(0.5, 1.5, (16, 16)).astype(np.float32)
+    h = v.astype(np.float16)
+    got = o.colprod_f16(h.view(np.uint16), 16, 16, 16)
+    for j in range(16):
+        ex = exact_prod(h[:, j].astype(np.float64))
+        assert abs(Fraction(got[j]) - ex) <= Fraction(1, 10**14) * abs(ex)
+    b = torch.from_numpy(v).to(torch.bfloat16)
+    bb = b.view(torch.int16).numpy().view(np.uint16)
+    got = o.colprod_bf16(bb, 16, 16, 16)
+    bd = b.to(torch.float64).numpy()
+    for j in range(16):
+        ex = exact_prod(bd[:, j])
+        assert abs(Fraction(got[j]) - ex) <= Fraction(1, 10**14) * abs(ex)
+
+
+def _i32(v: int) -> int:
+    v %= U32
+    return v - U32 if v >= 1 << 31 else v
+
+
+def pin_colprod_i32_bruteforce(o):
+    """Full-range int32 against Python big-int products modulo 2^32."""
+    rng = np.random.default_rng(20)
+    R, C, ld = 16, 13, 16
+    t = rng.integers(-2**31, 2**31, (R, ld), dtype=np.int64).astype(np.int32)
+    got = o.colprod_i32(t, R, C, ld)
+    for j in range(C):
+        p = 1
+        for i in range(R):
+            p *= int(t[i, j])
+        assert int(got[j]) == _i32(p), j
+
+
+def pin_colprod_i32_closed_forms(o):
+    """(-1)^R, 3^R mod 2^32, 2^R = 0 for R >= 32, INT_MIN * -1 = INT_MIN."""
+    for R in (7, 8):
+        got = o.colprod_i32(np.full((R, 2), -1, np.int32), R, 2, 2)
+        assert got.tolist() == [(-1) ** R] * 2
+    got = o.colprod_i32(np.full((4096, 3), 3, np.int32), 4096, 3, 3)
+    assert got.tolist() == [_i32(pow(3, 4096, U32))] * 3
+    got = o.colprod_i32(np.full((40, 1), 2, np.int32), 40, 1, 1)
+    assert got.tolist() == [0]
+    got = o.colprod_i32(np.array([[-2**31], [-1]], np.int32), 2, 1, 1)
+    assert got.tolist() == [-2**31]
+
+
+PINS = [
+    pin_sum_bruteforce, pin_sum_integer_exact, pin_sum_arithmetic_series,
+    pin_sum_cancellation, pin_sum_accum, pin_sum_empty, pin_sum_nonfinite,
+    pin_sum_subnormal,
+    pin_maxmin_bruteforce, pin_maxmin_nan_policy, pin_maxmin_accum,
+    pin_maxmin_empty, pin_maxmin_special,
+    pin_page_sum_golden, pin_page_sum_integer_exact, pin_page_sum_error_bound,
+    pin_rows_bruteforce, pin_rows_page_golden, pin_rows_empty,
+    pin_colprod_f32_bruteforce, pin_colprod_f32_closed_forms,
+    pin_colprod_empty, pin_f16_decode_exhaustive, pin_bf16_decode_exhaustive,
+    pin_colprod_16bit_bruteforce, pin_colprod_i32_bruteforce,
+    pin_colprod_i32_closed_forms,
+]
