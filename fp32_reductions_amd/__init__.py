@@ -1,0 +1,218 @@
+"""fp32_reductions_amd -- Python binding of libreduce (gfx950 HIP kernels).
+
+Thin ctypes layer over the C ABI in ``include/reduce.h``: it checks that
+torch tensors have the dtype, device and extent an entry point expects,
+passes their device pointers and the current HIP stream, and turns a
+non-zero status into ``ReduceError``.  Every step of the reduction runs in
+the HIP kernels of ``libreduce.so``; there is no CPU fallback.  Importing
+this package raises if the library has not been built
+(``python -m fp32_reductions_amd.build``).
+
+Names follow the C ABI:
+
+    sum_f32 / max_f32 / min_f32 (x, out, accum=False, stream=None)
+    sum_f32_atomic / max_f32_atomic / min_f32_atomic (same)
+    sum_rows_f32 / max_rows_f32 / min_rows_f32 (x, out, n=None, accum=False)
+    colprod_f32 / colprod_f16 / colprod_bf16 / colprod_i32 (src, out, C=None)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIBRARY = os.path.join(_PKG, "libreduce.so")
+
+RED_OK, RED_ERR_INVALID, RED_ERR_ALIGN, RED_ERR_NOMEM, RED_ERR_HIP = range(5)
+
+
+class ReduceError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__("%s: %s (status %d)" % (where, status_str(status), status))
+
+
+if not os.path.exists(LIBRARY):
+    raise ImportError(
+        "libreduce.so is not built at %s; run "
+        "'python -m fp32_reductions_amd.build' (hipcc, gfx950)" % LIBRARY)
+
+_lib = ctypes.CDLL(LIBRARY)
+
+_P, _SZ, _I = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
+_SIGS = {
+    "red_sum_f32": [_P, _SZ, _P, _I, _P],
+    "red_max_f32": [_P, _SZ, _P, _I, _P],
+    "red_min_f32": [_P, _SZ, _P, _I, _P],
+    "red_sum_f32_atomic": [_P, _SZ, _P, _I, _P],
+    "red_max_f32_atomic": [_P, _SZ, _P, _I, _P],
+    "red_min_f32_atomic": [_P, _SZ, _P, _I, _P],
+    "red_sum_rows_f32": [_P, _SZ, _SZ, _SZ, _P, _I, _P],
+    "red_max_rows_f32": [_P, _SZ, _SZ, _SZ, _P, _I, _P],
+    "red_min_rows_f32": [_P, _SZ, _SZ, _SZ, _P, _I, _P],
+    "red_colprod_f32": [_P, _SZ, _SZ, _SZ, _P, _P],
+    "red_colprod_f16": [_P, _SZ, _SZ, _SZ, _P, _P],
+    "red_colprod_bf16": [_P, _SZ, _SZ, _SZ, _P, _P],
+    "red_colprod_i32": [_P, _SZ, _SZ, _SZ, _P, _P],
+}
+for _name, _args in _SIGS.items():
+    _fn = getattr(_lib, _name)
+    _fn.argtypes = _args
+    _fn.restype = _I
+_lib.red_status_str.argtypes = [_I]
+_lib.red_status_str.restype = ctypes.c_char_p
+_lib.red_abi_version.argtypes = []
+_lib.red_abi_version.restype = _I
+
+EXPORTS = tuple(_SIGS) + ("red_status_str", "red_abi_version")
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libreduce (raw C ABI, for callers holding raw pointers)."""
+    return _lib
+
+
+def status_str(status: int) -> str:
+    return _lib.red_status_str(status).decode()
+
+
+def abi_version() -> int:
+    return _lib.red_abi_version()
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def _check(status: int, where: str) -> None:
+    if status != RED_OK:
+        raise ReduceError(status, where)
+
+
+def _need(t: torch.Tensor, dtype, what: str) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % what)
+    if t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (what, dtype, t.dtype))
+    if t.device.type != "cuda":
+        raise ValueError("%s must be a device (cuda/HIP) tensor" % what)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % what)
+
+
+# ---------------------------------------------------------------------------
+# 1-D vector -> scalar
+# ---------------------------------------------------------------------------
+
+def _reduce1d(name: str, x, out, accum, stream):
+    _need(x, torch.float32, "x")
+    _need(out, torch.float32, "out")
+    if out.numel() < 1:
+        raise ValueError("out needs one element")
+    _check(getattr(_lib, name)(x.data_ptr(), x.numel(), out.data_ptr(),
+                               int(bool(accum)), _stream(stream)), name)
+    return out
+
+
+def sum_f32(x, out, accum=False, stream=None):
+    """out[0] = [out[0] +] sum(x), x any contiguous fp32 device tensor."""
+    return _reduce1d("red_sum_f32", x, out, accum, stream)
+
+
+def max_f32(x, out, accum=False, stream=None):
+    return _reduce1d("red_max_f32", x, out, accum, stream)
+
+
+def min_f32(x, out, accum=False, stream=None):
+    return _reduce1d("red_min_f32", x, out, accum, stream)
+
+
+def sum_f32_atomic(x, out, accum=False, stream=None):
+    return _reduce1d("red_sum_f32_atomic", x, out, accum, stream)
+
+
+def max_f32_atomic(x, out, accum=False, stream=None):
+    return _reduce1d("red_max_f32_atomic", x, out, accum, stream)
+
+
+def min_f32_atomic(x, out, accum=False, stream=None):
+    return _reduce1d("red_min_f32_atomic", x, out, accum, stream)
+
+
+# ---------------------------------------------------------------------------
+# segmented rows
+# ---------------------------------------------------------------------------
+
+def _rows(name: str, x, out, n, accum, stream):
+    _need(x, torch.float32, "x")
+    _need(out, torch.float32, "out")
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D (rows, ld)")
+    rows, ld = x.shape
+    n = ld if n is None else int(n)
+    if not 0 <= n <= ld:
+        raise ValueError("need 0 <= n <= ld")
+    if out.numel() < rows:
+        raise ValueError("out needs one element per row")
+    _check(getattr(_lib, name)(x.data_ptr(), rows, n, ld, out.data_ptr(),
+                               int(bool(accum)), _stream(stream)), name)
+    return out
+
+
+def sum_rows_f32(x, out, n=None, accum=False, stream=None):
+    """out[r] = [out[r] +] sum(x[r, :n]) for a row-major (rows, ld) x."""
+    return _rows("red_sum_rows_f32", x, out, n, accum, stream)
+
+
+def max_rows_f32(x, out, n=None, accum=False, stream=None):
+    return _rows("red_max_rows_f32", x, out, n, accum, stream)
+
+
+def min_rows_f32(x, out, n=None, accum=False, stream=None):
+    return _rows("red_min_rows_f32", x, out, n, accum, stream)
+
+
+# ---------------------------------------------------------------------------
+# column product
+# ---------------------------------------------------------------------------
+
+def _colprod(name: str, src, out, C, dtype, stream):
+    _need(src, dtype, "src")
+    _need(out, dtype, "out")
+    if src.dim() != 2:
+        raise ValueError("src must be 2-D (R, ld)")
+    R, ld = src.shape
+    C = ld if C is None else int(C)
+    if not 0 <= C <= ld:
+        raise ValueError("need 0 <= C <= ld")
+    if out.numel() < C:
+        raise ValueError("out needs C elements")
+    _check(getattr(_lib, name)(src.data_ptr(), R, C, ld, out.data_ptr(),
+                               _stream(stream)), name)
+    return out
+
+
+def colprod_f32(src, out, C=None, stream=None):
+    """out[j] = prod_i src[i, j] for j < C (TCOLPROD), fp32."""
+    return _colprod("red_colprod_f32", src, out, C, torch.float32, stream)
+
+
+def colprod_f16(src, out, C=None, stream=None):
+    """binary16 tile (torch.float16); fp32 products rounded once to fp16."""
+    return _colprod("red_colprod_f16", src, out, C, torch.float16, stream)
+
+
+def colprod_bf16(src, out, C=None, stream=None):
+    """bfloat16 tile (torch.bfloat16); fp32 products rounded once to bf16."""
+    return _colprod("red_colprod_bf16", src, out, C, torch.bfloat16, stream)
+
+
+def colprod_i32(src, out, C=None, stream=None):
+    """int32 tile; products modulo 2^32."""
+    return _colprod("red_colprod_i32", src, out, C, torch.int32, stream)

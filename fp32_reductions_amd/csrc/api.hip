@@ -1,0 +1,276 @@
+// api.hip -- the extern "C" entry points declared in include/reduce.h.
+//
+// Every entry point validates its arguments before touching the HIP
+// runtime, returns early (RED_OK, nothing enqueued) for empty input, looks
+// up the device's compute-unit count and, where the kernel needs one, the
+// calling stream's workspace, then enqueues the kernel and returns.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstdlib>
+#include <map>
+#include <mutex>
+#include <utility>
+
+#include "internal.hpp"
+#include "reduce.h"
+
+namespace {
+
+using red::ColType;
+using red::DeviceInfo;
+using red::OpKind;
+using red::Workspace;
+
+// Fixed workspace per (device, stream): partial results and tickets.  The
+// kernels size their grids so that they never need more than this.
+constexpr size_t kPartialBytes = size_t(16) << 20;
+constexpr size_t kTickets = 16384;
+
+std::mutex g_mu;
+std::map<int, DeviceInfo> g_dev;
+std::map<std::pair<int, uintptr_t>, Workspace> g_ws;
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+// (count - 1) * stride + width elements of `elem` bytes fit in size_t.
+bool extent_ok(size_t count, size_t stride, size_t width, size_t elem)
+{
+    size_t span;
+    if (__builtin_mul_overflow(count - 1, stride, &span))
+        return false;
+    if (__builtin_add_overflow(span, width, &span))
+        return false;
+    return !__builtin_mul_overflow(span, elem, &span);
+}
+
+int current_device(int* dev, DeviceInfo* info)
+{
+    if (hipGetDevice(dev) != hipSuccess)
+        return RED_ERR_HIP;
+    std::lock_guard<std::mutex> lock(g_mu);
+    auto it = g_dev.find(*dev);
+    if (it == g_dev.end()) {
+        int cus = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount,
+                                  *dev) != hipSuccess || cus <= 0)
+            return RED_ERR_HIP;
+        it = g_dev.emplace(*dev, DeviceInfo{cus}).first;
+    }
+    *info = it->second;
+    return RED_OK;
+}
+
+// The workspace of (dev, stream), created on first use.  Its tickets are
+// zeroed by a kernel on `stream`, so they are ready before any later kernel
+// on that stream runs.
+int stream_workspace(int dev, hipStream_t stream, Workspace* ws)
+{
+    std::lock_guard<std::mutex> lock(g_mu);
+    const auto key = std::make_pair(dev, (uintptr_t)stream);
+    auto it = g_ws.find(key);
+    if (it != g_ws.end()) {
+        *ws = it->second;
+        return RED_OK;
+    }
+    // Failure injection for tests of the RED_ERR_NOMEM path.
+    const char* fail = std::getenv("RED_TEST_FAIL_ALLOC");
+    if (fail && fail[0] == '1')
+        return RED_ERR_NOMEM;
+    void* base = nullptr;
+    const size_t bytes = kPartialBytes + kTickets * sizeof(unsigned);
+    if (hipMalloc(&base, bytes) != hipSuccess) {
+        (void)hipGetLastError(); // clear the sticky allocation error
+        return RED_ERR_NOMEM;
+    }
+    Workspace w;
+    w.partials = base;
+    w.partial_bytes = kPartialBytes;
+    w.tickets = reinterpret_cast<unsigned*>(static_cast<char*>(base) + kPartialBytes);
+    w.n_tickets = kTickets;
+    if (red::launch_fill_u32(w.tickets, kTickets, 0u, stream) != hipSuccess) {
+        (void)hipFree(base);
+        return RED_ERR_HIP;
+    }
+    g_ws.emplace(key, w);
+    *ws = w;
+    return RED_OK;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? RED_OK : RED_ERR_HIP; }
+
+int check_1d(const float* x, size_t n, const float* out)
+{
+    if (!x || !out)
+        return RED_ERR_INVALID;
+    if (n > SIZE_MAX / sizeof(float))
+        return RED_ERR_INVALID;
+    if (!aligned(x, sizeof(float)) || !aligned(out, sizeof(float)))
+        return RED_ERR_ALIGN;
+    return RED_OK;
+}
+
+int reduce1d(OpKind op, const float* x, size_t n, float* out, int accum,
+             red_stream_t stream)
+{
+    if (n == 0)
+        return RED_OK;
+    int st = check_1d(x, n, out);
+    if (st != RED_OK)
+        return st;
+    int dev;
+    DeviceInfo info;
+    if ((st = current_device(&dev, &info)) != RED_OK)
+        return st;
+    Workspace ws;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    if ((st = stream_workspace(dev, s, &ws)) != RED_OK)
+        return st;
+    return hip_status(red::launch_reduce1d(op, x, n, out, accum, info, ws, s));
+}
+
+int reduce1d_atomic(OpKind op, const float* x, size_t n, float* out, int accum,
+                    red_stream_t stream)
+{
+    if (n == 0)
+        return RED_OK;
+    int st = check_1d(x, n, out);
+    if (st != RED_OK)
+        return st;
+    int dev;
+    DeviceInfo info;
+    if ((st = current_device(&dev, &info)) != RED_OK)
+        return st;
+    return hip_status(red::launch_reduce1d_atomic(
+        op, x, n, out, accum, info, static_cast<hipStream_t>(stream)));
+}
+
+int reduce_rows(OpKind op, const float* x, size_t rows, size_t n, size_t ld,
+                float* out, int accum, red_stream_t stream)
+{
+    if (rows == 0 || n == 0)
+        return RED_OK;
+    if (!x || !out || ld < n || !extent_ok(rows, ld, n, sizeof(float)) ||
+        rows > SIZE_MAX / sizeof(float))
+        return RED_ERR_INVALID;
+    if (!aligned(x, sizeof(float)) || !aligned(out, sizeof(float)))
+        return RED_ERR_ALIGN;
+    int dev;
+    DeviceInfo info;
+    int st = current_device(&dev, &info);
+    if (st != RED_OK)
+        return st;
+    return hip_status(red::launch_rows(op, x, rows, n, ld, out, accum, info,
+                                       static_cast<hipStream_t>(stream)));
+}
+
+int colprod(ColType t, const void* src, size_t R, size_t C, size_t ld,
+            void* dst, red_stream_t stream)
+{
+    if (R == 0 || C == 0)
+        return RED_OK;
+    const size_t es = red::colprod_elem_size(t);
+    if (!src || !dst || ld < C || !extent_ok(R, ld, C, es) ||
+        C > SIZE_MAX / sizeof(float))
+        return RED_ERR_INVALID;
+    // A launch holds at most 2^32 - 1 work-items per grid dimension.
+    const size_t cols_per_wg = 64 * (16 / es);
+    if ((C + cols_per_wg - 1) / cols_per_wg >= (size_t(1) << 24))
+        return RED_ERR_INVALID;
+    if (!aligned(src, es) || !aligned(dst, es))
+        return RED_ERR_ALIGN;
+    int dev;
+    DeviceInfo info;
+    int st = current_device(&dev, &info);
+    if (st != RED_OK)
+        return st;
+    Workspace ws;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    if ((st = stream_workspace(dev, s, &ws)) != RED_OK)
+        return st;
+    const red::ColprodPlan plan = red::colprod_plan(t, R, C, info, ws);
+    return hip_status(red::launch_colprod(t, src, R, C, ld, dst, plan, ws, s));
+}
+
+} // namespace
+
+extern "C" {
+
+int red_sum_f32(const float* x, size_t n, float* out, int accum, red_stream_t stream)
+{
+    return reduce1d(OpKind::Sum, x, n, out, accum, stream);
+}
+int red_max_f32(const float* x, size_t n, float* out, int accum, red_stream_t stream)
+{
+    return reduce1d(OpKind::Max, x, n, out, accum, stream);
+}
+int red_min_f32(const float* x, size_t n, float* out, int accum, red_stream_t stream)
+{
+    return reduce1d(OpKind::Min, x, n, out, accum, stream);
+}
+
+int red_sum_f32_atomic(const float* x, size_t n, float* out, int accum, red_stream_t stream)
+{
+    return reduce1d_atomic(OpKind::Sum, x, n, out, accum, stream);
+}
+int red_max_f32_atomic(const float* x, size_t n, float* out, int accum, red_stream_t stream)
+{
+    return reduce1d_atomic(OpKind::Max, x, n, out, accum, stream);
+}
+int red_min_f32_atomic(const float* x, size_t n, float* out, int accum, red_stream_t stream)
+{
+    return reduce1d_atomic(OpKind::Min, x, n, out, accum, stream);
+}
+
+int red_sum_rows_f32(const float* x, size_t rows, size_t n, size_t ld, float* out,
+                     int accum, red_stream_t stream)
+{
+    return reduce_rows(OpKind::Sum, x, rows, n, ld, out, accum, stream);
+}
+int red_max_rows_f32(const float* x, size_t rows, size_t n, size_t ld, float* out,
+                     int accum, red_stream_t stream)
+{
+    return reduce_rows(OpKind::Max, x, rows, n, ld, out, accum, stream);
+}
+int red_min_rows_f32(const float* x, size_t rows, size_t n, size_t ld, float* out,
+                     int accum, red_stream_t stream)
+{
+    return reduce_rows(OpKind::Min, x, rows, n, ld, out, accum, stream);
+}
+
+int red_colprod_f32(const float* src, size_t R, size_t C, size_t ld, float* dst,
+                    red_stream_t stream)
+{
+    return colprod(ColType::F32, src, R, C, ld, dst, stream);
+}
+int red_colprod_f16(const uint16_t* src, size_t R, size_t C, size_t ld, uint16_t* dst,
+                    red_stream_t stream)
+{
+    return colprod(ColType::F16, src, R, C, ld, dst, stream);
+}
+int red_colprod_bf16(const uint16_t* src, size_t R, size_t C, size_t ld, uint16_t* dst,
+                     red_stream_t stream)
+{
+    return colprod(ColType::BF16, src, R, C, ld, dst, stream);
+}
+int red_colprod_i32(const int32_t* src, size_t R, size_t C, size_t ld, int32_t* dst,
+                    red_stream_t stream)
+{
+    return colprod(ColType::I32, src, R, C, ld, dst, stream);
+}
+
+const char* red_status_str(int status)
+{
+    switch (status) {
+    case RED_OK: return "ok";
+    case RED_ERR_INVALID: return "invalid argument";
+    case RED_ERR_ALIGN: return "pointer not aligned to its element size";
+    case RED_ERR_NOMEM: return "workspace allocation failed";
+    case RED_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+    }
+}
+
+int red_abi_version(void) { return RED_ABI_VERSION; }
+
+} // extern "C"

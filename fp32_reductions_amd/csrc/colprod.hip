@@ -1,0 +1,303 @@
+// colprod.hip -- column product of a row-major tile (TCOLPROD).
+//
+// PTO ISA "TCOLPROD", "Math Interpretation": dst[0,j] is the product of
+// src[i,j] over the R valid rows, for each of the C valid columns;
+// "Constraints": row-major source, destination of the same element type
+// (half, float, bfloat16, int32 among the listed ones).
+//
+// Layout of the work:
+//  * each lane owns V consecutive columns, V = 16 bytes / sizeof(T) (4 for
+//    f32 / i32, 8 for f16 / bf16), so one 16-byte load per row feeds all of
+//    them and a wave reads 1 KiB of a row contiguously;
+//  * a workgroup (4 waves) covers one block of 64*V columns and a slice of
+//    rows; its waves take interleaved rows of the slice and combine their
+//    partial products in LDS in wave order;
+//  * when the grid needs more workgroups than there are column blocks, the
+//    rows are split into S slices (blockIdx.y); each workgroup stores its
+//    partial row in the workspace and takes a ticket for its column block;
+//    the last one to arrive multiplies the S partial rows in slice order,
+//    narrows once to T and writes dst, then resets the ticket.
+//
+// Arithmetic: f32, f16 and bf16 multiply in fp32 (16-bit values widen
+// exactly), i32 in uint32 (wraps modulo 2^32).  f16 / bf16 round once, to
+// nearest even, when the final product is stored.
+#include "device.hpp"
+#include "internal.hpp"
+
+namespace red {
+namespace {
+
+constexpr int kRowsInFlight = 8; // 16-byte loads in flight per lane
+
+struct TraitsF32 {
+    using T = float;
+    using A = float;
+    static constexpr int V = 4;
+    static __device__ __forceinline__ A one() { return 1.0f; }
+    static __device__ __forceinline__ A widen(T v) { return v; }
+    static __device__ __forceinline__ T narrow(A a) { return a; }
+    static __device__ __forceinline__ void unpack(const uint4& u, A* a)
+    {
+        a[0] = __uint_as_float(u.x); a[1] = __uint_as_float(u.y);
+        a[2] = __uint_as_float(u.z); a[3] = __uint_as_float(u.w);
+    }
+};
+
+struct TraitsI32 {
+    using T = int32_t;
+    using A = uint32_t;
+    static constexpr int V = 4;
+    static __device__ __forceinline__ A one() { return 1u; }
+    static __device__ __forceinline__ A widen(T v) { return (uint32_t)v; }
+    static __device__ __forceinline__ T narrow(A a) { return (int32_t)a; }
+    static __device__ __forceinline__ void unpack(const uint4& u, A* a)
+    {
+        a[0] = u.x; a[1] = u.y; a[2] = u.z; a[3] = u.w;
+    }
+};
+
+// IEEE binary16 stored as its 16-bit pattern.
+struct TraitsF16 {
+    using T = uint16_t;
+    using A = float;
+    static constexpr int V = 8;
+    static __device__ __forceinline__ A one() { return 1.0f; }
+    static __device__ __forceinline__ A widen(T v)
+    {
+        return (float)__builtin_bit_cast(_Float16, v);
+    }
+    static __device__ __forceinline__ T narrow(A a)
+    {
+        return __builtin_bit_cast(uint16_t, (_Float16)a); // round to nearest even
+    }
+    static __device__ __forceinline__ void unpack(const uint4& u, A* a)
+    {
+        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            a[2 * k] = widen((uint16_t)(w[k] & 0xffffu));
+            a[2 * k + 1] = widen((uint16_t)(w[k] >> 16));
+        }
+    }
+};
+
+// bfloat16 stored as its 16-bit pattern: the upper half of a binary32.
+struct TraitsBF16 {
+    using T = uint16_t;
+    using A = float;
+    static constexpr int V = 8;
+    static __device__ __forceinline__ A one() { return 1.0f; }
+    static __device__ __forceinline__ A widen(T v)
+    {
+        return __uint_as_float((uint32_t)v << 16);
+    }
+    static __device__ __forceinline__ T narrow(A a)
+    {
+        const uint32_t u = __float_as_uint(a);
+        if ((u & 0x7fffffffu) > 0x7f800000u)
+            return (uint16_t)((u >> 16) | 0x0040u); // NaN stays a quiet NaN
+        return (uint16_t)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
+    }
+    static __device__ __forceinline__ void unpack(const uint4& u, A* a)
+    {
+        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            a[2 * k] = __uint_as_float(w[k] << 16);
+            a[2 * k + 1] = __uint_as_float(w[k] & 0xffff0000u);
+        }
+    }
+};
+
+// VEC: src is 16-byte aligned and ld * sizeof(T) is a multiple of 16, so
+// every lane's V columns of every row form one aligned 16-byte vector.
+template <class Tr, bool VEC>
+__global__ __launch_bounds__(kBlock) void colprod_kernel(
+    const typename Tr::T* __restrict__ src, uint64_t R, uint64_t C,
+    uint64_t ld, typename Tr::T* __restrict__ dst,
+    typename Tr::A* __restrict__ partials, unsigned* __restrict__ tickets,
+    uint64_t rows_per_split)
+{
+    using T = typename Tr::T;
+    using A = typename Tr::A;
+    constexpr int V = Tr::V;
+    constexpr int kCols = kWave * V; // columns per workgroup
+
+    __shared__ A lds[kWaves][kCols];
+    __shared__ int s_last;
+
+    const uint32_t lane = threadIdx.x & (kWave - 1);
+    const uint32_t wave = threadIdx.x / kWave;
+    const uint64_t cb = blockIdx.x;
+    const uint32_t S = gridDim.y;
+    const uint64_t s = blockIdx.y;
+    const uint64_t j0 = cb * kCols + (uint64_t)lane * V;
+    const uint64_t r0 = s * rows_per_split;
+    const uint64_t r1 = (r0 + rows_per_split < R) ? r0 + rows_per_split : R;
+
+    A acc[V];
+#pragma unroll
+    for (int k = 0; k < V; ++k)
+        acc[k] = Tr::one();
+
+    if (j0 < C) {
+        const T* __restrict__ col = src + j0;
+        uint64_t r = r0 + wave;
+        if (VEC && j0 + V <= C) {
+            for (; r + (uint64_t)kWaves * (kRowsInFlight - 1) < r1;
+                 r += (uint64_t)kWaves * kRowsInFlight) {
+                uint4 v[kRowsInFlight];
+#pragma unroll
+                for (int u = 0; u < kRowsInFlight; ++u)
+                    v[u] = *reinterpret_cast<const uint4*>(
+                        col + (r + (uint64_t)u * kWaves) * ld);
+#pragma unroll
+                for (int u = 0; u < kRowsInFlight; ++u) {
+                    A a[V];
+                    Tr::unpack(v[u], a);
+#pragma unroll
+                    for (int k = 0; k < V; ++k)
+                        acc[k] = acc[k] * a[k];
+                }
+            }
+            for (; r < r1; r += kWaves) {
+                A a[V];
+                Tr::unpack(*reinterpret_cast<const uint4*>(col + r * ld), a);
+#pragma unroll
+                for (int k = 0; k < V; ++k)
+                    acc[k] = acc[k] * a[k];
+            }
+        } else {
+            for (; r < r1; r += kWaves) {
+#pragma unroll
+                for (int k = 0; k < V; ++k)
+                    if (j0 + k < C)
+                        acc[k] = acc[k] * Tr::widen(col[r * ld + k]);
+            }
+        }
+    }
+
+    // Combine the four waves' partial rows in wave order.
+#pragma unroll
+    for (int k = 0; k < V; ++k)
+        lds[wave][lane * V + k] = acc[k];
+    __syncthreads();
+
+    for (uint32_t c = threadIdx.x; c < (uint32_t)kCols; c += kBlock) {
+        A p = lds[0][c];
+#pragma unroll
+        for (int w = 1; w < kWaves; ++w)
+            p = p * lds[w][c];
+        const uint64_t j = cb * kCols + c;
+        if (j < C) {
+            if (S == 1)
+                dst[j] = Tr::narrow(p);
+            else
+                partials[s * C + j] = p;
+        }
+    }
+    if (S == 1)
+        return;
+
+    // Make this workgroup's partial row visible device-wide, then take a
+    // ticket for the column block.
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const unsigned prev = __hip_atomic_fetch_add(
+            &tickets[cb], 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+        s_last = (prev == S - 1);
+    }
+    __syncthreads();
+    if (!s_last)
+        return;
+
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    for (uint32_t c = threadIdx.x; c < (uint32_t)kCols; c += kBlock) {
+        const uint64_t j = cb * kCols + c;
+        if (j >= C)
+            continue;
+        A p = partials[j];
+        for (uint32_t k = 1; k < S; ++k)
+            p = p * partials[(uint64_t)k * C + j];
+        dst[j] = Tr::narrow(p);
+    }
+    if (threadIdx.x == 0)
+        __hip_atomic_store(&tickets[cb], 0u, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+}
+
+template <class Tr>
+hipError_t launch_typed(const void* src, size_t R, size_t C, size_t ld,
+                        void* dst, const ColprodPlan& plan,
+                        const Workspace& ws, hipStream_t stream)
+{
+    using T = typename Tr::T;
+    using A = typename Tr::A;
+    const dim3 grid(plan.col_blocks, plan.splits);
+    const bool vec = (((uintptr_t)src & 15u) == 0) && ((ld * sizeof(T)) % 16 == 0);
+    const T* s = static_cast<const T*>(src);
+    T* d = static_cast<T*>(dst);
+    A* part = static_cast<A*>(ws.partials);
+    if (vec)
+        colprod_kernel<Tr, true><<<grid, kBlock, 0, stream>>>(
+            s, R, C, ld, d, part, ws.tickets, plan.rows_per_split);
+    else
+        colprod_kernel<Tr, false><<<grid, kBlock, 0, stream>>>(
+            s, R, C, ld, d, part, ws.tickets, plan.rows_per_split);
+    return hipGetLastError();
+}
+
+} // namespace
+
+size_t colprod_elem_size(ColType t)
+{
+    return (t == ColType::F16 || t == ColType::BF16) ? 2 : 4;
+}
+
+// Fewest rows a workgroup should own when the rows are split: below this
+// the partial-row traffic grows relative to the tile.
+constexpr uint64_t kMinRowsPerSplit = 32;
+constexpr uint64_t kMaxSplits = 65535; // gridDim.y limit
+
+ColprodPlan colprod_plan(ColType t, size_t R, size_t C, const DeviceInfo& dev,
+                         const Workspace& ws)
+{
+    ColprodPlan p;
+    const uint64_t cols = (uint64_t)kWave * (16 / colprod_elem_size(t));
+    p.col_blocks = (unsigned)((C + cols - 1) / cols);
+    const uint64_t target = (uint64_t)dev.cus * kWgPerCu;
+    uint64_t S = 1;
+    if (p.col_blocks < target)
+        S = (target + p.col_blocks - 1) / p.col_blocks;
+    const uint64_t s_rows = (R + kMinRowsPerSplit - 1) / kMinRowsPerSplit;
+    if (S > s_rows)
+        S = s_rows;
+    if (S > kMaxSplits)
+        S = kMaxSplits;
+    // The workspace bounds S * C partial values and the ticket count.
+    while (S > 1 && (S * C * 4 > ws.partial_bytes || p.col_blocks > ws.n_tickets))
+        S = (S + 1) / 2;
+    if (S < 1)
+        S = 1;
+    p.rows_per_split = (R + S - 1) / S;
+    S = (R + p.rows_per_split - 1) / p.rows_per_split; // no empty slice
+    p.splits = (unsigned)S;
+    p.partial_bytes = S > 1 ? S * C * 4 : 0;
+    return p;
+}
+
+hipError_t launch_colprod(ColType t, const void* src, size_t R, size_t C,
+                          size_t ld, void* dst, const ColprodPlan& plan,
+                          const Workspace& ws, hipStream_t stream)
+{
+    switch (t) {
+    case ColType::F32: return launch_typed<TraitsF32>(src, R, C, ld, dst, plan, ws, stream);
+    case ColType::I32: return launch_typed<TraitsI32>(src, R, C, ld, dst, plan, ws, stream);
+    case ColType::F16: return launch_typed<TraitsF16>(src, R, C, ld, dst, plan, ws, stream);
+    case ColType::BF16: return launch_typed<TraitsBF16>(src, R, C, ld, dst, plan, ws, stream);
+    }
+    return hipErrorInvalidValue;
+}
+
+} // namespace red

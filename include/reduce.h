@@ -1,0 +1,187 @@
+/*
+ * reduce.h -- C ABI of libreduce: dense-array reduction on AMD Instinct
+ * MI355X (gfx950).
+ *
+ * Two families of operations:
+ *
+ *   1. A 1-D fp32 vector reduced to one scalar by sum, max or min, with an
+ *      accum mode that folds the old destination value into the result
+ *      (TVM TIRx docs, "reduction -> sm100_packed": introduction, section
+ *      "What it accepts" -- a 1-D fp32 source and a one-element
+ *      destination -- and the table in "How inputs change the algorithm",
+ *      row "accum").  The same reduction applied independently to each row
+ *      of a row-major matrix is the segmented ("rows") form.
+ *
+ *   2. A row-major tile reduced column-wise by product to one row
+ *      (PTO ISA "TCOLPROD": "Math Interpretation" -- dst[0,j] is the
+ *      product of src[i,j] over the R valid rows, for each of the C valid
+ *      columns; "Constraints" -- row-major layout, dst and src share the
+ *      element type, the column counts agree, and a tile with zero valid
+ *      rows or columns returns early).
+ *
+ * Conventions shared by every entry point:
+ *
+ *   - Every pointer is a DEVICE pointer (HBM of the current HIP device).
+ *     The caller owns all buffers and must keep them alive until the work
+ *     enqueued on `stream` has completed.  The library keeps no pointer
+ *     after the call returns.
+ *   - Every call is asynchronous with respect to the host: it validates its
+ *     arguments, enqueues kernels on `stream` and returns.  `stream` is a
+ *     hipStream_t passed as an opaque pointer; NULL means the null stream.
+ *     Results are visible after the stream is synchronised.
+ *   - The return value is a status code (enum red_status).  Errors are
+ *     reported synchronously and never abort.  A status other than RED_OK
+ *     means nothing was enqueued, except RED_ERR_HIP after a launch, which
+ *     reports what hipGetLastError() returned.  Faults raised while a
+ *     kernel runs surface at the caller's next synchronisation, as for any
+ *     HIP kernel.
+ *   - The destination must not overlap the source (not checked).
+ *   - Empty input (n == 0, rows == 0, R == 0 or C == 0) returns RED_OK,
+ *     enqueues nothing and leaves the destination untouched, also under
+ *     accum; for column products this is TCOLPROD's early return, and the
+ *     empty product 1 is NOT written.  Pointers are not inspected then.
+ *   - Floating point follows IEEE-754 with round to nearest even.
+ *     Subnormal inputs and results are kept (no flush to zero).
+ *   - max / min are IEEE-754-2008 maxNum / minNum: a quiet NaN operand is
+ *     ignored; the result is NaN only if every operand is NaN.  When the
+ *     extreme is a zero that occurs with both signs, either zero may be
+ *     returned.
+ *   - The default (non-atomic) entry points are deterministic: for a given
+ *     input, device model and library build the result bits never change
+ *     between runs.  Internally they use a per-(device, stream) workspace of
+ *     a fixed size, created on the first call on that stream (that first
+ *     call allocates device memory and must not be made under HIP graph
+ *     capture).  Calls on different streams never share a workspace;
+ *     concurrent calls on the same stream are ordered by the stream.
+ *   - Thread safety: any host thread may call any entry point.
+ */
+#ifndef LIBREDUCE_REDUCE_H
+#define LIBREDUCE_REDUCE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define RED_ABI_VERSION 1
+
+/* A hipStream_t, passed as an opaque pointer (NULL: the null stream). */
+typedef void* red_stream_t;
+
+enum red_status {
+    RED_OK = 0,
+    RED_ERR_INVALID = 1, /* null pointer for non-empty input, ld too small,
+                            or a size whose byte extent overflows size_t */
+    RED_ERR_ALIGN = 2,   /* a pointer not aligned to its element size */
+    RED_ERR_NOMEM = 3,   /* the per-stream workspace could not be allocated */
+    RED_ERR_HIP = 4      /* the HIP runtime reported an error */
+};
+
+/* ---------------------------------------------------------------------
+ * 1-D fp32 vector -> scalar
+ *
+ * x      : n fp32 values, 4-byte aligned (16-byte alignment not required).
+ * n      : number of elements; any n >= 0 (no minimum length).
+ * out    : one fp32 value, 4-byte aligned.
+ * accum  : 0 -> *out = reduce(x);  nonzero -> *out = old *out (+|max|min)
+ *          reduce(x), with the old value folded in first.
+ *
+ * sum: the fp32 result lies within 1e-6 * (|old| + sum |x_i|) of the exact
+ * sum for the sizes this library is built for (n up to 2^31); it is
+ * computed with per-thread 8-wide accumulators, a fixed tree and a
+ * fixed-order combine of per-workgroup partials.
+ * max / min: exact (order cannot change the result).
+ * ------------------------------------------------------------------- */
+int red_sum_f32(const float* x, size_t n, float* out, int accum,
+                red_stream_t stream);
+int red_max_f32(const float* x, size_t n, float* out, int accum,
+                red_stream_t stream);
+int red_min_f32(const float* x, size_t n, float* out, int accum,
+                red_stream_t stream);
+
+/* Single-pass variants: each workgroup folds its partial into *out with
+ * one device-scope atomic, as the one-atomic-per-program block reduce in
+ * the imxueqiu.com blog post on a Triton vector-sum kernel does (its
+ * hand-written C version: warp reduce, shared-memory combine, one atomicAdd
+ * by thread 0).  Same arguments and error behaviour as above.  With
+ * accum == 0 the library first sets *out to the identity (-0.0 for sum, a
+ * quiet NaN for max / min) on `stream`.  sum uses the hardware fp32 atomic
+ * add, so its rounding order -- and its last bits -- vary from run to run
+ * (same error bound); max / min use a compare-and-swap loop and are exact.
+ * No workspace is used. */
+int red_sum_f32_atomic(const float* x, size_t n, float* out, int accum,
+                       red_stream_t stream);
+int red_max_f32_atomic(const float* x, size_t n, float* out, int accum,
+                       red_stream_t stream);
+int red_min_f32_atomic(const float* x, size_t n, float* out, int accum,
+                       red_stream_t stream);
+
+/* ---------------------------------------------------------------------
+ * Segmented rows: out[r] = reduce(x[r*ld .. r*ld + n)) for r < rows
+ *
+ * x      : row-major fp32 matrix, 4-byte aligned; row r starts at x + r*ld.
+ *          Elements between n and ld in a row are never read.
+ * rows   : number of rows; n : elements reduced per row; ld : row stride
+ *          in elements, ld >= n (RED_ERR_INVALID otherwise).
+ * out    : rows fp32 values, 4-byte aligned.
+ * accum  : nonzero folds old out[r] into row r's result.
+ *
+ * Rows of at most 64 elements are reduced one per thread in exactly the
+ * single-precision order of the TVM page's "Algorithm" section (8 slots,
+ * chunks of 8, leftovers into slot i mod 8, the 8 -> 4 -> 2 -> 1 tree,
+ * accum into slot 0 first); longer rows one per wavefront (or one per
+ * workgroup for few, very long rows).  Same tolerances as the 1-D calls.
+ * ------------------------------------------------------------------- */
+int red_sum_rows_f32(const float* x, size_t rows, size_t n, size_t ld,
+                     float* out, int accum, red_stream_t stream);
+int red_max_rows_f32(const float* x, size_t rows, size_t n, size_t ld,
+                     float* out, int accum, red_stream_t stream);
+int red_min_rows_f32(const float* x, size_t rows, size_t n, size_t ld,
+                     float* out, int accum, red_stream_t stream);
+
+/* ---------------------------------------------------------------------
+ * Column product (TCOLPROD): dst[j] = prod_{i<R} src[i*ld + j], j < C
+ *
+ * src    : row-major tile of element type T, aligned to sizeof(T); row i
+ *          starts at src + i*ld.  Elements between C and ld are never read.
+ * R, C   : valid rows and columns; ld : row stride in elements, ld >= C
+ *          (RED_ERR_INVALID otherwise -- the analogue of TCOLPROD's check
+ *          that source and destination agree on the valid column count).
+ * dst    : C values of the same element type T, aligned to sizeof(T).
+ *
+ * f32    : products accumulate in fp32; relative error <= (R-1) * 2^-24
+ *          whatever the order.
+ * f16/bf16 (given as uint16_t bit patterns: IEEE binary16 / bfloat16):
+ *          values are widened exactly to fp32, multiplied in fp32, and the
+ *          final product is rounded once to T (round to nearest even).
+ * i32    : products wrap modulo 2^32 (two's complement); bit-exact.
+ *
+ * Deterministic: the row range is split over workgroups in a fixed way and
+ * the partial products are multiplied in index order.
+ * ------------------------------------------------------------------- */
+int red_colprod_f32(const float* src, size_t R, size_t C, size_t ld,
+                    float* dst, red_stream_t stream);
+int red_colprod_f16(const uint16_t* src, size_t R, size_t C, size_t ld,
+                    uint16_t* dst, red_stream_t stream);
+int red_colprod_bf16(const uint16_t* src, size_t R, size_t C, size_t ld,
+                     uint16_t* dst, red_stream_t stream);
+int red_colprod_i32(const int32_t* src, size_t R, size_t C, size_t ld,
+                    int32_t* dst, red_stream_t stream);
+
+/* ---------------------------------------------------------------------
+ * Utilities
+ * ------------------------------------------------------------------- */
+
+/* Static, NUL-terminated description of a status code (never NULL). */
+const char* red_status_str(int status);
+
+/* RED_ABI_VERSION of the built library. */
+int red_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBREDUCE_REDUCE_H */

@@ -1,0 +1,130 @@
+"""GPU parity of the segmented row reductions against the CPU oracle.
+
+Rows of at most 64 elements run the TVM page's thread-scope order and must
+match the oracle's replay of that order bit for bit; longer rows are held
+to the sum tolerance; max / min are bit-exact everywhere."""
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from gpu_helpers import check_exact, check_sum, dev, host, say
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def red():
+    import fp32_reductions_amd as red
+    return red
+
+
+@pytest.fixture(scope="module")
+def orc():
+    return oracle.get()
+
+
+def run_rows(red, op, xd, n, old=None, accum=False):
+    rows = xd.shape[0]
+    out = (torch.zeros(rows, dtype=torch.float32, device="cuda") if old is None
+           else dev(np.asarray(old, np.float32)))
+    getattr(red, "%s_rows_f32" % op)(xd, out, n=n, accum=accum)
+    return host(out)
+
+
+def check_rows(orc, op, x, n, got, accum=False, old=None, what=""):
+    rows, ld = x.shape
+    if op == "sum":
+        if n <= 64:  # the page's own order, bit for bit
+            want = orc.rows_page_sum_f32(x, rows, n, ld, accum, old)
+            bad = np.nonzero(got.view(np.uint32) != want.view(np.uint32))[0]
+            assert bad.size == 0, "%s: row %d got %r want %r" % (
+                what, bad[0], got[bad[0]], want[bad[0]])
+        s, a = orc.rows_sum_f32(x, rows, n, ld, accum, old)
+        err = np.abs(got.astype(np.float64) - s)
+        assert (err <= 1e-6 * a).all(), "%s: worst %g" % (what, float((err / np.maximum(a, 1e-300)).max()))
+    else:
+        fn = orc.rows_max_f32 if op == "max" else orc.rows_min_f32
+        want = fn(x, rows, n, ld, accum, old)
+        eq = (got.view(np.uint32) == want.view(np.uint32)) | ((got == 0) & (want == 0)) \
+            | (np.isnan(got) & np.isnan(want))
+        assert eq.all(), "%s: row %d" % (what, int(np.nonzero(~eq)[0][0]))
+
+
+@pytest.fixture(scope="module")
+def rows32():
+    say("generate 4096 x 32 rows (seed 0)")
+    a, _ = workloads.rows32()
+    return a, dev(a)
+
+
+@pytest.mark.parametrize("accum", [False, True])
+@pytest.mark.parametrize("op", ["sum", "max", "min"])
+def test_rows32(red, orc, rows32, op, accum):
+    x, xd = rows32
+    say("rows32 op=%s accum=%s" % (op, accum))
+    old = workloads.uniform_f32(30, 4096, -3.0, 3.0) if accum else None
+    got = run_rows(red, op, xd, 32, old, accum)
+    check_rows(orc, op, x, 32, got, accum, old, "rows32 %s" % op)
+
+
+def test_rows32_demo_sum_is_exact_for_integers(red):
+    """The page's demonstration length (32 elements, one thread): with
+    integer values the result equals the exact sum."""
+    say("rows32 integer demo")
+    x = workloads.integers_i32(31, (4096, 32), -100, 101).astype(np.float32)
+    got = run_rows(red, "sum", dev(x), 32)
+    assert (got == x.astype(np.int64).sum(axis=1)).all()
+
+
+@pytest.fixture(scope="module")
+def rows1000():
+    say("generate 65536 x 1000 rows (seed 4)")
+    x = workloads.rows1000_x()
+    return x, dev(x)
+
+
+@pytest.mark.parametrize("op", ["sum", "max"])
+def test_rows1000(red, orc, rows1000, op):
+    x, xd = rows1000
+    say("rows1000 op=%s" % op)
+    got = run_rows(red, op, xd, 1000)
+    check_rows(orc, op, x, 1000, got, what="rows1000 %s" % op)
+
+
+SHAPES = [  # (rows, n, ld, element offset of the base pointer)
+    (1, 1, 1, 0), (5, 7, 7, 0), (9, 8, 8, 0), (9, 9, 9, 1), (33, 17, 19, 2),
+    (300, 64, 64, 0), (300, 64, 67, 3), (257, 65, 65, 0), (100, 100, 103, 1),
+    (70, 1000, 1000, 2), (3, 4097, 4100, 0), (1, 16385, 16385, 0),
+    (2, 100003, 100010, 1), (4096, 31, 32, 0), (2049, 250, 256, 0),
+]
+
+
+@pytest.mark.parametrize("rows,n,ld,off", SHAPES)
+def test_rows_shapes(red, orc, rows, n, ld, off):
+    say("rows shape rows=%d n=%d ld=%d off=%d" % (rows, n, ld, off))
+    flat = workloads.uniform_f32(32, rows * ld + off + 4, -4.0, 4.0)
+    flat[off:off + rows * ld].reshape(rows, ld)[:, n:] = np.nan  # padding
+    fd = dev(flat)
+    x = flat[off:off + rows * ld].reshape(rows, ld)
+    xd = fd[off:off + rows * ld].view(rows, ld)
+    old = workloads.uniform_f32(33, rows, -2.0, 2.0)
+    for op in ("sum", "max", "min"):
+        for accum in (False, True):
+            got = run_rows(red, op, xd, n, old if accum else None, accum)
+            check_rows(orc, op, x, n, got, accum, old if accum else None,
+                       "rows=%d n=%d ld=%d off=%d %s accum=%s" % (rows, n, ld, off, op, accum))
+
+
+def test_rows_empty_untouched(red):
+    say("rows empty")
+    x = torch.ones((4, 8), dtype=torch.float32, device="cuda")
+    for op in ("sum", "max", "min"):
+        out = torch.full((4,), 9.5, dtype=torch.float32, device="cuda")
+        getattr(red, op + "_rows_f32")(x, out, n=0, accum=True)
+        assert (host(out) == 9.5).all()
+        e = torch.ones((0, 8), dtype=torch.float32, device="cuda")
+        getattr(red, op + "_rows_f32")(e, out, n=8)
+        assert (host(out) == 9.5).all()

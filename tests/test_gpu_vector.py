@@ -1,0 +1,200 @@
+"""GPU parity of the 1-D fp32 reductions (sum / max / min, accum, atomic
+variant) against the CPU oracle: the full-size 2^24 and 2^30 + 7 vectors,
+every small length with every 16-byte misalignment, special values,
+extreme positions, exact integer sums and run-to-run determinism."""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from gpu_helpers import check_exact, check_sum, dev, host, say
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def red():
+    import fp32_reductions_amd as red
+    return red
+
+
+@pytest.fixture(scope="module")
+def orc():
+    return oracle.get()
+
+
+OPS = ("sum", "max", "min")
+
+
+def run(red, op, x_dev, accum=False, old=0.0, atomic=False):
+    out = torch.full((1,), old, dtype=torch.float32, device="cuda")
+    fn = getattr(red, "%s_f32%s" % (op, "_atomic" if atomic else ""))
+    fn(x_dev, out, accum=accum)
+    return host(out)[0]
+
+
+def check(orc, op, x, got, accum=False, old=0.0, what=""):
+    if op == "sum":
+        s, a = orc.sum_f32(x, accum, old)
+        check_sum(got, s, a, what)
+    elif op == "max":
+        check_exact(got, orc.max_f32(x, accum, old), what)
+    else:
+        check_exact(got, orc.min_f32(x, accum, old), what)
+
+
+# ---------------------------------------------------------------------------
+# full-size workloads
+# ---------------------------------------------------------------------------
+
+@pytest.fixture(scope="module")
+def vec16m():
+    say("generate 2^24 uniform[-1,1) vector (seed 1)")
+    x = workloads.vec16m()
+    return x, dev(x)
+
+
+@pytest.mark.parametrize("atomic", [False, True], ids=["twopass", "atomic"])
+@pytest.mark.parametrize("accum", [False, True], ids=["noaccum", "accum3.25"])
+@pytest.mark.parametrize("op", OPS)
+def test_vec16m(red, orc, vec16m, op, accum, atomic):
+    x, xd = vec16m
+    old = workloads.ACCUM_PRESET if accum else 0.0
+    say("vec16m op=%s accum=%s atomic=%s" % (op, accum, atomic))
+    got = run(red, op, xd, accum, old, atomic)
+    check(orc, op, x, got, accum, old, "vec16m %s" % op)
+    if op == "max" and accum:
+        assert got == np.float32(3.25)  # closed form: 3.25 exceeds every x
+
+
+@pytest.fixture(scope="module")
+def vec1g():
+    say("generate 2^30+7 normal vector, 1% scaled by 1e6 (seed 3)")
+    x = workloads.vec1g()
+    return x, dev(x)
+
+
+@pytest.mark.parametrize("op", OPS)
+def test_vec1g(red, orc, vec1g, op):
+    x, xd = vec1g
+    say("vec1g n=2^30+7 op=%s" % op)
+    got = run(red, op, xd)
+    check(orc, op, x, got, what="vec1g %s" % op)
+
+
+@pytest.mark.parametrize("op", OPS)
+def test_vec1g_atomic(red, orc, vec1g, op):
+    x, xd = vec1g
+    say("vec1g atomic op=%s" % op)
+    got = run(red, op, xd, atomic=True)
+    check(orc, op, x, got, what="vec1g atomic %s" % op)
+
+
+# ---------------------------------------------------------------------------
+# small and ragged lengths, every misalignment
+# ---------------------------------------------------------------------------
+
+SIZES = (list(range(1, 18)) + [31, 32, 33, 63, 64, 65, 255, 256, 257, 1000,
+                               4095, 4096, 4097, 65537]
+         + [(1 << 20) + k for k in range(8)])
+
+
+@pytest.fixture(scope="module")
+def base():
+    x = workloads.uniform_f32(21, (1 << 20) + 16, -10.0, 10.0)
+    return x, dev(x)
+
+
+@pytest.mark.parametrize("atomic", [False, True], ids=["twopass", "atomic"])
+@pytest.mark.parametrize("n", SIZES)
+def test_lengths_and_offsets(red, orc, base, n, atomic):
+    x, xd = base
+    say("lengths n=%d atomic=%s" % (n, atomic))
+    for off in range(4):
+        xs, xds = x[off:off + n], xd[off:off + n]
+        for op in OPS:
+            for accum, old in ((False, 0.0), (True, -2.5)):
+                got = run(red, op, xds, accum, old, atomic)
+                check(orc, op, xs, got, accum, old,
+                      "n=%d off=%d %s accum=%s" % (n, off, op, accum))
+
+
+@pytest.mark.parametrize("n", [7, 1000, (1 << 20) + 5])
+def test_extreme_positions(red, orc, n):
+    say("extreme positions n=%d" % n)
+    rng = np.random.default_rng(22)
+    for where in sorted({0, 1, n // 2, n - 4, n - 2, n - 1} & set(range(n))):
+        x = rng.uniform(-1, 1, n).astype(np.float32)
+        x[where] = 5.0
+        assert run(red, "max", dev(x)) == np.float32(5.0), where
+        x[where] = -5.0
+        assert run(red, "min", dev(x)) == np.float32(-5.0), where
+
+
+def test_integer_sums_are_exact(red):
+    """Integers in [-8, 8]: every partial sum is an integer below 2^24, so
+    every order is exact and the fp32 result equals the exact sum."""
+    say("integer sums")
+    for n, seed in (((1 << 20) + 3, 23), (12345, 24), (2, 25)):
+        x = workloads.integers_i32(seed, n, -8, 9).astype(np.float32)
+        want = float(np.sum(x.astype(np.int64)))
+        assert run(red, "sum", dev(x)) == want
+        assert run(red, "sum", dev(x), True, 7.0) == want + 7.0
+
+
+def test_special_values(red, orc):
+    say("special values")
+    nan, inf = float("nan"), float("inf")
+    cases = [
+        [nan, 1.0, nan, -3.0],
+        [nan] * 9,
+        [nan] * 3000 + [2.0] + [nan] * 3000,
+        [inf, 1.0, -2.0],
+        [-inf, 1.0, 5.0] * 100,
+        [2.0 ** -149, -(2.0 ** -149), 0.0, 2.0 ** -140] * 50,
+        [0.0, -0.0] * 1000,
+        [-0.0] * 17,
+    ]
+    for vals in cases:
+        x = np.array(vals, np.float32)
+        xd = dev(x)
+        for op in OPS:
+            got = run(red, op, xd)
+            what = "special %s %s" % (op, vals[:4])
+            check(orc, op, x, got, what=what)
+    # subnormals are summed, not flushed: exact small integer multiples
+    x = np.full(1000, 2.0 ** -149, np.float32)
+    assert run(red, "sum", dev(x)) == np.float32(1000 * 2.0 ** -149)
+    # accum under NaN policy
+    x = dev(np.array([nan, nan], np.float32))
+    assert run(red, "max", x, True, 1.5) == np.float32(1.5)
+    assert math.isnan(run(red, "min", x))
+
+
+def test_empty_leaves_out_untouched(red):
+    say("empty input")
+    x = torch.empty(0, dtype=torch.float32, device="cuda")
+    for op in OPS:
+        for atomic in (False, True):
+            for accum in (False, True):
+                assert run(red, op, x, accum, 42.0, atomic) == np.float32(42.0)
+
+
+def test_deterministic(red, vec16m):
+    """The default path gives the same bits every time and on any stream."""
+    say("determinism")
+    _, xd = vec16m
+    for op in OPS:
+        ref = run(red, op, xd)
+        for _ in range(3):
+            assert np.float32(run(red, op, xd)).tobytes() == np.float32(ref).tobytes()
+        s = torch.cuda.Stream()
+        with torch.cuda.stream(s):
+            out = torch.zeros(1, dtype=torch.float32, device="cuda")
+            getattr(red, op + "_f32")(xd, out)
+        s.synchronize()
+        assert host(out)[0].tobytes() == np.float32(ref).tobytes()

@@ -117,6 +117,12 @@ def vec1g(n: int = N_VEC1G):
     return x
 
 
+def rows1000_x():
+    """X[65536, 1000] f32 alone (the first draw of rows1000's generator)."""
+    rng = np.random.default_rng(4)
+    return _uniform_f32(rng, -1.0, 1.0, 65536 * 1000).reshape(65536, 1000)
+
+
 def rows1000():
     """(X[65536, 1000] f32, B[2048, 32768] bf16 bits, H[2048, 32768] f16 bits)."""
     rng = np.random.default_rng(4)
