@@ -1,0 +1,494 @@
+"""Benchmark of libreduce on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+Prints ONE JSON line on stdout.  A step is one pass of the workload's calls
+over its input (default workload ``vec16m``: a 2^24-element fp32 vector
+reduced by sum, max and min, then again with accum into a destination
+preset to 3.25).  ``value`` is whole-step effective bandwidth: algorithmic
+bytes of all calls in a step divided by the wall time per step, with every
+input already resident in HBM.
+
+Cold cache: MI355X's 256 MB Infinity Cache would hold a 64 MiB vector
+between calls, so the input exists as several identical copies in HBM and
+consecutive calls read different copies, which puts at least 1 GiB of other
+traffic between two reads of the same copy.  No flush runs in the timed
+region.
+
+``roofline`` covers the dominant kernel: its algorithmic bytes per launch
+over its mean launch duration, measured with HIP events recorded on the
+launch stream around every launch inside the timed region.  ``traffic`` is
+the HBM bytes per launch measured with rocprofv3 counters (FETCH_SIZE,
+WRITE_SIZE, scaled against a plain copy kernel), read from the committed
+counter summary under profiles/, or null when that summary was taken on a
+different kernel source.
+
+``cpu_baseline`` times the CPU oracle (single-threaded, as written) on whole
+steps of the same workload for about ten seconds, as a reference point only.
+
+Other workloads (--workload): vec1g (2^30+7 vector), colprod4k (4096 x 16384
+f32 and i32 column products), rows1000 (65536 x 1000 row sum / max, then
+2048 x 32768 bf16 / f16 column products), rows32 (4096 x 32 rows, 16 x 16
+tile), copycal (a plain device copy, for counter calibration).
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import workloads  # noqa: E402
+
+METRIC = "effective HBM GB/s (% of peak) for fp32 vector sum/max/min and colprod"
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E peak, 8 TB/s
+COLD_BYTES = 1 << 30   # other traffic between two reads of the same copy
+PROFILES = os.path.join(ROOT, "profiles")
+CSRC = os.path.join(ROOT, "fp32_reductions_amd", "csrc")
+
+
+def log(msg: str) -> None:
+    print("[bench] " + msg, file=sys.stderr, flush=True)
+
+
+class HipEvents:
+    """Timing-only HIP events recorded on the launch stream.
+
+    Created with hipEventDisableSystemFence: recording such an event skips
+    the system-scope cache writeback / invalidate a default event performs
+    (on MI355X a default event pair added ~7 us to every 16 us launch).  The
+    events come from the HIP runtime already loaded in the process (the one
+    torch and libreduce share), and are read only after a device-wide
+    synchronize."""
+
+    DISABLE_SYSTEM_FENCE = 0x20000000
+
+    def __init__(self):
+        path = None
+        with open("/proc/self/maps") as fh:
+            for line in fh:
+                if "libamdhip64" in line:
+                    path = line.split()[-1]
+                    break
+        hip = ctypes.CDLL(path or "libamdhip64.so")
+        hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+        hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float),
+                                            ctypes.c_void_p, ctypes.c_void_p]
+        hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.hip = hip
+        self.record_fn = hip.hipEventRecord
+
+    def create(self) -> int:
+        ev = ctypes.c_void_p()
+        if self.hip.hipEventCreateWithFlags(ctypes.byref(ev), self.DISABLE_SYSTEM_FENCE) != 0:
+            raise RuntimeError("hipEventCreateWithFlags failed")
+        return ev.value
+
+    def elapsed_ms(self, a: int, b: int) -> float:
+        ms = ctypes.c_float()
+        if self.hip.hipEventElapsedTime(ctypes.byref(ms), a, b) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value
+
+    def destroy(self, ev: int) -> None:
+        self.hip.hipEventDestroy(ev)
+
+
+class Call:
+    """One library call in a step: make(step_index) returns a pre-marshalled
+    plan (fp32_reductions_amd.plan) that enqueues it when called."""
+
+    def __init__(self, name, kernel, nbytes, make):
+        self.name, self.kernel, self.nbytes, self.make = name, kernel, nbytes, make
+
+
+class Workload:
+    def __init__(self, name, desc, config, calls, dominant, sources, cpu):
+        self.name = name
+        self.desc = desc
+        self.config = config      # extra config keys
+        self.calls = calls
+        self.dominant = dominant  # call names timed for the roofline
+        self.sources = sources    # csrc files that define the dominant kernel
+        self.cpu = cpu            # list of (bytes, host callable) for one step
+
+
+class Rotor:
+    """Identical copies of one device tensor, handed out round-robin.
+
+    With ``uses`` reads of the tensor per step and ``step_bytes`` read by the
+    whole step, enough copies are made that at least COLD_BYTES of other
+    reads separate two reads of the same copy.  A tensor of COLD_BYTES or
+    more needs no copies."""
+
+    def __init__(self, t, uses: int, step_bytes: int):
+        nbytes = t.numel() * t.element_size()
+        if nbytes >= COLD_BYTES:
+            count = 1
+        else:
+            count = max(2, -(-uses * COLD_BYTES // step_bytes) + 1)
+        self.copies = [t] + [t.clone() for _ in range(count - 1)]
+        self.i = 0
+
+    def next(self):
+        t = self.copies[self.i]
+        self.i = (self.i + 1) % len(self.copies)
+        return t
+
+    def __len__(self):
+        return len(self.copies)
+
+
+def up(torch, a):
+    if a.dtype == np.uint16:
+        a = a.view(np.int16)
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+# ---------------------------------------------------------------------------
+# workloads
+# ---------------------------------------------------------------------------
+
+def wl_vec16m(torch, red, orc, steps):
+    x = workloads.vec16m()
+    n = x.size
+    xs = Rotor(up(torch, x), 6, 6 * 4 * n)
+    outs = torch.zeros((steps, 3), dtype=torch.float32, device="cuda")
+    accs = torch.full((steps, 3), workloads.ACCUM_PRESET, dtype=torch.float32,
+                      device="cuda")
+    calls = []
+    for j, op in enumerate(("sum", "max", "min")):
+        def plain(k, op=op, j=j):
+            return red.plan(op + "_f32", xs.next(), outs[k, j:j + 1])
+
+        def accum(k, op=op, j=j):
+            return red.plan(op + "_f32", xs.next(), accs[k, j:j + 1], accum=True)
+
+        kern = "reduce1d_stream_kernel<Op{0}> + reduce1d_finish_kernel<Op{0}>".format(op.capitalize())
+        calls.append(Call(op, kern, 4 * n + 4, plain))
+        calls.append(Call(op + "_accum", kern, 4 * n + 8, accum))
+    calls = [calls[0], calls[2], calls[4], calls[1], calls[3], calls[5]]
+    cpu = [(4 * n + 4, lambda: orc.sum_f32(x)), (4 * n + 4, lambda: orc.max_f32(x)),
+           (4 * n + 4, lambda: orc.min_f32(x)),
+           (4 * n + 8, lambda: orc.sum_f32(x, True, 3.25)),
+           (4 * n + 8, lambda: orc.max_f32(x, True, 3.25)),
+           (4 * n + 8, lambda: orc.min_f32(x, True, 3.25))]
+    return Workload(
+        "vec16m",
+        "one fp32 vector of 2^24 elements, uniform[-1,1), seed 1; sum, max, min, "
+        "then sum, max, min with accum into a destination preset to 3.25",
+        {"n": n, "calls_per_step": 6, "cold_copies": len(xs)},
+        calls, ["sum"], ["reduce1d.hip", "device.hpp"], cpu)
+
+
+def wl_vec1g(torch, red, orc, steps):
+    log("generating 2^30+7 vector")
+    x = workloads.vec1g()
+    n = x.size
+    xd = up(torch, x)
+    outs = torch.zeros((steps, 3), dtype=torch.float32, device="cuda")
+    calls = []
+    for j, op in enumerate(("sum", "max", "min")):
+        kern = "reduce1d_stream_kernel<Op{0}> + reduce1d_finish_kernel<Op{0}>".format(op.capitalize())
+        calls.append(Call(op, kern, 4 * n + 4,
+                          lambda k, op=op, j=j: red.plan(op + "_f32", xd, outs[k, j:j + 1])))
+    cpu = [(4 * n + 4, lambda: orc.sum_f32(x)), (4 * n + 4, lambda: orc.max_f32(x)),
+           (4 * n + 4, lambda: orc.min_f32(x))]
+    return Workload(
+        "vec1g",
+        "one fp32 vector of 2^30+7 elements, normal(0,1) with 1% of entries "
+        "scaled by 1e6, seed 3; sum, max, min",
+        {"n": n, "calls_per_step": 3, "cold_copies": 1},
+        calls, ["sum"], ["reduce1d.hip", "device.hpp"], cpu)
+
+
+def wl_colprod4k(torch, red, orc, steps):
+    log("generating 4096 x 16384 f32 / i32 tiles")
+    f, i = workloads.colprod4k_f32_i32()
+    R, C = f.shape
+    nbytes = 4 * R * C + 4 * C
+    fs = Rotor(up(torch, f), 1, 2 * nbytes)
+    is_ = Rotor(up(torch, i), 1, 2 * nbytes)
+    of = torch.zeros(C, dtype=torch.float32, device="cuda")
+    oi = torch.zeros(C, dtype=torch.int32, device="cuda")
+    calls = [Call("colprod_f32", "colprod_kernel<TraitsF32> + colprod_finish_kernel<TraitsF32>", nbytes,
+                  lambda k: red.plan("colprod_f32", fs.next(), of)),
+             Call("colprod_i32", "colprod_kernel<TraitsI32> + colprod_finish_kernel<TraitsI32>", nbytes,
+                  lambda k: red.plan("colprod_i32", is_.next(), oi))]
+    cpu = [(nbytes, lambda: orc.colprod_f32(f, R, C, C)),
+           (nbytes, lambda: orc.colprod_i32(i, R, C, C))]
+    return Workload(
+        "colprod4k",
+        "column products of a 4096 x 16384 fp32 tile, uniform[0.999,1.001), and "
+        "an int32 tile of the same shape, values in {-3..3}\\{0}, seed 2",
+        {"R": R, "C": C, "calls_per_step": 2, "cold_copies": len(fs)},
+        calls, ["colprod_f32"], ["colprod.hip", "device.hpp"], cpu)
+
+
+def wl_rows1000(torch, red, orc, steps):
+    log("generating 65536 x 1000 rows and 2048 x 32768 bf16 / f16 tiles")
+    x, b, h = workloads.rows1000()
+    rows, n = x.shape
+    R, C = b.shape
+    rbytes = 4 * rows * n + 4 * rows
+    tbytes = 2 * R * C + 2 * C
+    step = 2 * rbytes + 2 * tbytes
+    xs = Rotor(up(torch, x), 2, step)
+    bs = Rotor(up(torch, b).view(torch.bfloat16), 1, step)
+    hs = Rotor(up(torch, h).view(torch.float16), 1, step)
+    o1 = torch.zeros(rows, dtype=torch.float32, device="cuda")
+    o2 = torch.zeros(rows, dtype=torch.float32, device="cuda")
+    ob = torch.zeros(C, dtype=torch.bfloat16, device="cuda")
+    oh = torch.zeros(C, dtype=torch.float16, device="cuda")
+    calls = [Call("rows_sum", "rows_wave_kernel<OpSum>", rbytes,
+                  lambda k: red.plan("sum_rows_f32", xs.next(), o1)),
+             Call("rows_max", "rows_wave_kernel<OpMax>", rbytes,
+                  lambda k: red.plan("max_rows_f32", xs.next(), o2)),
+             Call("colprod_bf16", "colprod_kernel<TraitsBF16> + colprod_finish_kernel<TraitsBF16>", tbytes,
+                  lambda k: red.plan("colprod_bf16", bs.next(), ob)),
+             Call("colprod_f16", "colprod_kernel<TraitsF16> + colprod_finish_kernel<TraitsF16>", tbytes,
+                  lambda k: red.plan("colprod_f16", hs.next(), oh))]
+    cpu = [(rbytes, lambda: orc.rows_sum_f32(x, rows, n, n)),
+           (rbytes, lambda: orc.rows_max_f32(x, rows, n, n)),
+           (tbytes, lambda: orc.colprod_bf16(b, R, C, C)),
+           (tbytes, lambda: orc.colprod_f16(h, R, C, C))]
+    return Workload(
+        "rows1000",
+        "65536 rows x 1000 fp32, uniform[-1,1), row sum and row max; then column "
+        "products of 2048 x 32768 bf16 and f16 tiles, uniform[0.99,1.01), seed 4",
+        {"rows": rows, "n": n, "R": R, "C": C, "calls_per_step": 4,
+         "cold_copies": [len(xs), len(bs), len(hs)]},
+        calls, ["rows_sum"], ["rows.hip", "device.hpp"], cpu)
+
+
+def wl_rows32(torch, red, orc, steps):
+    a, t = workloads.rows32()
+    rows, n = a.shape
+    ad, td = up(torch, a), up(torch, t)
+    o = [torch.zeros(rows, dtype=torch.float32, device="cuda") for _ in range(3)]
+    ot = torch.zeros(16, dtype=torch.float32, device="cuda")
+    rbytes = 4 * rows * n + 4 * rows
+    calls = [Call("rows_sum", "rows_thread_kernel<OpSum>", rbytes,
+                  lambda k: red.plan("sum_rows_f32", ad, o[0])),
+             Call("rows_max", "rows_thread_kernel<OpMax>", rbytes,
+                  lambda k: red.plan("max_rows_f32", ad, o[1])),
+             Call("rows_min", "rows_thread_kernel<OpMin>", rbytes,
+                  lambda k: red.plan("min_rows_f32", ad, o[2])),
+             Call("colprod_tile16", "colprod_kernel<TraitsF32>", 16 * 16 * 4 + 64,
+                  lambda k: red.plan("colprod_f32", td, ot))]
+    cpu = [(rbytes, lambda: orc.rows_page_sum_f32(a, rows, n, n)),
+           (rbytes, lambda: orc.rows_max_f32(a, rows, n, n)),
+           (rbytes, lambda: orc.rows_min_f32(a, rows, n, n)),
+           (16 * 16 * 4 + 64, lambda: orc.colprod_f32(t, 16, 16, 16))]
+    return Workload(
+        "rows32",
+        "4096 rows x 32 fp32, uniform[-1,1), seed 0: row sum, max, min (one "
+        "thread per row); one 16 x 16 fp32 tile column product",
+        {"rows": rows, "n": n, "calls_per_step": 4, "cold_copies": 1},
+        calls, ["rows_sum"], ["rows.hip", "device.hpp"], cpu)
+
+
+def wl_copycal(torch, red, orc, steps):
+    """A plain elementwise copy of known size (256 MiB read, 256 MiB
+    written) for scaling the FETCH_SIZE / WRITE_SIZE counters."""
+    n = 1 << 26
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    calls = [Call("copy", "elementwise copy", 8 * n,
+                  lambda k: (lambda: torch.neg(src, out=dst)))]
+    return Workload("copycal", "plain device copy of 2^26 fp32 (256 MiB in, 256 MiB out)",
+                    {"n": n, "calls_per_step": 1, "cold_copies": 1},
+                    calls, ["copy"], [], [])
+
+
+WORKLOADS = {"vec16m": wl_vec16m, "vec1g": wl_vec1g, "colprod4k": wl_colprod4k,
+             "rows1000": wl_rows1000, "rows32": wl_rows32, "copycal": wl_copycal}
+
+
+# ---------------------------------------------------------------------------
+# counters committed under profiles/
+# ---------------------------------------------------------------------------
+
+def source_hash(files) -> str:
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def committed_traffic(wl: Workload):
+    """HBM bytes per launch of the dominant kernel from the committed counter
+    summary, or None if absent or taken on different kernel source."""
+    path = os.path.join(PROFILES, "%s_%s_counters.txt" % (wl.dominant[0], wl.name))
+    if not wl.sources or not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path) as fh:
+        for line in fh:
+            if "=" in line and not line.startswith("#"):
+                k, v = line.split("=", 1)
+                vals[k.strip()] = v.strip()
+    if vals.get("kernel_source_sha256_16") != source_hash(wl.sources):
+        return None
+    try:
+        return float(vals["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+# ---------------------------------------------------------------------------
+# main
+# ---------------------------------------------------------------------------
+
+def cpu_baseline(wl: Workload, budget_s: float = 10.0):
+    if not wl.cpu:
+        return None
+    total_bytes, t0, steps = 0, time.perf_counter(), 0
+    while True:
+        for nbytes, fn in wl.cpu:
+            fn()
+            total_bytes += nbytes
+        steps += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": round(total_bytes / dt / 1e9, 3), "unit": "GB/s", "cores": 1,
+            "kind": "oracle",
+            "sample": "%d whole step(s) of the same workload (all %d calls, same "
+                      "host arrays), single-threaded C oracle, %.1f s"
+                      % (steps, len(wl.cpu), dt)}
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="vec16m", choices=sorted(WORKLOADS))
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="time budget of the CPU-oracle baseline (0: skip)")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: multi-GPU runs are not part of "
+              "this library (got --gpus %d)" % args.gpus, file=sys.stderr)
+        return 2
+
+    import torch
+
+    import fp32_reductions_amd as red
+    import oracle
+
+    orc = oracle.get()
+    torch.cuda.set_device(0)
+    props = torch.cuda.get_device_properties(0)
+    K, W = args.steps, args.warmup
+    wl = WORKLOADS[args.workload](torch, red, orc, K + W)
+    stream = torch.cuda.current_stream()
+
+    log("workload %s: %d calls/step, warmup %d, steps %d" % (wl.name, len(wl.calls), W, K))
+    plans = [[call.make(k) for call in wl.calls] for k in range(W + K)]
+    for k in range(W):
+        for p in plans[k]:
+            p()
+    torch.cuda.synchronize()
+
+    # Timed region: K steps.  Events bracket only the dominant call of each
+    # step (recording an event pair between two kernels stalls the queue for
+    # a few microseconds, so bracketing every call would slow the step).
+    hev = HipEvents()
+    sh = stream.cuda_stream
+    record = hev.record_fn
+    names = [call.name for call in wl.calls]
+    dom_idx = [names.index(name) for name in wl.dominant]
+    ev = {j: [(hev.create(), hev.create()) for _ in range(K)] for j in dom_idx}
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(K):
+        for j, p in enumerate(plans[W + k]):
+            if j in ev:
+                record(ev[j][k][0], sh)
+                p()
+                record(ev[j][k][1], sh)
+            else:
+                p()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+
+    ms_per_step = (t1 - t0) * 1e3 / K
+    step_bytes = sum(call.nbytes for call in wl.calls)
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+    dom_durs = {j: [hev.elapsed_ms(a, b) for a, b in ev[j]] for j in dom_idx}
+
+    # Per-call breakdown (not part of the timed region): a short pass with an
+    # event pair around every call.
+    kb = min(K, 50)
+    evb = [[(hev.create(), hev.create()) for _ in wl.calls] for _ in range(kb)]
+    torch.cuda.synchronize()
+    for k in range(kb):
+        for j, p in enumerate(plans[W + k]):
+            record(evb[k][j][0], sh)
+            p()
+            record(evb[k][j][1], sh)
+    torch.cuda.synchronize()
+    per_call = {}
+    for j, call in enumerate(wl.calls):
+        durs = [hev.elapsed_ms(evb[k][j][0], evb[k][j][1]) for k in range(kb)]
+        per_call[call.name] = {"kernel": call.kernel, "bytes": call.nbytes,
+                               "mean_us": round(1e3 * float(np.mean(durs)), 3),
+                               "median_us": round(1e3 * float(np.median(durs)), 3),
+                               "gbs_mean": round(call.nbytes / (float(np.mean(durs)) * 1e-3) / 1e9, 1)}
+    for evs in list(ev.values()) + evb:
+        for a, b in evs:
+            hev.destroy(a)
+            hev.destroy(b)
+    dom_bytes = float(np.mean([wl.calls[j].nbytes for j in dom_idx]))
+    dom_us = 1e3 * float(np.mean([np.mean(dom_durs[j]) for j in dom_idx]))
+    achieved = dom_bytes / (dom_us * 1e-6) / 1e9
+    traffic = committed_traffic(wl)
+
+    line = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32" if wl.name != "rows1000" else "f32,bf16,f16",
+        "data": "synthetic",
+        "config": dict({"workload": "%s: %s" % (wl.name, wl.desc)}, **wl.config),
+        "pct_of_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
+        "roofline": {"bound": "hbm", "kernel": wl.calls[dom_idx[0]].kernel,
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic,
+                     "bytes_per_launch": dom_bytes, "mean_launch_us": round(dom_us, 3)},
+        "per_call": per_call,
+        "device": {"name": props.name, "cus": props.multi_processor_count},
+    }
+    if args.cpu_seconds > 0:
+        log("timing the CPU oracle (~%.0f s)" % args.cpu_seconds)
+        line["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
+    else:
+        line["cpu_baseline"] = None
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -14,6 +14,11 @@ Names follow the C ABI:
     sum_f32_atomic / max_f32_atomic / min_f32_atomic (same)
     sum_rows_f32 / max_rows_f32 / min_rows_f32 (x, out, n=None, accum=False)
     colprod_f32 / colprod_f16 / colprod_bf16 / colprod_i32 (src, out, C=None)
+
+``plan(name, *args, **kwargs)`` marshals the same arguments once and returns
+a ``Plan``; calling it enqueues the C entry point with the stored pointers,
+sizes and stream, without re-checking the tensors.  The caller keeps the
+tensors alive and unchanged in shape while the plan is in use.
 """
 from __future__ import annotations
 
@@ -95,6 +100,23 @@ def _check(status: int, where: str) -> None:
         raise ReduceError(status, where)
 
 
+class Plan:
+    """A C entry point with its arguments already marshalled."""
+
+    __slots__ = ("name", "fn", "args", "keep")
+
+    def __init__(self, name, args, keep):
+        self.name = name
+        self.fn = getattr(_lib, name)
+        self.args = args
+        self.keep = keep  # the tensors whose pointers are in args
+
+    def __call__(self) -> None:
+        status = self.fn(*self.args)
+        if status != RED_OK:
+            raise ReduceError(status, self.name)
+
+
 def _need(t: torch.Tensor, dtype, what: str) -> None:
     if not isinstance(t, torch.Tensor):
         raise TypeError("%s must be a torch.Tensor" % what)
@@ -110,13 +132,18 @@ def _need(t: torch.Tensor, dtype, what: str) -> None:
 # 1-D vector -> scalar
 # ---------------------------------------------------------------------------
 
-def _reduce1d(name: str, x, out, accum, stream):
+def _args_reduce1d(name: str, x, out, accum=False, stream=None):
     _need(x, torch.float32, "x")
     _need(out, torch.float32, "out")
     if out.numel() < 1:
         raise ValueError("out needs one element")
-    _check(getattr(_lib, name)(x.data_ptr(), x.numel(), out.data_ptr(),
-                               int(bool(accum)), _stream(stream)), name)
+    return (x.data_ptr(), x.numel(), out.data_ptr(), int(bool(accum)),
+            _stream(stream)), (x, out)
+
+
+def _reduce1d(name: str, x, out, accum, stream):
+    args, _ = _args_reduce1d(name, x, out, accum, stream)
+    _check(getattr(_lib, name)(*args), name)
     return out
 
 
@@ -149,7 +176,7 @@ def min_f32_atomic(x, out, accum=False, stream=None):
 # segmented rows
 # ---------------------------------------------------------------------------
 
-def _rows(name: str, x, out, n, accum, stream):
+def _args_rows(name: str, x, out, n=None, accum=False, stream=None):
     _need(x, torch.float32, "x")
     _need(out, torch.float32, "out")
     if x.dim() != 2:
@@ -160,8 +187,13 @@ def _rows(name: str, x, out, n, accum, stream):
         raise ValueError("need 0 <= n <= ld")
     if out.numel() < rows:
         raise ValueError("out needs one element per row")
-    _check(getattr(_lib, name)(x.data_ptr(), rows, n, ld, out.data_ptr(),
-                               int(bool(accum)), _stream(stream)), name)
+    return (x.data_ptr(), rows, n, ld, out.data_ptr(), int(bool(accum)),
+            _stream(stream)), (x, out)
+
+
+def _rows(name: str, x, out, n, accum, stream):
+    args, _ = _args_rows(name, x, out, n, accum, stream)
+    _check(getattr(_lib, name)(*args), name)
     return out
 
 
@@ -182,7 +214,12 @@ def min_rows_f32(x, out, n=None, accum=False, stream=None):
 # column product
 # ---------------------------------------------------------------------------
 
-def _colprod(name: str, src, out, C, dtype, stream):
+_COLPROD_DTYPE = {"red_colprod_f32": torch.float32, "red_colprod_f16": torch.float16,
+                  "red_colprod_bf16": torch.bfloat16, "red_colprod_i32": torch.int32}
+
+
+def _args_colprod(name: str, src, out, C=None, stream=None):
+    dtype = _COLPROD_DTYPE[name]
     _need(src, dtype, "src")
     _need(out, dtype, "out")
     if src.dim() != 2:
@@ -193,26 +230,51 @@ def _colprod(name: str, src, out, C, dtype, stream):
         raise ValueError("need 0 <= C <= ld")
     if out.numel() < C:
         raise ValueError("out needs C elements")
-    _check(getattr(_lib, name)(src.data_ptr(), R, C, ld, out.data_ptr(),
-                               _stream(stream)), name)
+    return (src.data_ptr(), R, C, ld, out.data_ptr(), _stream(stream)), (src, out)
+
+
+def _colprod(name: str, src, out, C, stream):
+    args, _ = _args_colprod(name, src, out, C, stream)
+    _check(getattr(_lib, name)(*args), name)
     return out
 
 
 def colprod_f32(src, out, C=None, stream=None):
     """out[j] = prod_i src[i, j] for j < C (TCOLPROD), fp32."""
-    return _colprod("red_colprod_f32", src, out, C, torch.float32, stream)
+    return _colprod("red_colprod_f32", src, out, C, stream)
 
 
 def colprod_f16(src, out, C=None, stream=None):
     """binary16 tile (torch.float16); fp32 products rounded once to fp16."""
-    return _colprod("red_colprod_f16", src, out, C, torch.float16, stream)
+    return _colprod("red_colprod_f16", src, out, C, stream)
 
 
 def colprod_bf16(src, out, C=None, stream=None):
     """bfloat16 tile (torch.bfloat16); fp32 products rounded once to bf16."""
-    return _colprod("red_colprod_bf16", src, out, C, torch.bfloat16, stream)
+    return _colprod("red_colprod_bf16", src, out, C, stream)
 
 
 def colprod_i32(src, out, C=None, stream=None):
     """int32 tile; products modulo 2^32."""
-    return _colprod("red_colprod_i32", src, out, C, torch.int32, stream)
+    return _colprod("red_colprod_i32", src, out, C, stream)
+
+
+# ---------------------------------------------------------------------------
+# pre-marshalled calls
+# ---------------------------------------------------------------------------
+
+_MARSHAL = {}
+for _op in ("sum", "max", "min"):
+    _MARSHAL["%s_f32" % _op] = ("red_%s_f32" % _op, _args_reduce1d)
+    _MARSHAL["%s_f32_atomic" % _op] = ("red_%s_f32_atomic" % _op, _args_reduce1d)
+    _MARSHAL["%s_rows_f32" % _op] = ("red_%s_rows_f32" % _op, _args_rows)
+for _t in ("f32", "f16", "bf16", "i32"):
+    _MARSHAL["colprod_" + _t] = ("red_colprod_" + _t, _args_colprod)
+
+
+def plan(name: str, *args, **kwargs) -> Plan:
+    """Marshal the arguments of entry point ``name`` (e.g. "sum_f32") once;
+    the returned Plan enqueues the call each time it is called."""
+    cname, marshal = _MARSHAL[name]
+    cargs, keep = marshal(cname, *args, **kwargs)
+    return Plan(cname, cargs, keep)

@@ -22,10 +22,9 @@ using red::DeviceInfo;
 using red::OpKind;
 using red::Workspace;
 
-// Fixed workspace per (device, stream): partial results and tickets.  The
-// kernels size their grids so that they never need more than this.
+// Fixed workspace per (device, stream) for partial results.  The kernels
+// size their grids so that they never need more than this.
 constexpr size_t kPartialBytes = size_t(16) << 20;
-constexpr size_t kTickets = 16384;
 
 std::mutex g_mu;
 std::map<int, DeviceInfo> g_dev;
@@ -61,9 +60,7 @@ int current_device(int* dev, DeviceInfo* info)
     return RED_OK;
 }
 
-// The workspace of (dev, stream), created on first use.  Its tickets are
-// zeroed by a kernel on `stream`, so they are ready before any later kernel
-// on that stream runs.
+// The workspace of (dev, stream), created on first use.
 int stream_workspace(int dev, hipStream_t stream, Workspace* ws)
 {
     std::lock_guard<std::mutex> lock(g_mu);
@@ -78,20 +75,13 @@ int stream_workspace(int dev, hipStream_t stream, Workspace* ws)
     if (fail && fail[0] == '1')
         return RED_ERR_NOMEM;
     void* base = nullptr;
-    const size_t bytes = kPartialBytes + kTickets * sizeof(unsigned);
-    if (hipMalloc(&base, bytes) != hipSuccess) {
+    if (hipMalloc(&base, kPartialBytes) != hipSuccess) {
         (void)hipGetLastError(); // clear the sticky allocation error
         return RED_ERR_NOMEM;
     }
     Workspace w;
     w.partials = base;
     w.partial_bytes = kPartialBytes;
-    w.tickets = reinterpret_cast<unsigned*>(static_cast<char*>(base) + kPartialBytes);
-    w.n_tickets = kTickets;
-    if (red::launch_fill_u32(w.tickets, kTickets, 0u, stream) != hipSuccess) {
-        (void)hipFree(base);
-        return RED_ERR_HIP;
-    }
     g_ws.emplace(key, w);
     *ws = w;
     return RED_OK;

@@ -14,9 +14,10 @@
 //    partial products in LDS in wave order;
 //  * when the grid needs more workgroups than there are column blocks, the
 //    rows are split into S slices (blockIdx.y); each workgroup stores its
-//    partial row in the workspace and takes a ticket for its column block;
-//    the last one to arrive multiplies the S partial rows in slice order,
-//    narrows once to T and writes dst, then resets the ticket.
+//    partial row in the workspace, and a second kernel multiplies the S
+//    partial rows of each column in slice order, narrows once to T and
+//    writes dst;
+//  * tile loads are non-temporal: each element is read once.
 //
 // Arithmetic: f32, f16 and bf16 multiply in fp32 (16-bit values widen
 // exactly), i32 in uint32 (wraps modulo 2^32).  f16 / bf16 round once, to
@@ -115,8 +116,7 @@ template <class Tr, bool VEC>
 __global__ __launch_bounds__(kBlock) void colprod_kernel(
     const typename Tr::T* __restrict__ src, uint64_t R, uint64_t C,
     uint64_t ld, typename Tr::T* __restrict__ dst,
-    typename Tr::A* __restrict__ partials, unsigned* __restrict__ tickets,
-    uint64_t rows_per_split)
+    typename Tr::A* __restrict__ partials, uint64_t rows_per_split)
 {
     using T = typename Tr::T;
     using A = typename Tr::A;
@@ -124,7 +124,6 @@ __global__ __launch_bounds__(kBlock) void colprod_kernel(
     constexpr int kCols = kWave * V; // columns per workgroup
 
     __shared__ A lds[kWaves][kCols];
-    __shared__ int s_last;
 
     const uint32_t lane = threadIdx.x & (kWave - 1);
     const uint32_t wave = threadIdx.x / kWave;
@@ -149,8 +148,8 @@ __global__ __launch_bounds__(kBlock) void colprod_kernel(
                 uint4 v[kRowsInFlight];
 #pragma unroll
                 for (int u = 0; u < kRowsInFlight; ++u)
-                    v[u] = *reinterpret_cast<const uint4*>(
-                        col + (r + (uint64_t)u * kWaves) * ld);
+                    v[u] = load_stream(reinterpret_cast<const uint4*>(
+                        col + (r + (uint64_t)u * kWaves) * ld));
 #pragma unroll
                 for (int u = 0; u < kRowsInFlight; ++u) {
                     A a[V];
@@ -162,7 +161,7 @@ __global__ __launch_bounds__(kBlock) void colprod_kernel(
             }
             for (; r < r1; r += kWaves) {
                 A a[V];
-                Tr::unpack(*reinterpret_cast<const uint4*>(col + r * ld), a);
+                Tr::unpack(load_stream(reinterpret_cast<const uint4*>(col + r * ld)), a);
 #pragma unroll
                 for (int k = 0; k < V; ++k)
                     acc[k] = acc[k] * a[k];
@@ -196,35 +195,22 @@ __global__ __launch_bounds__(kBlock) void colprod_kernel(
                 partials[s * C + j] = p;
         }
     }
-    if (S == 1)
-        return;
+}
 
-    // Make this workgroup's partial row visible device-wide, then take a
-    // ticket for the column block.
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        const unsigned prev = __hip_atomic_fetch_add(
-            &tickets[cb], 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-        s_last = (prev == S - 1);
-    }
-    __syncthreads();
-    if (!s_last)
+// Second pass (S > 1): one thread per column multiplies the S partial rows
+// in slice order and narrows the product once to T.
+template <class Tr>
+__global__ __launch_bounds__(kBlock) void colprod_finish_kernel(
+    const typename Tr::A* __restrict__ partials, uint32_t S, uint64_t C,
+    typename Tr::T* __restrict__ dst)
+{
+    const uint64_t j = (uint64_t)blockIdx.x * kBlock + threadIdx.x;
+    if (j >= C)
         return;
-
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-    for (uint32_t c = threadIdx.x; c < (uint32_t)kCols; c += kBlock) {
-        const uint64_t j = cb * kCols + c;
-        if (j >= C)
-            continue;
-        A p = partials[j];
-        for (uint32_t k = 1; k < S; ++k)
-            p = p * partials[(uint64_t)k * C + j];
-        dst[j] = Tr::narrow(p);
-    }
-    if (threadIdx.x == 0)
-        __hip_atomic_store(&tickets[cb], 0u, __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
+    typename Tr::A p = partials[j];
+    for (uint32_t k = 1; k < S; ++k)
+        p = p * partials[(uint64_t)k * C + j];
+    dst[j] = Tr::narrow(p);
 }
 
 template <class Tr>
@@ -241,10 +227,13 @@ hipError_t launch_typed(const void* src, size_t R, size_t C, size_t ld,
     A* part = static_cast<A*>(ws.partials);
     if (vec)
         colprod_kernel<Tr, true><<<grid, kBlock, 0, stream>>>(
-            s, R, C, ld, d, part, ws.tickets, plan.rows_per_split);
+            s, R, C, ld, d, part, plan.rows_per_split);
     else
         colprod_kernel<Tr, false><<<grid, kBlock, 0, stream>>>(
-            s, R, C, ld, d, part, ws.tickets, plan.rows_per_split);
+            s, R, C, ld, d, part, plan.rows_per_split);
+    if (plan.splits > 1)
+        colprod_finish_kernel<Tr><<<(unsigned)((C + kBlock - 1) / kBlock), kBlock, 0, stream>>>(
+            part, plan.splits, C, d);
     return hipGetLastError();
 }
 
@@ -266,7 +255,7 @@ ColprodPlan colprod_plan(ColType t, size_t R, size_t C, const DeviceInfo& dev,
     ColprodPlan p;
     const uint64_t cols = (uint64_t)kWave * (16 / colprod_elem_size(t));
     p.col_blocks = (unsigned)((C + cols - 1) / cols);
-    const uint64_t target = (uint64_t)dev.cus * kWgPerCu;
+    const uint64_t target = (uint64_t)dev.cus * kColprodWgPerCu;
     uint64_t S = 1;
     if (p.col_blocks < target)
         S = (target + p.col_blocks - 1) / p.col_blocks;
@@ -275,8 +264,8 @@ ColprodPlan colprod_plan(ColType t, size_t R, size_t C, const DeviceInfo& dev,
         S = s_rows;
     if (S > kMaxSplits)
         S = kMaxSplits;
-    // The workspace bounds S * C partial values and the ticket count.
-    while (S > 1 && (S * C * 4 > ws.partial_bytes || p.col_blocks > ws.n_tickets))
+    // The workspace bounds S * C partial values.
+    while (S > 1 && S * C * 4 > ws.partial_bytes)
         S = (S + 1) / 2;
     if (S < 1)
         S = 1;

@@ -140,6 +140,26 @@ __device__ __forceinline__ float4 identity4()
 }
 
 // ---------------------------------------------------------------------------
+// Streaming loads.  Every input element is read exactly once, so the loads
+// carry the non-temporal hint: the lines are not kept in L2 / Infinity
+// Cache at the expense of data that is reused.
+// ---------------------------------------------------------------------------
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float4 load_stream(const float4* p)
+{
+    const f32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(p));
+    return make_float4(v.x, v.y, v.z, v.w);
+}
+
+__device__ __forceinline__ uint4 load_stream(const uint4* p)
+{
+    const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+// ---------------------------------------------------------------------------
 // Wave64 reduction with DPP.
 //
 // GFX9 DPP controls used: row_shr:k (0x110 + k) reads lane i-k of the same

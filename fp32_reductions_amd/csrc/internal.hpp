@@ -10,14 +10,12 @@ namespace red {
 
 enum class OpKind { Sum, Max, Min };
 
-// Per-(device, stream) scratch owned by the library.  Tickets must be zero
-// whenever no kernel of this library is running on the stream: every kernel
-// that takes a ticket puts it back to zero before it exits.
+// Per-(device, stream) scratch owned by the library: the partial results
+// the first pass of a reduction hands to its second pass.  Calls on one
+// stream are ordered, so they can share it.
 struct Workspace {
-    void* partials = nullptr;      // per-workgroup partial results
+    void* partials = nullptr;
     size_t partial_bytes = 0;
-    unsigned* tickets = nullptr;   // arrival counters
-    size_t n_tickets = 0;
 };
 
 // Launch geometry chosen by the host from the device.
@@ -25,11 +23,22 @@ struct DeviceInfo {
     int cus = 0;                   // compute units
 };
 
-// Workgroups launched per compute unit for the streaming kernels.
-constexpr int kWgPerCu = 8;
+// Workgroups per compute unit for the 1-D streaming kernel and for the
+// column product (measured on MI355X: fewer, longer-lived workgroups stream
+// HBM faster than a full-occupancy grid).
+#ifndef RED_STREAM_WG_PER_CU
+#define RED_STREAM_WG_PER_CU 2
+#endif
+#ifndef RED_COLPROD_WG_PER_CU
+#define RED_COLPROD_WG_PER_CU 1
+#endif
+constexpr int kStreamWgPerCu = RED_STREAM_WG_PER_CU;
+constexpr int kColprodWgPerCu = RED_COLPROD_WG_PER_CU;
+// Row count from which the row kernels use one wave per row whatever n is.
+constexpr int kRowsWavePerCu = 8;
 
 // ---- 1-D vector -> scalar (reduce1d.hip) ----------------------------------
-// Deterministic form: partials + last-arriving-workgroup finish.
+// Deterministic form: per-workgroup partials, then a one-workgroup finish.
 hipError_t launch_reduce1d(OpKind op, const float* x, size_t n, float* out,
                            int accum, const DeviceInfo& dev,
                            const Workspace& ws, hipStream_t stream);
@@ -39,7 +48,7 @@ hipError_t launch_reduce1d_atomic(OpKind op, const float* x, size_t n,
                                   hipStream_t stream);
 // Number of workgroups launch_reduce1d uses for n elements at address x.
 unsigned reduce1d_grid(const float* x, size_t n, const DeviceInfo& dev);
-// Zero `count` 32-bit words on `stream` with a kernel (no memset node).
+// Set `count` 32-bit words to `value` on `stream` with a kernel.
 hipError_t launch_fill_u32(unsigned* p, size_t count, unsigned value,
                            hipStream_t stream);
 

@@ -1,16 +1,19 @@
 // reduce1d.hip -- 1-D fp32 vector -> scalar (sum / max / min, accum).
 //
-// One kernel per call.  Each thread streams its share of the vector in
-// grid-stride order with 16-byte (dwordx4) loads, eight loads in flight,
-// into a per-thread multi-wide accumulator; the accumulator collapses along
-// a fixed tree, the wave reduces with DPP, the workgroup through LDS.
+// The vector is cut into one contiguous chunk per workgroup (two workgroups
+// per compute unit); each thread streams its share of the chunk in sweeps
+// of eight non-temporal 16-byte (dwordx4) loads in flight into a per-thread
+// multi-wide accumulator, which collapses along a fixed tree; the wave
+// reduces with DPP and the workgroup through LDS.  (Measured on MI355X: contiguous chunks at two workgroups per CU
+// stream at ~7.1 TB/s for 1 GiB; a grid-stride walk with eight workgroups
+// per CU stayed near 5 TB/s.)
 //
 // The cross-workgroup step takes one of two forms:
-//  * deterministic (default): every workgroup stores its partial, then
-//    takes a ticket with a device-scope atomic; the workgroup that draws the
-//    last ticket combines all partials in index order (folding the old
-//    destination first under accum), writes the scalar and returns the
-//    ticket counter to zero.  No second kernel launch.
+//  * deterministic (default): every workgroup stores its partial; a second,
+//    one-workgroup kernel combines the partials in index order (folding the
+//    old destination first under accum) and writes the scalar.  (Measured
+//    on MI355X for 64 MiB: 13.5 us per call, against 15-16 us for a single
+//    kernel whose last-arriving workgroup finishes behind atomic counters.)
 //  * atomic: every workgroup folds its partial into the destination with
 //    one device-scope atomic, the structure of the block reduce in the
 //    imxueqiu.com blog post on a Triton vector-sum kernel (warp reduce,
@@ -22,10 +25,15 @@
 #include "device.hpp"
 #include "internal.hpp"
 
+#ifndef RED_STREAM_UNROLL
+#define RED_STREAM_UNROLL 8
+#endif
+
 namespace red {
 namespace {
 
-constexpr int kUnroll = 8; // float4 loads in flight per thread
+constexpr int kUnroll = RED_STREAM_UNROLL;         // 16-byte loads in flight per thread
+constexpr uint64_t kSweep = (uint64_t)kBlock * kUnroll; // vectors per workgroup sweep
 
 // Elements before the first 16-byte boundary of x (x is 4-byte aligned).
 __host__ __device__ inline uint32_t head_count(const float* x, uint64_t n)
@@ -35,32 +43,36 @@ __host__ __device__ inline uint32_t head_count(const float* x, uint64_t n)
     return (uint32_t)(h < n ? h : n);
 }
 
-// Per-thread part: grid-stride stream + scalar head / tail, then the
-// thread's collapse.  Returns the thread's value.
+// Per-thread part: this workgroup's contiguous chunk of whole vectors, plus
+// (workgroup 0, thread 0) the scalar head and tail; then the collapse.
 template <class Op>
 __device__ __forceinline__ float thread_part(const float* __restrict__ x,
-                                             uint64_t n, float first)
+                                             uint64_t n)
 {
     const uint32_t head = head_count(x, n);
     const uint64_t nvec = (n - head) / 4;
-    const uint64_t T = (uint64_t)gridDim.x * kBlock;
-    const uint64_t t = (uint64_t)blockIdx.x * kBlock + threadIdx.x;
     const float4* __restrict__ xv = reinterpret_cast<const float4*>(x + head);
 
-    Acc<Op> acc(first);
-    uint64_t i = t;
-    for (; i + (kUnroll - 1) * T < nvec; i += kUnroll * T) {
+    // Chunk of whole sweeps; the last chunks may be short or empty.
+    const uint64_t per_wg = (nvec + gridDim.x - 1) / gridDim.x;
+    const uint64_t per = (per_wg + kSweep - 1) / kSweep * kSweep;
+    const uint64_t b0 = (uint64_t)blockIdx.x * per;
+    const uint64_t b1 = (b0 + per < nvec) ? b0 + per : nvec;
+
+    Acc<Op> acc(Op::identity());
+    uint64_t i = b0 + threadIdx.x;
+    for (; i + (uint64_t)(kUnroll - 1) * kBlock < b1; i += kSweep) {
         float4 v[kUnroll];
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u)
-            v[u] = xv[i + u * T];
+            v[u] = load_stream(xv + i + (uint64_t)u * kBlock);
 #pragma unroll
         for (int u = 0; u < kUnroll; u += 2)
             acc.fold2(v[u], v[u + 1]);
     }
-    for (; i < nvec; i += T)
-        acc.fold1(xv[i]);
-    if (t == 0) {
+    for (; i < b1; i += kBlock)
+        acc.fold1(load_stream(xv + i));
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
         for (uint32_t k = 0; k < head; ++k)
             acc.fold_scalar(x[k]);
         for (uint64_t k = head + 4 * nvec; k < n; ++k)
@@ -69,41 +81,35 @@ __device__ __forceinline__ float thread_part(const float* __restrict__ x,
     return acc.collapse();
 }
 
+// First pass: each workgroup writes its partial to partials[blockIdx.x].
 template <class Op>
-__global__ __launch_bounds__(kBlock) void reduce1d_kernel(
-    const float* __restrict__ x, uint64_t n, float* __restrict__ out,
-    int accum, float* __restrict__ partials, unsigned* __restrict__ ticket)
+__global__ __launch_bounds__(kBlock) void reduce1d_stream_kernel(
+    const float* __restrict__ x, uint64_t n, float* __restrict__ partials)
 {
     __shared__ float lds[kWaves];
-    __shared__ int s_last;
-
-    const float r = block_reduce<Op>(thread_part<Op>(x, n, Op::identity()), lds);
-
-    // Publish this workgroup's partial; the release half of the ticket RMW
-    // orders the store before the ticket.
-    if (threadIdx.x == 0) {
+    const float r = block_reduce<Op>(thread_part<Op>(x, n), lds);
+    if (threadIdx.x == 0)
         partials[blockIdx.x] = r;
-        const unsigned prev = __hip_atomic_fetch_add(
-            ticket, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-        s_last = (prev == gridDim.x - 1);
-    }
-    __syncthreads();
-    if (!s_last)
-        return;
+}
 
-    // Last workgroup: every partial is visible after the acquire.
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+// Second pass, one workgroup: combine the G partials in index order (each
+// thread folds partials t, t + 256, ..., then the workgroup tree), with the
+// old destination in the first slot under accum.  The kernel boundary makes
+// the first pass's stores visible; no atomics are involved.
+template <class Op>
+__global__ __launch_bounds__(kBlock) void reduce1d_finish_kernel(
+    const float* __restrict__ partials, unsigned G, float* __restrict__ out,
+    int accum)
+{
+    __shared__ float lds[kWaves];
     float v = Op::identity();
     if (threadIdx.x == 0 && accum)
-        v = *out; // the old destination takes the first slot
-    for (unsigned k = threadIdx.x; k < gridDim.x; k += kBlock)
+        v = *out;
+    for (unsigned k = threadIdx.x; k < G; k += kBlock)
         v = Op::apply(v, partials[k]);
     const float total = block_reduce<Op>(v, lds);
-    if (threadIdx.x == 0) {
+    if (threadIdx.x == 0)
         *out = total;
-        __hip_atomic_store(ticket, 0u, __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
-    }
 }
 
 // Fold r into *out with maxNum / minNum semantics by compare-and-swap.
@@ -130,7 +136,7 @@ __global__ __launch_bounds__(kBlock) void reduce1d_atomic_kernel(
     const float* __restrict__ x, uint64_t n, float* __restrict__ out)
 {
     __shared__ float lds[kWaves];
-    const float r = block_reduce<Op>(thread_part<Op>(x, n, Op::identity()), lds);
+    const float r = block_reduce<Op>(thread_part<Op>(x, n), lds);
     if (threadIdx.x == 0) {
         if constexpr (__is_same(Op, OpSum))
             unsafeAtomicAdd(out, r); // hardware global_atomic_add_f32
@@ -151,8 +157,9 @@ template <class Op>
 hipError_t launch_det(const float* x, size_t n, float* out, int accum,
                       unsigned grid, const Workspace& ws, hipStream_t stream)
 {
-    reduce1d_kernel<Op><<<grid, kBlock, 0, stream>>>(
-        x, n, out, accum, static_cast<float*>(ws.partials), ws.tickets);
+    float* partials = static_cast<float*>(ws.partials);
+    reduce1d_stream_kernel<Op><<<grid, kBlock, 0, stream>>>(x, n, partials);
+    reduce1d_finish_kernel<Op><<<1, kBlock, 0, stream>>>(partials, grid, out, accum);
     return hipGetLastError();
 }
 
@@ -175,9 +182,8 @@ hipError_t launch_atomic(const float* x, size_t n, float* out, int accum,
 unsigned reduce1d_grid(const float* x, size_t n, const DeviceInfo& dev)
 {
     const uint64_t nvec = (n - head_count(x, n)) / 4;
-    const uint64_t per_wg = (uint64_t)kBlock * kUnroll; // vectors per sweep
-    uint64_t g = (nvec + per_wg - 1) / per_wg;
-    const uint64_t cap = (uint64_t)dev.cus * kWgPerCu;
+    uint64_t g = (nvec + kSweep - 1) / kSweep;
+    const uint64_t cap = (uint64_t)dev.cus * kStreamWgPerCu;
     if (g > cap)
         g = cap;
     if (g < 1)
@@ -190,7 +196,7 @@ hipError_t launch_reduce1d(OpKind op, const float* x, size_t n, float* out,
                            const Workspace& ws, hipStream_t stream)
 {
     const unsigned grid = reduce1d_grid(x, n, dev);
-    if ((size_t)grid * sizeof(float) > ws.partial_bytes || ws.n_tickets < 1)
+    if ((size_t)grid * sizeof(float) > ws.partial_bytes)
         return hipErrorInvalidValue;
     switch (op) {
     case OpKind::Sum: return launch_det<OpSum>(x, n, out, accum, grid, ws, stream);

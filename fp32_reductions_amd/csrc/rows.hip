@@ -12,8 +12,8 @@
 //    accum adds the old destination into slot 0 first ("How inputs change
 //    the algorithm").  max / min use four slots folded with max3 / min3.
 //  * rows_wave: one wave64 per row; each lane keeps the multi-wide
-//    accumulator over 16-byte loads (four in flight), then a DPP wave
-//    reduce; lane 0 stores.  No LDS, no second pass.
+//    accumulator over non-temporal 16-byte loads (four in flight), then a
+//    DPP wave reduce; lane 0 stores.  No LDS, no second pass.
 //  * rows_block: one 256-thread workgroup per row, for few very long rows.
 #include "device.hpp"
 #include "internal.hpp"
@@ -142,7 +142,7 @@ __device__ __forceinline__ float row_lane_part(const float* __restrict__ p,
 #pragma unroll
         for (int u = 0; u < kRowUnroll; ++u) {
             const uint64_t idx = base + (uint64_t)u * LANES;
-            v[u] = idx < nvec ? pv[idx] : identity4<Op>();
+            v[u] = idx < nvec ? load_stream(pv + idx) : identity4<Op>();
         }
 #pragma unroll
         for (int u = 0; u < kRowUnroll; u += 2)
@@ -213,7 +213,7 @@ hipError_t launch_rows_op(const float* x, size_t rows, size_t n, size_t ld,
         else
             rows_thread_kernel<Op, false><<<grid, kBlock, 0, stream>>>(
                 x, rows, (uint32_t)n, ld, out, accum);
-    } else if (n <= kWaveRowMax || rows >= (size_t)dev.cus * kWgPerCu) {
+    } else if (n <= kWaveRowMax || rows >= (size_t)dev.cus * kRowsWavePerCu) {
         const unsigned grid = cap_grid((rows + kWaves - 1) / kWaves);
         rows_wave_kernel<Op><<<grid, kBlock, 0, stream>>>(x, rows, n, ld, out,
                                                           accum);

@@ -198,3 +198,19 @@ def test_deterministic(red, vec16m):
             getattr(red, op + "_f32")(xd, out)
         s.synchronize()
         assert host(out)[0].tobytes() == np.float32(ref).tobytes()
+
+
+def test_plan_matches_call(red, vec16m):
+    """A pre-marshalled plan enqueues the same call: same bits."""
+    say("plan vs call")
+    _, xd = vec16m
+    for op in OPS:
+        ref = run(red, op, xd, True, 1.25)
+        out = torch.full((1,), 1.25, dtype=torch.float32, device="cuda")
+        p = red.plan(op + "_f32", xd, out, accum=True)
+        p()
+        assert host(out)[0].tobytes() == np.float32(ref).tobytes()
+    with pytest.raises(red.ReduceError):
+        bad = red.plan("sum_f32", xd, torch.zeros(1, device="cuda"))
+        bad.args = (0,) + bad.args[1:]  # a null input pointer is rejected
+        bad()
