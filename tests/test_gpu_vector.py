@@ -41,6 +41,9 @@ def check(orc, op, x, got, accum=False, old=0.0, what=""):
     if op == "sum":
         s, a = orc.sum_f32(x, accum, old)
         check_sum(got, s, a, what)
+        if a > 0 and x.size >= (1 << 20):
+            say("%s: |gpu - exact| / sum|x| = %.3g (tolerance 1e-6)"
+                % (what, abs(float(got) - s) / a))
     elif op == "max":
         check_exact(got, orc.max_f32(x, accum, old), what)
     else:
