@@ -11,9 +11,12 @@
 //    (0,1)+=(2,3), (4,5)+=(6,7), (0,1)+=(4,5), result = slot 0 + slot 1.
 //    accum adds the old destination into slot 0 first ("How inputs change
 //    the algorithm").  max / min use four slots folded with max3 / min3.
-//  * rows_wave: one wave64 per row; each lane keeps the multi-wide
-//    accumulator over non-temporal 16-byte loads (four in flight), then a
-//    DPP wave reduce; lane 0 stores.  No LDS, no second pass.
+//  * rows_wave2 (64 < n <= 1024): one wave64 per pair of rows; each lane
+//    issues its four non-temporal 16-byte loads of both rows, keeps one
+//    multi-wide accumulator per row, then two DPP wave reduces; lane 0
+//    stores.  No LDS, no second pass.
+//  * rows_wave: the same with one row per wave and any n, looping over the
+//    row four vectors per lane at a time.
 //  * rows_block: one 256-thread workgroup per row, for few very long rows.
 #include "device.hpp"
 #include "internal.hpp"
@@ -156,6 +159,10 @@ __device__ __forceinline__ float row_lane_part(const float* __restrict__ p,
     return acc.collapse();
 }
 
+// Two rows per wave at a time when both are short enough for one sweep:
+// all of both rows' loads are issued before either row is reduced.
+constexpr uint64_t kPairRowMax = (uint64_t)kWave * kRowUnroll * 4; // 1024 elements
+
 template <class Op>
 __global__ __launch_bounds__(kBlock) void rows_wave_kernel(
     const float* __restrict__ x, uint64_t rows, uint64_t n, uint64_t ld,
@@ -171,6 +178,56 @@ __global__ __launch_bounds__(kBlock) void rows_wave_kernel(
         const float total = wave_reduce<Op>(v);
         if (lane == 0)
             out[r] = total;
+    }
+}
+
+// Rows of at most kPairRowMax elements: each wave takes rows 2w and 2w + 1
+// of its stride, loading both before reducing.
+template <class Op>
+__global__ __launch_bounds__(kBlock) void rows_wave2_kernel(
+    const float* __restrict__ x, uint64_t rows, uint64_t n, uint64_t ld,
+    float* __restrict__ out, int accum)
+{
+    const uint32_t lane = threadIdx.x & (kWave - 1);
+    const uint64_t stride = (uint64_t)gridDim.x * kWaves * 2;
+    for (uint64_t r = ((uint64_t)blockIdx.x * kWaves + threadIdx.x / kWave) * 2;
+         r < rows; r += stride) {
+        const bool second = r + 1 < rows; // uniform across the wave
+        const float* __restrict__ p0 = x + r * ld;
+        const float* __restrict__ p1 = second ? p0 + ld : p0;
+        const uint32_t h0 = head_count(p0, n), h1 = head_count(p1, n);
+        const uint64_t nv0 = (n - h0) / 4, nv1 = (n - h1) / 4;
+        const float4* __restrict__ v0 = reinterpret_cast<const float4*>(p0 + h0);
+        const float4* __restrict__ v1 = reinterpret_cast<const float4*>(p1 + h1);
+        float4 a[kRowUnroll], b[kRowUnroll];
+#pragma unroll
+        for (int u = 0; u < kRowUnroll; ++u) {
+            const uint64_t idx = lane + (uint64_t)u * kWave;
+            a[u] = idx < nv0 ? load_stream(v0 + idx) : identity4<Op>();
+            b[u] = (second && idx < nv1) ? load_stream(v1 + idx) : identity4<Op>();
+        }
+        Acc<Op> acc0((lane == 0 && accum) ? out[r] : Op::identity());
+        Acc<Op> acc1((lane == 0 && accum && second) ? out[r + 1] : Op::identity());
+#pragma unroll
+        for (int u = 0; u < kRowUnroll; u += 2) {
+            acc0.fold2(a[u], a[u + 1]);
+            acc1.fold2(b[u], b[u + 1]);
+        }
+        if (lane < h0)
+            acc0.fold_scalar(p0[lane]);
+        if (lane < h1)
+            acc1.fold_scalar(p1[lane]);
+        if (h0 + 4 * nv0 + lane < n)
+            acc0.fold_scalar(p0[h0 + 4 * nv0 + lane]);
+        if (h1 + 4 * nv1 + lane < n)
+            acc1.fold_scalar(p1[h1 + 4 * nv1 + lane]);
+        const float t0 = wave_reduce<Op>(acc0.collapse());
+        const float t1 = wave_reduce<Op>(acc1.collapse());
+        if (lane == 0) {
+            out[r] = t0;
+            if (second)
+                out[r + 1] = t1;
+        }
     }
 }
 
@@ -213,6 +270,10 @@ hipError_t launch_rows_op(const float* x, size_t rows, size_t n, size_t ld,
         else
             rows_thread_kernel<Op, false><<<grid, kBlock, 0, stream>>>(
                 x, rows, (uint32_t)n, ld, out, accum);
+    } else if (n <= kPairRowMax) {
+        const unsigned grid = cap_grid((rows + 2 * kWaves - 1) / (2 * kWaves));
+        rows_wave2_kernel<Op><<<grid, kBlock, 0, stream>>>(x, rows, n, ld, out,
+                                                           accum);
     } else if (n <= kWaveRowMax || rows >= (size_t)dev.cus * kRowsWavePerCu) {
         const unsigned grid = cap_grid((rows + kWaves - 1) / kWaves);
         rows_wave_kernel<Op><<<grid, kBlock, 0, stream>>>(x, rows, n, ld, out,
