@@ -26,7 +26,8 @@ different kernel source.
 ``cpu_baseline`` times the CPU oracle (single-threaded, as written) on whole
 steps of the same workload for about ten seconds, as a reference point only.
 
-Other workloads (--workload): vec1g (2^30+7 vector), colprod4k (4096 x 16384
+Other workloads (--workload): vec16m_fused (the same vector, sum / max / min
+from one read per call), vec1g (2^30+7 vector), colprod4k (4096 x 16384
 f32 and i32 column products), rows1000 (65536 x 1000 row sum / max, then
 2048 x 32768 bf16 / f16 column products), rows32 (4096 x 32 rows, 16 x 16
 tile), copycal (a plain device copy, for counter calibration).
@@ -191,6 +192,32 @@ def wl_vec16m(torch, red, orc, steps):
         calls, ["sum"], ["reduce1d.hip", "device.hpp"], cpu)
 
 
+def wl_vec16m_fused(torch, red, orc, steps):
+    x = workloads.vec16m()
+    n = x.size
+    xs = Rotor(up(torch, x), 2, 2 * 4 * n)
+    outs = torch.zeros((steps, 3), dtype=torch.float32, device="cuda")
+    accs = torch.full((steps, 3), workloads.ACCUM_PRESET, dtype=torch.float32,
+                      device="cuda")
+    kern = "reduce1d_summaxmin_stream_kernel + reduce1d_summaxmin_finish_kernel"
+    calls = [Call("sum_max_min", kern, 4 * n + 12,
+                  lambda k: red.plan("sum_max_min_f32", xs.next(), outs[k])),
+             Call("sum_max_min_accum", kern, 4 * n + 24,
+                  lambda k: red.plan("sum_max_min_f32", xs.next(), accs[k], accum=True))]
+
+    def oracle_all(accum):
+        return (orc.sum_f32(x, accum, 3.25), orc.max_f32(x, accum, 3.25),
+                orc.min_f32(x, accum, 3.25))
+    cpu = [(4 * n + 12, lambda: oracle_all(False)), (4 * n + 24, lambda: oracle_all(True))]
+    return Workload(
+        "vec16m_fused",
+        "one fp32 vector of 2^24 elements, uniform[-1,1), seed 1; sum, max and min "
+        "from one read (fused call), then again with accum into destinations preset "
+        "to 3.25",
+        {"n": n, "calls_per_step": 2, "cold_copies": len(xs)},
+        calls, ["sum_max_min"], ["reduce1d.hip", "device.hpp"], cpu)
+
+
 def wl_vec1g(torch, red, orc, steps):
     log("generating 2^30+7 vector")
     x = workloads.vec1g()
@@ -311,7 +338,7 @@ def wl_copycal(torch, red, orc, steps):
                     calls, ["copy"], [], [])
 
 
-WORKLOADS = {"vec16m": wl_vec16m, "vec1g": wl_vec1g, "colprod4k": wl_colprod4k,
+WORKLOADS = {"vec16m": wl_vec16m, "vec16m_fused": wl_vec16m_fused, "vec1g": wl_vec1g, "colprod4k": wl_colprod4k,
              "rows1000": wl_rows1000, "rows32": wl_rows32, "copycal": wl_copycal}
 
 

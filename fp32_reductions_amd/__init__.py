@@ -6,11 +6,12 @@ passes their device pointers and the current HIP stream, and turns a
 non-zero status into ``ReduceError``.  Every step of the reduction runs in
 the HIP kernels of ``libreduce.so``; there is no CPU fallback.  Importing
 this package raises if the library has not been built
-(``python -m fp32_reductions_amd.build``).
+(``python fp32_reductions_amd/build.py``).
 
 Names follow the C ABI:
 
     sum_f32 / max_f32 / min_f32 (x, out, accum=False, stream=None)
+    sum_max_min_f32 (x, out[3], accum=False, stream=None)
     sum_f32_atomic / max_f32_atomic / min_f32_atomic (same)
     sum_rows_f32 / max_rows_f32 / min_rows_f32 (x, out, n=None, accum=False)
     colprod_f32 / colprod_f16 / colprod_bf16 / colprod_i32 (src, out, C=None)
@@ -42,7 +43,7 @@ class ReduceError(RuntimeError):
 if not os.path.exists(LIBRARY):
     raise ImportError(
         "libreduce.so is not built at %s; run "
-        "'python -m fp32_reductions_amd.build' (hipcc, gfx950)" % LIBRARY)
+        "'python fp32_reductions_amd/build.py' (hipcc, gfx950)" % LIBRARY)
 
 _lib = ctypes.CDLL(LIBRARY)
 
@@ -51,6 +52,7 @@ _SIGS = {
     "red_sum_f32": [_P, _SZ, _P, _I, _P],
     "red_max_f32": [_P, _SZ, _P, _I, _P],
     "red_min_f32": [_P, _SZ, _P, _I, _P],
+    "red_sum_max_min_f32": [_P, _SZ, _P, _I, _P],
     "red_sum_f32_atomic": [_P, _SZ, _P, _I, _P],
     "red_max_f32_atomic": [_P, _SZ, _P, _I, _P],
     "red_min_f32_atomic": [_P, _SZ, _P, _I, _P],
@@ -135,8 +137,9 @@ def _need(t: torch.Tensor, dtype, what: str) -> None:
 def _args_reduce1d(name: str, x, out, accum=False, stream=None):
     _need(x, torch.float32, "x")
     _need(out, torch.float32, "out")
-    if out.numel() < 1:
-        raise ValueError("out needs one element")
+    need = 3 if name == "red_sum_max_min_f32" else 1
+    if out.numel() < need:
+        raise ValueError("out needs %d element(s)" % need)
     return (x.data_ptr(), x.numel(), out.data_ptr(), int(bool(accum)),
             _stream(stream)), (x, out)
 
@@ -158,6 +161,11 @@ def max_f32(x, out, accum=False, stream=None):
 
 def min_f32(x, out, accum=False, stream=None):
     return _reduce1d("red_min_f32", x, out, accum, stream)
+
+
+def sum_max_min_f32(x, out, accum=False, stream=None):
+    """out[0:3] = [out[0:3] (+, max, min)] (sum, max, min) of x, one read."""
+    return _reduce1d("red_sum_max_min_f32", x, out, accum, stream)
 
 
 def sum_f32_atomic(x, out, accum=False, stream=None):
@@ -268,6 +276,7 @@ for _op in ("sum", "max", "min"):
     _MARSHAL["%s_f32" % _op] = ("red_%s_f32" % _op, _args_reduce1d)
     _MARSHAL["%s_f32_atomic" % _op] = ("red_%s_f32_atomic" % _op, _args_reduce1d)
     _MARSHAL["%s_rows_f32" % _op] = ("red_%s_rows_f32" % _op, _args_rows)
+_MARSHAL["sum_max_min_f32"] = ("red_sum_max_min_f32", _args_reduce1d)
 for _t in ("f32", "f16", "bf16", "i32"):
     _MARSHAL["colprod_" + _t] = ("red_colprod_" + _t, _args_colprod)
 

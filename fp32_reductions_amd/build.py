@@ -1,6 +1,9 @@
 """Build libreduce.so for gfx950 with hipcc, in-tree.
 
-    python -m fp32_reductions_amd.build
+    python fp32_reductions_amd/build.py
+
+(Run it as a file, or load it by path: importing the package would first
+load the library being rebuilt.)
 
 Each translation unit under csrc/ compiles to an object in csrc/_build/
 (in parallel), and the objects link into fp32_reductions_amd/libreduce.so.

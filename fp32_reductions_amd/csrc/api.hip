@@ -119,6 +119,25 @@ int reduce1d(OpKind op, const float* x, size_t n, float* out, int accum,
     return hip_status(red::launch_reduce1d(op, x, n, out, accum, info, ws, s));
 }
 
+int reduce1d_summaxmin(const float* x, size_t n, float* out, int accum,
+                       red_stream_t stream)
+{
+    if (n == 0)
+        return RED_OK;
+    int st = check_1d(x, n, out);
+    if (st != RED_OK)
+        return st;
+    int dev;
+    DeviceInfo info;
+    if ((st = current_device(&dev, &info)) != RED_OK)
+        return st;
+    Workspace ws;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    if ((st = stream_workspace(dev, s, &ws)) != RED_OK)
+        return st;
+    return hip_status(red::launch_reduce1d_summaxmin(x, n, out, accum, info, ws, s));
+}
+
 int reduce1d_atomic(OpKind op, const float* x, size_t n, float* out, int accum,
                     red_stream_t stream)
 {
@@ -197,6 +216,11 @@ int red_max_f32(const float* x, size_t n, float* out, int accum, red_stream_t st
 int red_min_f32(const float* x, size_t n, float* out, int accum, red_stream_t stream)
 {
     return reduce1d(OpKind::Min, x, n, out, accum, stream);
+}
+
+int red_sum_max_min_f32(const float* x, size_t n, float* out, int accum, red_stream_t stream)
+{
+    return reduce1d_summaxmin(x, n, out, accum, stream);
 }
 
 int red_sum_f32_atomic(const float* x, size_t n, float* out, int accum, red_stream_t stream)

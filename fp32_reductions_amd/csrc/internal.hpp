@@ -42,6 +42,10 @@ constexpr int kRowsWavePerCu = 8;
 hipError_t launch_reduce1d(OpKind op, const float* x, size_t n, float* out,
                            int accum, const DeviceInfo& dev,
                            const Workspace& ws, hipStream_t stream);
+// Fused: out[0..3) = sum, max, min of x from one read of x.
+hipError_t launch_reduce1d_summaxmin(const float* x, size_t n, float* out,
+                                     int accum, const DeviceInfo& dev,
+                                     const Workspace& ws, hipStream_t stream);
 // Single-pass form: one device-scope atomic per workgroup.
 hipError_t launch_reduce1d_atomic(OpKind op, const float* x, size_t n,
                                   float* out, int accum, const DeviceInfo& dev,

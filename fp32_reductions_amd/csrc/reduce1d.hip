@@ -14,6 +14,8 @@
 //    old destination first under accum) and writes the scalar.  (Measured
 //    on MI355X for 64 MiB: 13.5 us per call, against 15-16 us for a single
 //    kernel whose last-arriving workgroup finishes behind atomic counters.)
+//  * fused: sum, max and min of the same vector from one read of it; each
+//    result is bit-identical to the single-operation call's;
 //  * atomic: every workgroup folds its partial into the destination with
 //    one device-scope atomic, the structure of the block reduce in the
 //    imxueqiu.com blog post on a Triton vector-sum kernel (warp reduce,
@@ -43,11 +45,11 @@ __host__ __device__ inline uint32_t head_count(const float* x, uint64_t n)
     return (uint32_t)(h < n ? h : n);
 }
 
-// Per-thread part: this workgroup's contiguous chunk of whole vectors, plus
-// (workgroup 0, thread 0) the scalar head and tail; then the collapse.
-template <class Op>
-__device__ __forceinline__ float thread_part(const float* __restrict__ x,
-                                             uint64_t n)
+// Per-thread streaming: this workgroup's contiguous chunk of whole vectors,
+// plus (workgroup 0, thread 0) the scalar head and tail, folded into `acc`.
+template <class AccT>
+__device__ __forceinline__ void stream_part(const float* __restrict__ x,
+                                            uint64_t n, AccT& acc)
 {
     const uint32_t head = head_count(x, n);
     const uint64_t nvec = (n - head) / 4;
@@ -59,7 +61,6 @@ __device__ __forceinline__ float thread_part(const float* __restrict__ x,
     const uint64_t b0 = (uint64_t)blockIdx.x * per;
     const uint64_t b1 = (b0 + per < nvec) ? b0 + per : nvec;
 
-    Acc<Op> acc(Op::identity());
     uint64_t i = b0 + threadIdx.x;
     for (; i + (uint64_t)(kUnroll - 1) * kBlock < b1; i += kSweep) {
         float4 v[kUnroll];
@@ -78,8 +79,47 @@ __device__ __forceinline__ float thread_part(const float* __restrict__ x,
         for (uint64_t k = head + 4 * nvec; k < n; ++k)
             acc.fold_scalar(x[k]);
     }
+}
+
+template <class Op>
+__device__ __forceinline__ float thread_part(const float* __restrict__ x,
+                                             uint64_t n)
+{
+    Acc<Op> acc(Op::identity());
+    stream_part(x, n, acc);
     return acc.collapse();
 }
+
+// Sum, max and min of one stream at once.  Each part is the accumulator the
+// single-operation kernels use, fed the same elements in the same order, so
+// each result equals the corresponding single-operation result bit for bit.
+struct AccSumMaxMin {
+    Acc<OpSum> sum;
+    Acc<OpMax> max;
+    Acc<OpMin> min;
+    __device__ __forceinline__ AccSumMaxMin()
+        : sum(OpSum::identity()), max(OpMax::identity()), min(OpMin::identity())
+    {
+    }
+    __device__ __forceinline__ void fold2(const float4& a, const float4& b)
+    {
+        sum.fold2(a, b);
+        max.fold2(a, b);
+        min.fold2(a, b);
+    }
+    __device__ __forceinline__ void fold1(const float4& a)
+    {
+        sum.fold1(a);
+        max.fold1(a);
+        min.fold1(a);
+    }
+    __device__ __forceinline__ void fold_scalar(float v)
+    {
+        sum.fold_scalar(v);
+        max.fold_scalar(v);
+        min.fold_scalar(v);
+    }
+};
 
 // First pass: each workgroup writes its partial to partials[blockIdx.x].
 template <class Op>
@@ -110,6 +150,52 @@ __global__ __launch_bounds__(kBlock) void reduce1d_finish_kernel(
     const float total = block_reduce<Op>(v, lds);
     if (threadIdx.x == 0)
         *out = total;
+}
+
+// Fused first pass: partials[b], partials[G + b], partials[2G + b] receive
+// workgroup b's sum, max and min.
+__global__ __launch_bounds__(kBlock) void reduce1d_summaxmin_stream_kernel(
+    const float* __restrict__ x, uint64_t n, float* __restrict__ partials)
+{
+    __shared__ float lds[3][kWaves];
+    AccSumMaxMin acc;
+    stream_part(x, n, acc);
+    const float rs = block_reduce<OpSum>(acc.sum.collapse(), lds[0]);
+    const float rx = block_reduce<OpMax>(acc.max.collapse(), lds[1]);
+    const float rn = block_reduce<OpMin>(acc.min.collapse(), lds[2]);
+    if (threadIdx.x == 0) {
+        partials[blockIdx.x] = rs;
+        partials[gridDim.x + blockIdx.x] = rx;
+        partials[2 * gridDim.x + blockIdx.x] = rn;
+    }
+}
+
+// Fused second pass: out[0] = sum, out[1] = max, out[2] = min, each folded
+// exactly as the single-operation finish folds it.
+__global__ __launch_bounds__(kBlock) void reduce1d_summaxmin_finish_kernel(
+    const float* __restrict__ partials, unsigned G, float* __restrict__ out,
+    int accum)
+{
+    __shared__ float lds[3][kWaves];
+    float vs = OpSum::identity(), vx = OpMax::identity(), vn = OpMin::identity();
+    if (threadIdx.x == 0 && accum) {
+        vs = out[0];
+        vx = out[1];
+        vn = out[2];
+    }
+    for (unsigned k = threadIdx.x; k < G; k += kBlock) {
+        vs = OpSum::apply(vs, partials[k]);
+        vx = OpMax::apply(vx, partials[G + k]);
+        vn = OpMin::apply(vn, partials[2 * G + k]);
+    }
+    const float ts = block_reduce<OpSum>(vs, lds[0]);
+    const float tx = block_reduce<OpMax>(vx, lds[1]);
+    const float tn = block_reduce<OpMin>(vn, lds[2]);
+    if (threadIdx.x == 0) {
+        out[0] = ts;
+        out[1] = tx;
+        out[2] = tn;
+    }
 }
 
 // Fold r into *out with maxNum / minNum semantics by compare-and-swap.
@@ -178,6 +264,19 @@ hipError_t launch_atomic(const float* x, size_t n, float* out, int accum,
 }
 
 } // namespace
+
+hipError_t launch_reduce1d_summaxmin(const float* x, size_t n, float* out,
+                                     int accum, const DeviceInfo& dev,
+                                     const Workspace& ws, hipStream_t stream)
+{
+    const unsigned grid = reduce1d_grid(x, n, dev);
+    if ((size_t)grid * 3 * sizeof(float) > ws.partial_bytes)
+        return hipErrorInvalidValue;
+    float* partials = static_cast<float*>(ws.partials);
+    reduce1d_summaxmin_stream_kernel<<<grid, kBlock, 0, stream>>>(x, n, partials);
+    reduce1d_summaxmin_finish_kernel<<<1, kBlock, 0, stream>>>(partials, grid, out, accum);
+    return hipGetLastError();
+}
 
 unsigned reduce1d_grid(const float* x, size_t n, const DeviceInfo& dev)
 {

@@ -101,6 +101,17 @@ int red_max_f32(const float* x, size_t n, float* out, int accum,
 int red_min_f32(const float* x, size_t n, float* out, int accum,
                 red_stream_t stream);
 
+/* Fused sum, max and min of one vector from a single read of it: out points
+ * to three fp32 values, out[0] = sum, out[1] = max, out[2] = min (under
+ * accum each folds its own old value first).  The TVM page's reduction
+ * offers these three operators on the same 1-D source ("How inputs change
+ * the algorithm", row "op"); computing them together reads x once instead
+ * of three times.  Each result is bit-identical to the corresponding
+ * red_sum_f32 / red_max_f32 / red_min_f32 result.  out must be 4-byte
+ * aligned and must not overlap x. */
+int red_sum_max_min_f32(const float* x, size_t n, float* out, int accum,
+                        red_stream_t stream);
+
 /* Single-pass variants: each workgroup folds its partial into *out with
  * one device-scope atomic, as the one-atomic-per-program block reduce in
  * the imxueqiu.com blog post on a Triton vector-sum kernel does (its

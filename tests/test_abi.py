@@ -36,8 +36,12 @@ def declared_functions():
 @pytest.fixture(scope="module")
 def lib():
     if not os.path.exists(LIBRARY):
-        from fp32_reductions_amd import build
-        build.build()
+        import importlib.util
+        spec = importlib.util.spec_from_file_location(
+            "_libreduce_build", os.path.join(ROOT, "fp32_reductions_amd", "build.py"))
+        mod = importlib.util.module_from_spec(spec)
+        spec.loader.exec_module(mod)
+        mod.build()
     return ctypes.CDLL(LIBRARY)
 
 
@@ -47,6 +51,7 @@ def test_header_declares_the_abi():
         assert "red_%s_f32" % op in names
         assert "red_%s_f32_atomic" % op in names
         assert "red_%s_rows_f32" % op in names
+    assert "red_sum_max_min_f32" in names
     for t in ("f32", "f16", "bf16", "i32"):
         assert "red_colprod_" + t in names
     assert "red_status_str" in names and "red_abi_version" in names
@@ -82,6 +87,7 @@ def _fn(lib, name, argtypes):
 
 
 @pytest.mark.parametrize("name", ["red_sum_f32", "red_max_f32", "red_min_f32",
+                                  "red_sum_max_min_f32",
                                   "red_sum_f32_atomic", "red_max_f32_atomic",
                                   "red_min_f32_atomic"])
 def test_1d_validation(lib, name):

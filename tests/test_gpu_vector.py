@@ -217,3 +217,55 @@ def test_plan_matches_call(red, vec16m):
         bad = red.plan("sum_f32", xd, torch.zeros(1, device="cuda"))
         bad.args = (0,) + bad.args[1:]  # a null input pointer is rejected
         bad()
+
+
+# ---------------------------------------------------------------------------
+# fused sum + max + min (one read)
+# ---------------------------------------------------------------------------
+
+def run_fused(red, x_dev, accum=False, old=(0.0, 0.0, 0.0)):
+    out = torch.tensor(list(old), dtype=torch.float32, device="cuda")
+    red.sum_max_min_f32(x_dev, out, accum=accum)
+    return host(out)
+
+
+def check_fused(red, orc, x, xd, accum, old, what):
+    got = run_fused(red, xd, accum, old)
+    for j, op in enumerate(OPS):
+        sep = run(red, op, xd, accum, old[j])
+        assert got[j].tobytes() == np.float32(sep).tobytes(), (what, op, got[j], sep)
+        check(orc, op, x, got[j], accum, old[j], "%s fused %s" % (what, op))
+
+
+@pytest.mark.parametrize("accum", [False, True], ids=["noaccum", "accum"])
+def test_fused_vec16m(red, orc, vec16m, accum):
+    """One read gives the same three results, bit for bit, as three calls."""
+    x, xd = vec16m
+    say("fused vec16m accum=%s" % accum)
+    old = (3.25, 3.25, 3.25) if accum else (0.0, 0.0, 0.0)
+    check_fused(red, orc, x, xd, accum, old, "vec16m")
+
+
+def test_fused_vec1g(red, orc, vec1g):
+    x, xd = vec1g
+    say("fused vec1g")
+    check_fused(red, orc, x, xd, False, (0.0, 0.0, 0.0), "vec1g")
+
+
+@pytest.mark.parametrize("n", [1, 3, 7, 8, 9, 33, 257, 4097, (1 << 20) + 5])
+def test_fused_lengths(red, orc, base, n):
+    x, xd = base
+    say("fused lengths n=%d" % n)
+    for off in range(4):
+        for accum, old in ((False, (0.0, 0.0, 0.0)), (True, (-2.5, 100.0, -100.0))):
+            check_fused(red, orc, x[off:off + n], xd[off:off + n], accum, old,
+                        "n=%d off=%d" % (n, off))
+
+
+def test_fused_special_values(red, orc):
+    say("fused special values")
+    nan, inf = float("nan"), float("inf")
+    for vals in ([nan, 1.0, nan, -3.0], [nan] * 9, [inf, 1.0, -2.0],
+                 [2.0 ** -149, -(2.0 ** -149), 0.0] * 5):
+        x = np.array(vals, np.float32)
+        check_fused(red, orc, x, dev(x), False, (0.0, 0.0, 0.0), "special %s" % vals[:3])
