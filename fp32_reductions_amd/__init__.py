@@ -15,6 +15,7 @@ Names follow the C ABI:
     sum_f32_atomic / max_f32_atomic / min_f32_atomic (same)
     sum_rows_f32 / max_rows_f32 / min_rows_f32 (x, out, n=None, accum=False)
     colprod_f32 / colprod_f16 / colprod_bf16 / colprod_i32 (src, out, C=None)
+    colprod_i16 / colprod_u16 / colprod_u32 (src, out, C=None)
 
 ``plan(name, *args, **kwargs)`` marshals the same arguments once and returns
 a ``Plan``; calling it enqueues the C entry point with the stored pointers,
@@ -63,6 +64,9 @@ _SIGS = {
     "red_colprod_f16": [_P, _SZ, _SZ, _SZ, _P, _P],
     "red_colprod_bf16": [_P, _SZ, _SZ, _SZ, _P, _P],
     "red_colprod_i32": [_P, _SZ, _SZ, _SZ, _P, _P],
+    "red_colprod_i16": [_P, _SZ, _SZ, _SZ, _P, _P],
+    "red_colprod_u16": [_P, _SZ, _SZ, _SZ, _P, _P],
+    "red_colprod_u32": [_P, _SZ, _SZ, _SZ, _P, _P],
 }
 for _name, _args in _SIGS.items():
     _fn = getattr(_lib, _name)
@@ -120,9 +124,11 @@ class Plan:
 
 
 def _need(t: torch.Tensor, dtype, what: str) -> None:
+    """dtype may be one torch dtype or a tuple of accepted dtypes."""
     if not isinstance(t, torch.Tensor):
         raise TypeError("%s must be a torch.Tensor" % what)
-    if t.dtype != dtype:
+    ok = t.dtype in dtype if isinstance(dtype, tuple) else t.dtype == dtype
+    if not ok:
         raise TypeError("%s must be %s, got %s" % (what, dtype, t.dtype))
     if t.device.type != "cuda":
         raise ValueError("%s must be a device (cuda/HIP) tensor" % what)
@@ -222,8 +228,14 @@ def min_rows_f32(x, out, n=None, accum=False, stream=None):
 # column product
 # ---------------------------------------------------------------------------
 
+# Unsigned types may also arrive as the signed torch dtype of the same width
+# (bit patterns): torch's uint16 / uint32 support on the device is partial.
+_U16 = (torch.uint16, torch.int16) if hasattr(torch, "uint16") else (torch.int16,)
+_U32 = (torch.uint32, torch.int32) if hasattr(torch, "uint32") else (torch.int32,)
 _COLPROD_DTYPE = {"red_colprod_f32": torch.float32, "red_colprod_f16": torch.float16,
-                  "red_colprod_bf16": torch.bfloat16, "red_colprod_i32": torch.int32}
+                  "red_colprod_bf16": torch.bfloat16, "red_colprod_i32": torch.int32,
+                  "red_colprod_i16": torch.int16, "red_colprod_u16": _U16,
+                  "red_colprod_u32": _U32}
 
 
 def _args_colprod(name: str, src, out, C=None, stream=None):
@@ -267,6 +279,21 @@ def colprod_i32(src, out, C=None, stream=None):
     return _colprod("red_colprod_i32", src, out, C, stream)
 
 
+def colprod_i16(src, out, C=None, stream=None):
+    """int16 tile; products modulo 2^16."""
+    return _colprod("red_colprod_i16", src, out, C, stream)
+
+
+def colprod_u16(src, out, C=None, stream=None):
+    """uint16 tile (torch.uint16, or torch.int16 holding the bits); mod 2^16."""
+    return _colprod("red_colprod_u16", src, out, C, stream)
+
+
+def colprod_u32(src, out, C=None, stream=None):
+    """uint32 tile (torch.uint32, or torch.int32 holding the bits); mod 2^32."""
+    return _colprod("red_colprod_u32", src, out, C, stream)
+
+
 # ---------------------------------------------------------------------------
 # pre-marshalled calls
 # ---------------------------------------------------------------------------
@@ -277,7 +304,7 @@ for _op in ("sum", "max", "min"):
     _MARSHAL["%s_f32_atomic" % _op] = ("red_%s_f32_atomic" % _op, _args_reduce1d)
     _MARSHAL["%s_rows_f32" % _op] = ("red_%s_rows_f32" % _op, _args_rows)
 _MARSHAL["sum_max_min_f32"] = ("red_sum_max_min_f32", _args_reduce1d)
-for _t in ("f32", "f16", "bf16", "i32"):
+for _t in ("f32", "f16", "bf16", "i32", "i16", "u16", "u32"):
     _MARSHAL["colprod_" + _t] = ("red_colprod_" + _t, _args_colprod)
 
 

@@ -273,6 +273,22 @@ int red_colprod_i32(const int32_t* src, size_t R, size_t C, size_t ld, int32_t* 
     return colprod(ColType::I32, src, R, C, ld, dst, stream);
 }
 
+int red_colprod_i16(const int16_t* src, size_t R, size_t C, size_t ld, int16_t* dst,
+                    red_stream_t stream)
+{
+    return colprod(ColType::U16, src, R, C, ld, dst, stream);
+}
+int red_colprod_u16(const uint16_t* src, size_t R, size_t C, size_t ld, uint16_t* dst,
+                    red_stream_t stream)
+{
+    return colprod(ColType::U16, src, R, C, ld, dst, stream);
+}
+int red_colprod_u32(const uint32_t* src, size_t R, size_t C, size_t ld, uint32_t* dst,
+                    red_stream_t stream)
+{
+    return colprod(ColType::I32, src, R, C, ld, dst, stream);
+}
+
 const char* red_status_str(int status)
 {
     switch (status) {

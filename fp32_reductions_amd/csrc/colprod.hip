@@ -3,7 +3,8 @@
 // PTO ISA "TCOLPROD", "Math Interpretation": dst[0,j] is the product of
 // src[i,j] over the R valid rows, for each of the C valid columns;
 // "Constraints": row-major source, destination of the same element type
-// (half, float, bfloat16, int32 among the listed ones).
+// (half, float, bfloat16, int16, uint16, int32, uint32 among the listed
+// ones).
 //
 // Layout of the work:
 //  * each lane owns V consecutive columns, V = 16 bytes / sizeof(T) (4 for
@@ -20,8 +21,9 @@
 //  * tile loads are non-temporal: each element is read once.
 //
 // Arithmetic: f32, f16 and bf16 multiply in fp32 (16-bit values widen
-// exactly), i32 in uint32 (wraps modulo 2^32).  f16 / bf16 round once, to
-// nearest even, when the final product is stored.
+// exactly); i32 / u32 and i16 / u16 in uint32 (wrapping modulo 2^32; the
+// 16-bit types keep the low 16 bits of the final product).  f16 / bf16
+// round once, to nearest even, when the final product is stored.
 #include "device.hpp"
 #include "internal.hpp"
 
@@ -106,6 +108,28 @@ struct TraitsBF16 {
         for (int k = 0; k < 4; ++k) {
             a[2 * k] = __uint_as_float(w[k] << 16);
             a[2 * k + 1] = __uint_as_float(w[k] & 0xffff0000u);
+        }
+    }
+};
+
+// int16 / uint16 stored as their 16-bit patterns.  Products are taken in
+// uint32 and truncated once at the end: reduction modulo 2^16 commutes with
+// multiplication, so the low 16 bits are those of the exact product for the
+// signed and the unsigned reading alike.
+struct TraitsU16 {
+    using T = uint16_t;
+    using A = uint32_t;
+    static constexpr int V = 8;
+    static __device__ __forceinline__ A one() { return 1u; }
+    static __device__ __forceinline__ A widen(T v) { return (uint32_t)v; }
+    static __device__ __forceinline__ T narrow(A a) { return (uint16_t)(a & 0xffffu); }
+    static __device__ __forceinline__ void unpack(const uint4& u, A* a)
+    {
+        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            a[2 * k] = w[k] & 0xffffu;
+            a[2 * k + 1] = w[k] >> 16;
         }
     }
 };
@@ -241,7 +265,7 @@ hipError_t launch_typed(const void* src, size_t R, size_t C, size_t ld,
 
 size_t colprod_elem_size(ColType t)
 {
-    return (t == ColType::F16 || t == ColType::BF16) ? 2 : 4;
+    return (t == ColType::F16 || t == ColType::BF16 || t == ColType::U16) ? 2 : 4;
 }
 
 // Fewest rows a workgroup should own when the rows are split: below this
@@ -285,6 +309,7 @@ hipError_t launch_colprod(ColType t, const void* src, size_t R, size_t C,
     case ColType::I32: return launch_typed<TraitsI32>(src, R, C, ld, dst, plan, ws, stream);
     case ColType::F16: return launch_typed<TraitsF16>(src, R, C, ld, dst, plan, ws, stream);
     case ColType::BF16: return launch_typed<TraitsBF16>(src, R, C, ld, dst, plan, ws, stream);
+    case ColType::U16: return launch_typed<TraitsU16>(src, R, C, ld, dst, plan, ws, stream);
     }
     return hipErrorInvalidValue;
 }

@@ -62,7 +62,8 @@ hipError_t launch_rows(OpKind op, const float* x, size_t rows, size_t n,
                        hipStream_t stream);
 
 // ---- column product (colprod.hip) -----------------------------------------
-enum class ColType { F32, F16, BF16, I32 };
+// U16 carries int16 and uint16 (same bits); uint32 runs as I32 (same bits).
+enum class ColType { F32, F16, BF16, I32, U16 };
 size_t colprod_elem_size(ColType t);
 // Row splits the colprod kernel uses, and the workspace it needs.
 struct ColprodPlan {

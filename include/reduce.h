@@ -181,6 +181,19 @@ int red_colprod_bf16(const uint16_t* src, size_t R, size_t C, size_t ld,
 int red_colprod_i32(const int32_t* src, size_t R, size_t C, size_t ld,
                     int32_t* dst, red_stream_t stream);
 
+/* The other integer element types TCOLPROD lists ("Constraints": int16 and
+ * int32 on A2A3; int16, uint16, int32, uint32 on A5).  Same arguments,
+ * layout and errors as above; products wrap modulo 2^32 (u32) or 2^16 (i16,
+ * u16) and are bit-exact.  The low bits of a product depend only on the low
+ * bits of its factors, so i16 and u16 give the same bit patterns, and u32
+ * the same bits as i32. */
+int red_colprod_i16(const int16_t* src, size_t R, size_t C, size_t ld,
+                    int16_t* dst, red_stream_t stream);
+int red_colprod_u16(const uint16_t* src, size_t R, size_t C, size_t ld,
+                    uint16_t* dst, red_stream_t stream);
+int red_colprod_u32(const uint32_t* src, size_t R, size_t C, size_t ld,
+                    uint32_t* dst, red_stream_t stream);
+
 /* ---------------------------------------------------------------------
  * Utilities
  * ------------------------------------------------------------------- */

@@ -13,7 +13,8 @@ passage it follows, is stated in ``oracle.c``:
   "reduction -> sm100_packed" (introduction; "How inputs change the
   algorithm");
 * the page's own single-precision summation order -- same page, "Algorithm";
-* column products over fp32 / fp16 / bf16 / int32 -- PTO ISA "TCOLPROD"
+* column products over fp32 / fp16 / bf16 / int16 / uint16 / int32 / uint32
+  -- PTO ISA "TCOLPROD"
   ("Math Interpretation", "Constraints").
 """
 from __future__ import annotations
@@ -68,6 +69,8 @@ class Oracle:
             "oracle_colprod_f16": [_P, _SZ, _SZ, _SZ, _P],
             "oracle_colprod_bf16": [_P, _SZ, _SZ, _SZ, _P],
             "oracle_colprod_i32": [_P, _SZ, _SZ, _SZ, _P],
+            "oracle_colprod_u32": [_P, _SZ, _SZ, _SZ, _P],
+            "oracle_colprod_u16": [_P, _SZ, _SZ, _SZ, _P],
         }
         for name, args in sig.items():
             fn = getattr(lib, name)
@@ -176,6 +179,16 @@ class Oracle:
         """int32 column products modulo 2^32."""
         return self._colprod(self.lib.oracle_colprod_i32, src, R, C, ld,
                              np.int32, np.int32, dst)
+
+    def colprod_u32(self, src, R, C, ld, dst=None):
+        """uint32 column products modulo 2^32."""
+        return self._colprod(self.lib.oracle_colprod_u32, src, R, C, ld,
+                             np.uint32, np.uint32, dst)
+
+    def colprod_u16(self, src_bits, R, C, ld, dst=None):
+        """int16 / uint16 column products modulo 2^16, as uint16 patterns."""
+        return self._colprod(self.lib.oracle_colprod_u16, src_bits, R, C, ld,
+                             np.uint16, np.uint16, dst)
 
     def f16_to_f64(self, h: int) -> float:
         return self.lib.oracle_f16_to_f64(h)

@@ -20,7 +20,7 @@
  *   colprod -- PTO ISA "TCOLPROD", sections "Math Interpretation" (the
  *            per-column product over the R valid rows) and "Constraints"
  *            (early return for zero valid rows or columns; supported element
- *            types half, float, bfloat16, int32).
+ *            types half, float, bfloat16, int16, uint16, int32, uint32).
  *
  * Readings where the pages are silent (each is restated in the design doc):
  *   - n == 0 (1-D and rows) is treated like TCOLPROD's empty tile: nothing
@@ -29,7 +29,8 @@
  *     ignored; the result is NaN only when every operand is NaN.
  *   - accum folds the old dst into the first accumulator slot before any
  *     element; for the exact definitions the position does not matter.
- *   - int32 products wrap modulo 2^32 (computed in uint32_t).
+ *   - int32 / uint32 products wrap modulo 2^32, int16 / uint16 products
+ *     modulo 2^16 (computed in uint32_t).
  *   - half / bfloat16 are decoded exactly from their bit definitions.
  *
  * Every function here is pinned by tests/test_oracle.py (brute force with
@@ -323,6 +324,39 @@ int oracle_colprod_i32(const int32_t* src, size_t R, size_t C, size_t ld,
             p *= v;
         }
         memcpy(&dst[j], &p, sizeof p);
+    }
+    return 1;
+}
+
+/* uint32: the product modulo 2^32. */
+int oracle_colprod_u32(const uint32_t* src, size_t R, size_t C, size_t ld,
+                       uint32_t* dst)
+{
+    if (R == 0 || C == 0)
+        return 0;
+    for (size_t j = 0; j < C; j++) {
+        uint32_t p = 1u;
+        for (size_t i = 0; i < R; i++)
+            p *= src[i * ld + j];
+        dst[j] = p;
+    }
+    return 1;
+}
+
+/* int16 / uint16 (given as 16-bit patterns): the product modulo 2^16.  It is
+ * computed modulo 2^32 and truncated: reduction modulo 2^16 commutes with
+ * multiplication, so the low 16 bits are those of the exact product for
+ * signed and unsigned readings alike. */
+int oracle_colprod_u16(const uint16_t* src, size_t R, size_t C, size_t ld,
+                       uint16_t* dst)
+{
+    if (R == 0 || C == 0)
+        return 0;
+    for (size_t j = 0; j < C; j++) {
+        uint32_t p = 1u;
+        for (size_t i = 0; i < R; i++)
+            p *= (uint32_t)src[i * ld + j];
+        dst[j] = (uint16_t)(p & 0xffffu);
     }
     return 1;
 }

@@ -416,6 +416,47 @@ def pin_colprod_i32_closed_forms(o):
     assert got.tolist() == [-2**31]
 
 
+def pin_colprod_u32_bruteforce(o):
+    """uint32 against Python big-int products modulo 2^32."""
+    rng = np.random.default_rng(21)
+    R, C, ld = 16, 11, 13
+    t = rng.integers(0, 2**32, (R, ld), dtype=np.uint64).astype(np.uint32)
+    got = o.colprod_u32(t, R, C, ld)
+    for j in range(C):
+        p = 1
+        for i in range(R):
+            p *= int(t[i, j])
+        assert int(got[j]) == p % U32, j
+    got = o.colprod_u32(np.full((4096, 2), 3, np.uint32), 4096, 2, 2)
+    assert got.tolist() == [pow(3, 4096, U32)] * 2
+    assert (o.colprod_u32(np.ones((3, 3), np.uint32), 0, 3, 3,
+                          dst=np.full(3, 5, np.uint32)) == 5).all()
+
+
+def pin_colprod_u16_bruteforce(o):
+    """16-bit patterns against Python big-int products modulo 2^16, read
+    both as uint16 and as int16; closed forms (-1)^R, 3^R, 2^R."""
+    rng = np.random.default_rng(22)
+    R, C, ld = 16, 9, 12
+    t = rng.integers(0, 2**16, (R, ld), dtype=np.int64).astype(np.uint16)
+    got = o.colprod_u16(t, R, C, ld)
+    for j in range(C):
+        pu, ps = 1, 1
+        for i in range(R):
+            pu *= int(t[i, j])
+            ps *= int(t[i, j].astype(np.int16))
+        assert int(got[j]) == pu % (1 << 16) == ps % (1 << 16), j
+    m1 = np.full((7, 1), 0xFFFF, np.uint16)          # int16 -1
+    assert o.colprod_u16(m1, 7, 1, 1).tolist() == [0xFFFF]
+    assert o.colprod_u16(m1[:6], 6, 1, 1).tolist() == [1]
+    t3 = np.full((2048, 1), 3, np.uint16)
+    assert o.colprod_u16(t3, 2048, 1, 1).tolist() == [pow(3, 2048, 1 << 16)]
+    t2 = np.full((16, 1), 2, np.uint16)
+    assert o.colprod_u16(t2, 16, 1, 1).tolist() == [0]
+    assert o.colprod_u16(t2[:15], 15, 1, 1).tolist() == [1 << 15]
+    assert (o.colprod_u16(t3, 2048, 0, 1, dst=np.full(1, 9, np.uint16)) == 9).all()
+
+
 PINS = [
     pin_sum_bruteforce, pin_sum_integer_exact, pin_sum_arithmetic_series,
     pin_sum_cancellation, pin_sum_accum, pin_sum_empty, pin_sum_nonfinite,
@@ -427,5 +468,6 @@ PINS = [
     pin_colprod_f32_bruteforce, pin_colprod_f32_closed_forms,
     pin_colprod_empty, pin_f16_decode_exhaustive, pin_bf16_decode_exhaustive,
     pin_colprod_16bit_bruteforce, pin_colprod_i32_bruteforce,
-    pin_colprod_i32_closed_forms,
+    pin_colprod_i32_closed_forms, pin_colprod_u32_bruteforce,
+    pin_colprod_u16_bruteforce,
 ]

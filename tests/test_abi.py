@@ -52,7 +52,7 @@ def test_header_declares_the_abi():
         assert "red_%s_f32_atomic" % op in names
         assert "red_%s_rows_f32" % op in names
     assert "red_sum_max_min_f32" in names
-    for t in ("f32", "f16", "bf16", "i32"):
+    for t in ("f32", "f16", "bf16", "i32", "i16", "u16", "u32"):
         assert "red_colprod_" + t in names
     assert "red_status_str" in names and "red_abi_version" in names
 
@@ -120,7 +120,9 @@ def test_rows_validation(lib, name):
 
 
 @pytest.mark.parametrize("name,es", [("red_colprod_f32", 4), ("red_colprod_i32", 4),
-                                     ("red_colprod_f16", 2), ("red_colprod_bf16", 2)])
+                                     ("red_colprod_f16", 2), ("red_colprod_bf16", 2),
+                                     ("red_colprod_i16", 2), ("red_colprod_u16", 2),
+                                     ("red_colprod_u32", 4)])
 def test_colprod_validation(lib, name, es):
     f = _fn(lib, name, [P, SZ, SZ, SZ, P, P])
     # TCOLPROD's early return: zero valid rows or columns

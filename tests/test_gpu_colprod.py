@@ -205,3 +205,76 @@ def test_deterministic(red, tiles4k):
     ref = run(red, "f32", fd, 16384)
     for _ in range(2):
         assert run(red, "f32", fd, 16384).tobytes() == ref.tobytes()
+
+
+# ---------------------------------------------------------------------------
+# int16 / uint16 / uint32 (bit-exact modulo 2^16 / 2^32)
+# ---------------------------------------------------------------------------
+
+INT_KINDS = {  # kind: (host storage, torch storage, binding, oracle)
+    "i16": (np.int16, torch.int16, "colprod_i16", "colprod_u16"),
+    "u16": (np.uint16, torch.int16, "colprod_u16", "colprod_u16"),
+    "u32": (np.uint32, torch.int32, "colprod_u32", "colprod_u32"),
+}
+
+
+def run_int(red, kind, src_host_2d, C, off=0):
+    """Upload src (with an element offset), run, return the result bits."""
+    hdt, tdt, fn, _ = INT_KINDS[kind]
+    R, ld = src_host_2d.shape
+    flat = np.zeros(R * ld + off + 8, hdt)
+    flat[off:off + R * ld] = src_host_2d.reshape(-1)
+    signed = np.int16 if tdt == torch.int16 else np.int32
+    fd = dev(flat.view(signed))
+    sd = fd[off:off + R * ld].view(R, ld)
+    out = torch.zeros(max(C, 1), dtype=tdt, device="cuda")
+    getattr(red, fn)(sd, out, C=C)
+    return host(out).view(np.uint16 if tdt == torch.int16 else np.uint32)[:C]
+
+
+def want_int(orc, kind, src_host_2d, C):
+    R, ld = src_host_2d.shape
+    bits = src_host_2d.view(np.uint16) if kind in ("i16", "u16") else src_host_2d.view(np.uint32)
+    return getattr(orc, INT_KINDS[kind][3])(bits, R, C, ld)
+
+
+@pytest.mark.parametrize("kind", ["i16", "u16", "u32"])
+@pytest.mark.parametrize("R,C,ld,off", SHAPES)
+def test_int_shapes(red, orc, kind, R, C, ld, off):
+    say("colprod int shape %s R=%d C=%d ld=%d off=%d" % (kind, R, C, ld, off))
+    hdt = INT_KINDS[kind][0]
+    hi = 1 << (8 * np.dtype(hdt).itemsize)
+    rng = np.random.default_rng(50)
+    src = rng.integers(0, hi, (R, ld), dtype=np.uint64)
+    src = (src | 1).astype(np.uint64)  # odd: products stay nonzero
+    src = src.astype(np.uint16 if hi == 1 << 16 else np.uint32).view(hdt)
+    got = run_int(red, kind, src, C, off)
+    want = want_int(orc, kind, src, C)
+    bad = np.nonzero(got != want)[0]
+    assert bad.size == 0, "%s: column %d got %d want %d" % (kind, bad[0], got[bad[0]], want[bad[0]])
+
+
+@pytest.mark.parametrize("kind,R,C", [("u32", 4096, 16384), ("i16", 2048, 32768),
+                                      ("u16", 2048, 32768)])
+def test_int_large(red, orc, kind, R, C):
+    """Full-size tiles of odd values (whose products do not vanish)."""
+    say("colprod int large %s %dx%d" % (kind, R, C))
+    hdt = INT_KINDS[kind][0]
+    vals = workloads.odd_i32_tile(R, C, seed=51)  # {-3, -1, 1, 3}
+    src = vals.astype(hdt)
+    got = run_int(red, kind, src, C)
+    want = want_int(orc, kind, src, C)
+    assert (got == want).all()
+    assert (want != 0).all()
+
+
+def test_int_closed_forms(red):
+    say("colprod int closed forms")
+    m1 = np.full((4097, 5), -1, np.int16)
+    assert (run_int(red, "i16", m1, 5) == 0xFFFF).all()          # (-1)^odd
+    t3 = np.full((2048, 3), 3, np.uint16)
+    assert (run_int(red, "u16", t3, 3) == pow(3, 2048, 1 << 16)).all()
+    t2 = np.full((16, 3), 2, np.uint16)
+    assert (run_int(red, "u16", t2, 3) == 0).all()
+    big = np.full((3, 2), 0xFFFFFFFF, np.uint32)                   # (2^32-1)^3
+    assert (run_int(red, "u32", big, 2) == pow(2**32 - 1, 3, 1 << 32)).all()

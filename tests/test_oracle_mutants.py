@@ -63,6 +63,11 @@ MUTANTS = [
     ("f16_subnormal_scale", "ldexp((double)f, -24)", "ldexp((double)f, -25)"),
     ("bf16_shift", "uint32_t u = (uint32_t)b << 16;", "uint32_t u = (uint32_t)b << 15;"),
     ("i32_adds", "p *= v;", "p += v;"),
+    ("u16_keeps_high_bits", "dst[j] = (uint16_t)(p & 0xffffu);",
+     "dst[j] = (uint16_t)((p >> 1) & 0xffffu);"),
+    ("u32_starts_at_zero",
+     "        uint32_t p = 1u;\n        for (size_t i = 0; i < R; i++)\n            p *= src[i * ld + j];",
+     "        uint32_t p = 0u;\n        for (size_t i = 0; i < R; i++)\n            p *= src[i * ld + j];"),
     ("i32_signed_read",
      "uint32_t v;\n            memcpy(&v, &src[i * ld + j], sizeof v);",
      "uint32_t v = (uint32_t)(src[i * ld + j] & 0x7fffffff);"),
