@@ -30,7 +30,9 @@ Other workloads (--workload): vec16m_fused (the same vector, sum / max / min
 from one read per call), vec1g (2^30+7 vector), colprod4k (4096 x 16384
 f32 and i32 column products), rows1000 (65536 x 1000 row sum / max, then
 2048 x 32768 bf16 / f16 column products), rows32 (4096 x 32 rows, 16 x 16
-tile), copycal (a plain device copy, for counter calibration).
+tile), colprod_int (int16 and uint32 column products), cols4k (column
+sum / max / min of a 4096 x 16384 tile), copycal (a plain
+device copy, for counter calibration).
 """
 from __future__ import annotations
 
@@ -262,6 +264,32 @@ def wl_colprod4k(torch, red, orc, steps):
         calls, ["colprod_f32"], ["colprod.hip", "device.hpp"], cpu)
 
 
+def wl_colprod_int(torch, red, orc, steps):
+    """The other integer element types at the large tile shapes (odd values
+    from {-3, -1, 1, 3}, whose products do not vanish)."""
+    log("generating int16 2048 x 32768 and uint32 4096 x 16384 tiles")
+    h = workloads.odd_i32_tile(2048, 32768, seed=51).astype(np.int16)
+    u = workloads.odd_i32_tile(4096, 16384, seed=52)  # int32 bits of uint32 values
+    hb = 2 * h.size + 2 * h.shape[1]
+    ub = 4 * u.size + 4 * u.shape[1]
+    hs = Rotor(up(torch, h), 1, hb + ub)
+    us = Rotor(up(torch, u), 1, hb + ub)
+    oh = torch.zeros(h.shape[1], dtype=torch.int16, device="cuda")
+    ou = torch.zeros(u.shape[1], dtype=torch.int32, device="cuda")
+    calls = [Call("colprod_i16", "colprod_kernel<TraitsU16> + colprod_finish_kernel<TraitsU16>", hb,
+                  lambda k: red.plan("colprod_i16", hs.next(), oh)),
+             Call("colprod_u32", "colprod_kernel<TraitsI32> + colprod_finish_kernel<TraitsI32>", ub,
+                  lambda k: red.plan("colprod_u32", us.next(), ou))]
+    cpu = [(hb, lambda: orc.colprod_u16(h.view(np.uint16), 2048, 32768, 32768)),
+           (ub, lambda: orc.colprod_u32(u.view(np.uint32), 4096, 16384, 16384))]
+    return Workload(
+        "colprod_int",
+        "column products of a 2048 x 32768 int16 tile and a 4096 x 16384 uint32 tile, "
+        "values uniform over {-3, -1, 1, 3} (seeds 51, 52)",
+        {"calls_per_step": 2, "cold_copies": [len(hs), len(us)]},
+        calls, ["colprod_i16"], ["colprod.hip", "device.hpp"], cpu)
+
+
 def wl_rows1000(torch, red, orc, steps):
     log("generating 65536 x 1000 rows and 2048 x 32768 bf16 / f16 tiles")
     x, b, h = workloads.rows1000()
@@ -296,6 +324,26 @@ def wl_rows1000(torch, red, orc, steps):
         {"rows": rows, "n": n, "R": R, "C": C, "calls_per_step": 4,
          "cold_copies": [len(xs), len(bs), len(hs)]},
         calls, ["rows_sum"], ["rows.hip", "device.hpp"], cpu)
+
+
+def wl_cols4k(torch, red, orc, steps):
+    log("generating a 4096 x 16384 fp32 tile")
+    t = workloads.uniform_f32(60, (4096, 16384))
+    R, C = t.shape
+    nbytes = 4 * R * C + 4 * C
+    ts = Rotor(up(torch, t), 3, 3 * nbytes)
+    outs = [torch.zeros(C, dtype=torch.float32, device="cuda") for _ in range(3)]
+    calls = [Call(op + "_cols", "colred_kernel<TraitsF32, Op%s> + colred_finish_kernel" % op.capitalize(),
+                  nbytes, lambda k, op=op, j=j: red.plan(op + "_cols_f32", ts.next(), outs[j]))
+             for j, op in enumerate(("sum", "max", "min"))]
+    cpu = [(nbytes, lambda: orc.cols_sum_f32(t, R, C, C)),
+           (nbytes, lambda: orc.cols_max_f32(t, R, C, C)),
+           (nbytes, lambda: orc.cols_min_f32(t, R, C, C))]
+    return Workload(
+        "cols4k",
+        "column sum, max and min of a 4096 x 16384 fp32 tile, uniform[-1,1), seed 60",
+        {"R": R, "C": C, "calls_per_step": 3, "cold_copies": len(ts)},
+        calls, ["sum_cols"], ["colprod.hip", "device.hpp"], cpu)
 
 
 def wl_rows32(torch, red, orc, steps):
@@ -339,7 +387,7 @@ def wl_copycal(torch, red, orc, steps):
 
 
 WORKLOADS = {"vec16m": wl_vec16m, "vec16m_fused": wl_vec16m_fused, "vec1g": wl_vec1g, "colprod4k": wl_colprod4k,
-             "rows1000": wl_rows1000, "rows32": wl_rows32, "copycal": wl_copycal}
+             "rows1000": wl_rows1000, "colprod_int": wl_colprod_int, "cols4k": wl_cols4k, "rows32": wl_rows32, "copycal": wl_copycal}
 
 
 # ---------------------------------------------------------------------------

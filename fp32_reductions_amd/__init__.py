@@ -14,6 +14,7 @@ Names follow the C ABI:
     sum_max_min_f32 (x, out[3], accum=False, stream=None)
     sum_f32_atomic / max_f32_atomic / min_f32_atomic (same)
     sum_rows_f32 / max_rows_f32 / min_rows_f32 (x, out, n=None, accum=False)
+    sum_cols_f32 / max_cols_f32 / min_cols_f32 (src, out, C=None, accum=False)
     colprod_f32 / colprod_f16 / colprod_bf16 / colprod_i32 (src, out, C=None)
     colprod_i16 / colprod_u16 / colprod_u32 (src, out, C=None)
 
@@ -60,6 +61,9 @@ _SIGS = {
     "red_sum_rows_f32": [_P, _SZ, _SZ, _SZ, _P, _I, _P],
     "red_max_rows_f32": [_P, _SZ, _SZ, _SZ, _P, _I, _P],
     "red_min_rows_f32": [_P, _SZ, _SZ, _SZ, _P, _I, _P],
+    "red_sum_cols_f32": [_P, _SZ, _SZ, _SZ, _P, _I, _P],
+    "red_max_cols_f32": [_P, _SZ, _SZ, _SZ, _P, _I, _P],
+    "red_min_cols_f32": [_P, _SZ, _SZ, _SZ, _P, _I, _P],
     "red_colprod_f32": [_P, _SZ, _SZ, _SZ, _P, _P],
     "red_colprod_f16": [_P, _SZ, _SZ, _SZ, _P, _P],
     "red_colprod_bf16": [_P, _SZ, _SZ, _SZ, _P, _P],
@@ -225,6 +229,44 @@ def min_rows_f32(x, out, n=None, accum=False, stream=None):
 
 
 # ---------------------------------------------------------------------------
+# column sum / max / min
+# ---------------------------------------------------------------------------
+
+def _args_cols(name: str, src, out, C=None, accum=False, stream=None):
+    _need(src, torch.float32, "src")
+    _need(out, torch.float32, "out")
+    if src.dim() != 2:
+        raise ValueError("src must be 2-D (R, ld)")
+    R, ld = src.shape
+    C = ld if C is None else int(C)
+    if not 0 <= C <= ld:
+        raise ValueError("need 0 <= C <= ld")
+    if out.numel() < C:
+        raise ValueError("out needs C elements")
+    return (src.data_ptr(), R, C, ld, out.data_ptr(), int(bool(accum)),
+            _stream(stream)), (src, out)
+
+
+def _cols(name: str, src, out, C, accum, stream):
+    args, _ = _args_cols(name, src, out, C, accum, stream)
+    _check(getattr(_lib, name)(*args), name)
+    return out
+
+
+def sum_cols_f32(src, out, C=None, accum=False, stream=None):
+    """out[j] = [out[j] +] sum_i src[i, j] for j < C, fp32 (R, ld) tile."""
+    return _cols("red_sum_cols_f32", src, out, C, accum, stream)
+
+
+def max_cols_f32(src, out, C=None, accum=False, stream=None):
+    return _cols("red_max_cols_f32", src, out, C, accum, stream)
+
+
+def min_cols_f32(src, out, C=None, accum=False, stream=None):
+    return _cols("red_min_cols_f32", src, out, C, accum, stream)
+
+
+# ---------------------------------------------------------------------------
 # column product
 # ---------------------------------------------------------------------------
 
@@ -303,6 +345,7 @@ for _op in ("sum", "max", "min"):
     _MARSHAL["%s_f32" % _op] = ("red_%s_f32" % _op, _args_reduce1d)
     _MARSHAL["%s_f32_atomic" % _op] = ("red_%s_f32_atomic" % _op, _args_reduce1d)
     _MARSHAL["%s_rows_f32" % _op] = ("red_%s_rows_f32" % _op, _args_rows)
+    _MARSHAL["%s_cols_f32" % _op] = ("red_%s_cols_f32" % _op, _args_cols)
 _MARSHAL["sum_max_min_f32"] = ("red_sum_max_min_f32", _args_reduce1d)
 for _t in ("f32", "f16", "bf16", "i32", "i16", "u16", "u32"):
     _MARSHAL["colprod_" + _t] = ("red_colprod_" + _t, _args_colprod)

@@ -173,11 +173,11 @@ int reduce_rows(OpKind op, const float* x, size_t rows, size_t n, size_t ld,
                                        static_cast<hipStream_t>(stream)));
 }
 
-int colprod(ColType t, const void* src, size_t R, size_t C, size_t ld,
-            void* dst, red_stream_t stream)
+// Column reductions share validation: ld >= C, extents, grid limit,
+// alignment to the element size.
+int check_cols(ColType t, const void* src, size_t R, size_t C, size_t ld,
+               const void* dst)
 {
-    if (R == 0 || C == 0)
-        return RED_OK;
     const size_t es = red::colprod_elem_size(t);
     if (!src || !dst || ld < C || !extent_ok(R, ld, C, es) ||
         C > SIZE_MAX / sizeof(float))
@@ -188,10 +188,40 @@ int colprod(ColType t, const void* src, size_t R, size_t C, size_t ld,
         return RED_ERR_INVALID;
     if (!aligned(src, es) || !aligned(dst, es))
         return RED_ERR_ALIGN;
+    return RED_OK;
+}
+
+int cols(OpKind op, const float* src, size_t R, size_t C, size_t ld, float* dst,
+         int accum, red_stream_t stream)
+{
+    if (R == 0 || C == 0)
+        return RED_OK;
+    int st = check_cols(ColType::F32, src, R, C, ld, dst);
+    if (st != RED_OK)
+        return st;
     int dev;
     DeviceInfo info;
-    int st = current_device(&dev, &info);
+    if ((st = current_device(&dev, &info)) != RED_OK)
+        return st;
+    Workspace ws;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    if ((st = stream_workspace(dev, s, &ws)) != RED_OK)
+        return st;
+    const red::ColprodPlan plan = red::colprod_plan(ColType::F32, R, C, info, ws);
+    return hip_status(red::launch_cols(op, src, R, C, ld, dst, accum, plan, ws, s));
+}
+
+int colprod(ColType t, const void* src, size_t R, size_t C, size_t ld,
+            void* dst, red_stream_t stream)
+{
+    if (R == 0 || C == 0)
+        return RED_OK;
+    int st = check_cols(t, src, R, C, ld, dst);
     if (st != RED_OK)
+        return st;
+    int dev;
+    DeviceInfo info;
+    if ((st = current_device(&dev, &info)) != RED_OK)
         return st;
     Workspace ws;
     const hipStream_t s = static_cast<hipStream_t>(stream);
@@ -250,6 +280,22 @@ int red_min_rows_f32(const float* x, size_t rows, size_t n, size_t ld, float* ou
                      int accum, red_stream_t stream)
 {
     return reduce_rows(OpKind::Min, x, rows, n, ld, out, accum, stream);
+}
+
+int red_sum_cols_f32(const float* src, size_t R, size_t C, size_t ld, float* dst,
+                     int accum, red_stream_t stream)
+{
+    return cols(OpKind::Sum, src, R, C, ld, dst, accum, stream);
+}
+int red_max_cols_f32(const float* src, size_t R, size_t C, size_t ld, float* dst,
+                     int accum, red_stream_t stream)
+{
+    return cols(OpKind::Max, src, R, C, ld, dst, accum, stream);
+}
+int red_min_cols_f32(const float* src, size_t R, size_t C, size_t ld, float* dst,
+                     int accum, red_stream_t stream)
+{
+    return cols(OpKind::Min, src, R, C, ld, dst, accum, stream);
 }
 
 int red_colprod_f32(const float* src, size_t R, size_t C, size_t ld, float* dst,

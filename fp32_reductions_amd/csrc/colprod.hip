@@ -1,4 +1,5 @@
-// colprod.hip -- column product of a row-major tile (TCOLPROD).
+// colprod.hip -- column product of a row-major tile (TCOLPROD), and the
+// column sum / max / min built on the same layout.
 //
 // PTO ISA "TCOLPROD", "Math Interpretation": dst[0,j] is the product of
 // src[i,j] over the R valid rows, for each of the C valid columns;
@@ -19,6 +20,11 @@
 //    partial rows of each column in slice order, narrows once to T and
 //    writes dst;
 //  * tile loads are non-temporal: each element is read once.
+//
+// Column sum / max / min of an fp32 tile reduce each column by the TVM
+// page's operators ("reduction -> sm100_packed"), the 2-D case its fast
+// path leaves to a generic fallback ("How inputs change the algorithm"),
+// with the same identities and maxNum / minNum rules as the 1-D calls.
 //
 // Arithmetic: f32, f16 and bf16 multiply in fp32 (16-bit values widen
 // exactly); i32 / u32 and i16 / u16 in uint32 (wrapping modulo 2^32; the
@@ -134,13 +140,23 @@ struct TraitsU16 {
     }
 };
 
+// Product, the TCOLPROD operator, over the accumulator type A.
+template <class A>
+struct OpMul {
+    static __device__ __forceinline__ A identity() { return A(1); }
+    static __device__ __forceinline__ A apply(A a, A b) { return a * b; }
+};
+
 // VEC: src is 16-byte aligned and ld * sizeof(T) is a multiple of 16, so
 // every lane's V columns of every row form one aligned 16-byte vector.
-template <class Tr, bool VEC>
-__global__ __launch_bounds__(kBlock) void colprod_kernel(
+// Op combines accumulators (OpMul for TCOLPROD; OpSum / OpMax / OpMin for
+// the column sum / max / min).  Under accum (never for products) the old
+// dst[j] is folded in first.
+template <class Tr, class Op, bool VEC>
+__global__ __launch_bounds__(kBlock) void colred_kernel(
     const typename Tr::T* __restrict__ src, uint64_t R, uint64_t C,
     uint64_t ld, typename Tr::T* __restrict__ dst,
-    typename Tr::A* __restrict__ partials, uint64_t rows_per_split)
+    typename Tr::A* __restrict__ partials, uint64_t rows_per_split, int accum)
 {
     using T = typename Tr::T;
     using A = typename Tr::A;
@@ -161,7 +177,7 @@ __global__ __launch_bounds__(kBlock) void colprod_kernel(
     A acc[V];
 #pragma unroll
     for (int k = 0; k < V; ++k)
-        acc[k] = Tr::one();
+        acc[k] = Op::identity();
 
     if (j0 < C) {
         const T* __restrict__ col = src + j0;
@@ -180,7 +196,7 @@ __global__ __launch_bounds__(kBlock) void colprod_kernel(
                     Tr::unpack(v[u], a);
 #pragma unroll
                     for (int k = 0; k < V; ++k)
-                        acc[k] = acc[k] * a[k];
+                        acc[k] = Op::apply(acc[k], a[k]);
                 }
             }
             for (; r < r1; r += kWaves) {
@@ -188,14 +204,14 @@ __global__ __launch_bounds__(kBlock) void colprod_kernel(
                 Tr::unpack(load_stream(reinterpret_cast<const uint4*>(col + r * ld)), a);
 #pragma unroll
                 for (int k = 0; k < V; ++k)
-                    acc[k] = acc[k] * a[k];
+                    acc[k] = Op::apply(acc[k], a[k]);
             }
         } else {
             for (; r < r1; r += kWaves) {
 #pragma unroll
                 for (int k = 0; k < V; ++k)
                     if (j0 + k < C)
-                        acc[k] = acc[k] * Tr::widen(col[r * ld + k]);
+                        acc[k] = Op::apply(acc[k], Tr::widen(col[r * ld + k]));
             }
         }
     }
@@ -210,36 +226,36 @@ __global__ __launch_bounds__(kBlock) void colprod_kernel(
         A p = lds[0][c];
 #pragma unroll
         for (int w = 1; w < kWaves; ++w)
-            p = p * lds[w][c];
+            p = Op::apply(p, lds[w][c]);
         const uint64_t j = cb * kCols + c;
         if (j < C) {
             if (S == 1)
-                dst[j] = Tr::narrow(p);
+                dst[j] = Tr::narrow(accum ? Op::apply(Tr::widen(dst[j]), p) : p);
             else
                 partials[s * C + j] = p;
         }
     }
 }
 
-// Second pass (S > 1): one thread per column multiplies the S partial rows
-// in slice order and narrows the product once to T.
-template <class Tr>
-__global__ __launch_bounds__(kBlock) void colprod_finish_kernel(
+// Second pass (S > 1): one thread per column combines the S partial rows in
+// slice order (after the old dst[j] under accum) and narrows once to T.
+template <class Tr, class Op>
+__global__ __launch_bounds__(kBlock) void colred_finish_kernel(
     const typename Tr::A* __restrict__ partials, uint32_t S, uint64_t C,
-    typename Tr::T* __restrict__ dst)
+    typename Tr::T* __restrict__ dst, int accum)
 {
     const uint64_t j = (uint64_t)blockIdx.x * kBlock + threadIdx.x;
     if (j >= C)
         return;
-    typename Tr::A p = partials[j];
+    typename Tr::A p = accum ? Op::apply(Tr::widen(dst[j]), partials[j]) : partials[j];
     for (uint32_t k = 1; k < S; ++k)
-        p = p * partials[(uint64_t)k * C + j];
+        p = Op::apply(p, partials[(uint64_t)k * C + j]);
     dst[j] = Tr::narrow(p);
 }
 
-template <class Tr>
+template <class Tr, class Op>
 hipError_t launch_typed(const void* src, size_t R, size_t C, size_t ld,
-                        void* dst, const ColprodPlan& plan,
+                        void* dst, int accum, const ColprodPlan& plan,
                         const Workspace& ws, hipStream_t stream)
 {
     using T = typename Tr::T;
@@ -250,14 +266,14 @@ hipError_t launch_typed(const void* src, size_t R, size_t C, size_t ld,
     T* d = static_cast<T*>(dst);
     A* part = static_cast<A*>(ws.partials);
     if (vec)
-        colprod_kernel<Tr, true><<<grid, kBlock, 0, stream>>>(
-            s, R, C, ld, d, part, plan.rows_per_split);
+        colred_kernel<Tr, Op, true><<<grid, kBlock, 0, stream>>>(
+            s, R, C, ld, d, part, plan.rows_per_split, accum);
     else
-        colprod_kernel<Tr, false><<<grid, kBlock, 0, stream>>>(
-            s, R, C, ld, d, part, plan.rows_per_split);
+        colred_kernel<Tr, Op, false><<<grid, kBlock, 0, stream>>>(
+            s, R, C, ld, d, part, plan.rows_per_split, accum);
     if (plan.splits > 1)
-        colprod_finish_kernel<Tr><<<(unsigned)((C + kBlock - 1) / kBlock), kBlock, 0, stream>>>(
-            part, plan.splits, C, d);
+        colred_finish_kernel<Tr, Op><<<(unsigned)((C + kBlock - 1) / kBlock), kBlock, 0, stream>>>(
+            part, plan.splits, C, d, accum);
     return hipGetLastError();
 }
 
@@ -305,11 +321,23 @@ hipError_t launch_colprod(ColType t, const void* src, size_t R, size_t C,
                           const Workspace& ws, hipStream_t stream)
 {
     switch (t) {
-    case ColType::F32: return launch_typed<TraitsF32>(src, R, C, ld, dst, plan, ws, stream);
-    case ColType::I32: return launch_typed<TraitsI32>(src, R, C, ld, dst, plan, ws, stream);
-    case ColType::F16: return launch_typed<TraitsF16>(src, R, C, ld, dst, plan, ws, stream);
-    case ColType::BF16: return launch_typed<TraitsBF16>(src, R, C, ld, dst, plan, ws, stream);
-    case ColType::U16: return launch_typed<TraitsU16>(src, R, C, ld, dst, plan, ws, stream);
+    case ColType::F32: return launch_typed<TraitsF32, OpMul<float>>(src, R, C, ld, dst, 0, plan, ws, stream);
+    case ColType::I32: return launch_typed<TraitsI32, OpMul<uint32_t>>(src, R, C, ld, dst, 0, plan, ws, stream);
+    case ColType::F16: return launch_typed<TraitsF16, OpMul<float>>(src, R, C, ld, dst, 0, plan, ws, stream);
+    case ColType::BF16: return launch_typed<TraitsBF16, OpMul<float>>(src, R, C, ld, dst, 0, plan, ws, stream);
+    case ColType::U16: return launch_typed<TraitsU16, OpMul<uint32_t>>(src, R, C, ld, dst, 0, plan, ws, stream);
+    }
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_cols(OpKind op, const float* src, size_t R, size_t C,
+                       size_t ld, float* dst, int accum, const ColprodPlan& plan,
+                       const Workspace& ws, hipStream_t stream)
+{
+    switch (op) {
+    case OpKind::Sum: return launch_typed<TraitsF32, OpSum>(src, R, C, ld, dst, accum, plan, ws, stream);
+    case OpKind::Max: return launch_typed<TraitsF32, OpMax>(src, R, C, ld, dst, accum, plan, ws, stream);
+    case OpKind::Min: return launch_typed<TraitsF32, OpMin>(src, R, C, ld, dst, accum, plan, ws, stream);
     }
     return hipErrorInvalidValue;
 }

@@ -77,5 +77,9 @@ ColprodPlan colprod_plan(ColType t, size_t R, size_t C, const DeviceInfo& dev,
 hipError_t launch_colprod(ColType t, const void* src, size_t R, size_t C,
                           size_t ld, void* dst, const ColprodPlan& plan,
                           const Workspace& ws, hipStream_t stream);
+// Column sum / max / min of an fp32 tile (plan from colprod_plan(F32, ...)).
+hipError_t launch_cols(OpKind op, const float* src, size_t R, size_t C,
+                       size_t ld, float* dst, int accum, const ColprodPlan& plan,
+                       const Workspace& ws, hipStream_t stream);
 
 } // namespace red

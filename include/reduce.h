@@ -153,6 +153,24 @@ int red_min_rows_f32(const float* x, size_t rows, size_t n, size_t ld,
                      float* out, int accum, red_stream_t stream);
 
 /* ---------------------------------------------------------------------
+ * Column sum / max / min: dst[j] = reduce_{i<R} src[i*ld + j], j < C
+ *
+ * The reduction of the TVM page ("reduction -> sm100_packed") taken along
+ * the rows of a 2-D source -- the case its fast path leaves to a generic
+ * fallback ("How inputs change the algorithm", last row).  Layout, ld,
+ * alignment, empty-tile early return and errors as for the column product
+ * below; accum folds old dst[j] into column j first.  Same identities,
+ * NaN policy and tolerances as the 1-D calls: max / min exact, sum within
+ * 1e-6 * (|old| + sum |x|) per column.  Deterministic.
+ * ------------------------------------------------------------------- */
+int red_sum_cols_f32(const float* src, size_t R, size_t C, size_t ld,
+                     float* dst, int accum, red_stream_t stream);
+int red_max_cols_f32(const float* src, size_t R, size_t C, size_t ld,
+                     float* dst, int accum, red_stream_t stream);
+int red_min_cols_f32(const float* src, size_t R, size_t C, size_t ld,
+                     float* dst, int accum, red_stream_t stream);
+
+/* ---------------------------------------------------------------------
  * Column product (TCOLPROD): dst[j] = prod_{i<R} src[i*ld + j], j < C
  *
  * src    : row-major tile of element type T, aligned to sizeof(T); row i

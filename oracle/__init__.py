@@ -13,6 +13,7 @@ passage it follows, is stated in ``oracle.c``:
   "reduction -> sm100_packed" (introduction; "How inputs change the
   algorithm");
 * the page's own single-precision summation order -- same page, "Algorithm";
+* column sum / max / min of a 2-D fp32 tile -- the same reduction along rows;
 * column products over fp32 / fp16 / bf16 / int16 / uint16 / int32 / uint32
   -- PTO ISA "TCOLPROD"
   ("Math Interpretation", "Constraints").
@@ -71,6 +72,9 @@ class Oracle:
             "oracle_colprod_i32": [_P, _SZ, _SZ, _SZ, _P],
             "oracle_colprod_u32": [_P, _SZ, _SZ, _SZ, _P],
             "oracle_colprod_u16": [_P, _SZ, _SZ, _SZ, _P],
+            "oracle_cols_sum_f32": [_P, _SZ, _SZ, _SZ, _I, _P, _P, _P],
+            "oracle_cols_max_f32": [_P, _SZ, _SZ, _SZ, _I, _P],
+            "oracle_cols_min_f32": [_P, _SZ, _SZ, _SZ, _I, _P],
         }
         for name, args in sig.items():
             fn = getattr(lib, name)
@@ -189,6 +193,33 @@ class Oracle:
         """int16 / uint16 column products modulo 2^16, as uint16 patterns."""
         return self._colprod(self.lib.oracle_colprod_u16, src_bits, R, C, ld,
                              np.uint16, np.uint16, dst)
+
+    # -- column sum / max / min -----------------------------------------
+    def cols_sum_f32(self, src, R, C, ld, accum=False, old=None):
+        """Per-column (S, A) arrays in fp64; None for an empty tile."""
+        src = self._rows_view(src, R, C, ld)
+        o = (np.zeros(C, np.float32) if old is None
+             else np.ascontiguousarray(old, dtype=np.float32))
+        s = np.zeros(C, np.float64)
+        a = np.zeros(C, np.float64)
+        ok = self.lib.oracle_cols_sum_f32(_ptr(src), R, C, ld, int(bool(accum)),
+                                          _ptr(o), _ptr(s), _ptr(a))
+        return (s, a) if ok else None
+
+    def cols_max_f32(self, src, R, C, ld, accum=False, dst=None):
+        return self._cols_inplace(self.lib.oracle_cols_max_f32, src, R, C, ld,
+                                  accum, dst)
+
+    def cols_min_f32(self, src, R, C, ld, accum=False, dst=None):
+        return self._cols_inplace(self.lib.oracle_cols_min_f32, src, R, C, ld,
+                                  accum, dst)
+
+    def _cols_inplace(self, fn, src, R, C, ld, accum, dst):
+        src = self._rows_view(src, R, C, ld)
+        d = (np.zeros(C, np.float32) if dst is None
+             else np.array(dst, dtype=np.float32, copy=True))
+        fn(_ptr(src), R, C, ld, int(bool(accum)), _ptr(d))
+        return d
 
     def f16_to_f64(self, h: int) -> float:
         return self.lib.oracle_f16_to_f64(h)

@@ -17,6 +17,9 @@
  *   page-order sum -- same page, section "Algorithm": the 8-slot fp32
  *            accumulator, the chunk-of-8 fold, the scalar remainder and the
  *            8 -> 4 -> 2 -> 1 tree, replayed in single precision.
+ *   column sum / max / min -- the TVM page's reduction taken along the rows
+ *            of a 2-D source (the 2-D case its fast path hands to a generic
+ *            fallback, "How inputs change the algorithm").
  *   colprod -- PTO ISA "TCOLPROD", sections "Math Interpretation" (the
  *            per-column product over the R valid rows) and "Constraints"
  *            (early return for zero valid rows or columns; supported element
@@ -357,6 +360,61 @@ int oracle_colprod_u16(const uint16_t* src, size_t R, size_t C, size_t ld,
         for (size_t i = 0; i < R; i++)
             p *= (uint32_t)src[i * ld + j];
         dst[j] = (uint16_t)(p & 0xffffu);
+    }
+    return 1;
+}
+
+/* ------------------------------------------------------------------ */
+/* Column sum / max / min of a row-major fp32 tile                      */
+/* ------------------------------------------------------------------ */
+
+/* The 1-D definitions applied to each column j < C of the R x C valid
+ * region (row stride ld): the reduction the TVM page's primitive performs,
+ * taken along the first axis of a 2-D source instead of over a whole
+ * vector.  Under accum, column j folds old[j].  R == 0 or C == 0: nothing
+ * written. */
+int oracle_cols_sum_f32(const float* src, size_t R, size_t C, size_t ld,
+                        int accum, const float* old, double* s_out,
+                        double* a_out)
+{
+    if (R == 0 || C == 0)
+        return 0;
+    for (size_t j = 0; j < C; j++) {
+        neumaier_t st = {0.0, 0.0, 0.0, 0};
+        if (accum)
+            neumaier_add(&st, (double)old[j]);
+        for (size_t i = 0; i < R; i++)
+            neumaier_add(&st, (double)src[i * ld + j]);
+        s_out[j] = neumaier_result(&st);
+        a_out[j] = st.a;
+    }
+    return 1;
+}
+
+int oracle_cols_max_f32(const float* src, size_t R, size_t C, size_t ld,
+                        int accum, float* dst)
+{
+    if (R == 0 || C == 0)
+        return 0;
+    for (size_t j = 0; j < C; j++) {
+        float r = accum ? dst[j] : NAN;
+        for (size_t i = 0; i < R; i++)
+            r = max_num(r, src[i * ld + j]);
+        dst[j] = r;
+    }
+    return 1;
+}
+
+int oracle_cols_min_f32(const float* src, size_t R, size_t C, size_t ld,
+                        int accum, float* dst)
+{
+    if (R == 0 || C == 0)
+        return 0;
+    for (size_t j = 0; j < C; j++) {
+        float r = accum ? dst[j] : NAN;
+        for (size_t i = 0; i < R; i++)
+            r = min_num(r, src[i * ld + j]);
+        dst[j] = r;
     }
     return 1;
 }

@@ -457,6 +457,49 @@ def pin_colprod_u16_bruteforce(o):
     assert (o.colprod_u16(t3, 2048, 0, 1, dst=np.full(1, 9, np.uint16)) == 9).all()
 
 
+def pin_cols_bruteforce(o):
+    """Column sum / max / min of an ld-padded tile against exact sums and
+    Python's max / min per column (R != C catches a transposed index); the
+    NaN padding never enters; accum folds old[j]."""
+    rng = np.random.default_rng(23)
+    R, C, ld = 11, 6, 9
+    m = np.full((R, ld), np.nan, np.float32)
+    m[:, :C] = rng.uniform(-5, 5, (R, C)).astype(np.float32)
+    old = rng.uniform(-1, 1, C).astype(np.float32)
+    s, a = o.cols_sum_f32(m, R, C, ld)
+    s2, a2 = o.cols_sum_f32(m, R, C, ld, True, old)
+    mx = o.cols_max_f32(m, R, C, ld)
+    mn = o.cols_min_f32(m, R, C, ld, True, old)
+    for j in range(C):
+        col = m[:R, j]
+        ex = exact_sum(col)
+        ab = sum(abs(Fraction(float(v))) for v in col)
+        assert abs(Fraction(s[j]) - ex) <= Fraction(1, 10**15) * ab
+        assert abs(Fraction(a[j]) - ab) <= Fraction(1, 10**15) * ab
+        ex2 = ex + Fraction(float(old[j]))
+        assert abs(Fraction(s2[j]) - ex2) <= Fraction(1, 10**14) * (ab + 1)
+        assert mx[j] == max(col.tolist())
+        assert mn[j] == min(col.tolist() + [float(old[j])])
+
+
+def pin_cols_closed_forms(o):
+    """Ones sum to R; 1..R sums to R(R+1)/2; NaN policy; empty untouched."""
+    R = 1000
+    s, a = o.cols_sum_f32(np.ones((R, 3), np.float32), R, 3, 3)
+    assert (s == R).all() and (a == R).all()
+    ar = np.repeat(np.arange(1, R + 1, dtype=np.float32)[:, None], 2, axis=1)
+    s, _ = o.cols_sum_f32(ar, R, 2, 2)
+    assert (s == R * (R + 1) / 2).all()
+    assert (o.cols_max_f32(ar, R, 2, 2) == R).all()
+    assert (o.cols_min_f32(ar, R, 2, 2) == 1).all()
+    nan = float("nan")
+    t = np.array([[nan, 1.0], [2.0, nan], [nan, nan]], np.float32)
+    assert o.cols_max_f32(t, 3, 2, 2).tolist() == [2.0, 1.0]
+    assert math.isnan(o.cols_max_f32(t[2:], 1, 2, 2)[0])
+    assert o.cols_sum_f32(t, 0, 2, 2) is None
+    assert (o.cols_min_f32(t, 3, 0, 2, dst=np.full(2, 4.0)) == 4.0).all()
+
+
 PINS = [
     pin_sum_bruteforce, pin_sum_integer_exact, pin_sum_arithmetic_series,
     pin_sum_cancellation, pin_sum_accum, pin_sum_empty, pin_sum_nonfinite,
@@ -469,5 +512,5 @@ PINS = [
     pin_colprod_empty, pin_f16_decode_exhaustive, pin_bf16_decode_exhaustive,
     pin_colprod_16bit_bruteforce, pin_colprod_i32_bruteforce,
     pin_colprod_i32_closed_forms, pin_colprod_u32_bruteforce,
-    pin_colprod_u16_bruteforce,
+    pin_colprod_u16_bruteforce, pin_cols_bruteforce, pin_cols_closed_forms,
 ]

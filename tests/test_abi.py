@@ -51,6 +51,7 @@ def test_header_declares_the_abi():
         assert "red_%s_f32" % op in names
         assert "red_%s_f32_atomic" % op in names
         assert "red_%s_rows_f32" % op in names
+        assert "red_%s_cols_f32" % op in names
     assert "red_sum_max_min_f32" in names
     for t in ("f32", "f16", "bf16", "i32", "i16", "u16", "u32"):
         assert "red_colprod_" + t in names
@@ -117,6 +118,20 @@ def test_rows_validation(lib, name):
     assert f(A16, 1 << 40, 1 << 30, 1 << 30, A16, 0, None) == RED_ERR_INVALID
     assert f(A16 + 2, 3, 4, 4, A16, 0, None) == RED_ERR_ALIGN
     assert f(A16, 3, 4, 4, A16 + 3, 0, None) == RED_ERR_ALIGN
+
+
+@pytest.mark.parametrize("name", ["red_sum_cols_f32", "red_max_cols_f32",
+                                  "red_min_cols_f32"])
+def test_cols_validation(lib, name):
+    f = _fn(lib, name, [P, SZ, SZ, SZ, P, I, P])
+    assert f(None, 0, 16, 16, None, 1, None) == RED_OK
+    assert f(None, 16, 0, 16, None, 1, None) == RED_OK
+    assert f(None, 4, 4, 4, A16, 0, None) == RED_ERR_INVALID
+    assert f(A16, 4, 4, 4, None, 0, None) == RED_ERR_INVALID
+    assert f(A16, 4, 5, 4, A16, 0, None) == RED_ERR_INVALID      # ld < C
+    assert f(A16, 1 << 40, 1 << 30, 1 << 30, A16, 0, None) == RED_ERR_INVALID
+    assert f(A16 + 2, 4, 4, 4, A16, 0, None) == RED_ERR_ALIGN
+    assert f(A16, 4, 4, 4, A16 + 1, 0, None) == RED_ERR_ALIGN
 
 
 @pytest.mark.parametrize("name,es", [("red_colprod_f32", 4), ("red_colprod_i32", 4),
