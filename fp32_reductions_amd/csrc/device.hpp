@@ -1,12 +1,12 @@
 // device.hpp -- device-side building blocks shared by the libreduce kernels
 // (gfx950 / CDNA4, wave64).
 //
-//  * operator traits for sum / max / min with their identities;
+//  * operator traits for sum / max / min with their identities, and the
+//    wave64 DPP reduction (from include/reduce_device.hpp);
 //  * per-thread multi-wide accumulators (8 slots for sum, 4 for max / min)
-//    and their fixed collapse trees;
-//  * a wave64 reduction built from DPP row shifts and row broadcasts;
-//  * a workgroup reduction that combines the per-wave results through LDS
-//    in wave order.
+//    and their fixed collapse trees, for streaming loops;
+//  * the workgroup reduction over a 256-thread library workgroup;
+//  * non-temporal 16-byte streaming loads.
 //
 // Everything here is deterministic: the combination order depends only on
 // lane, wave and workgroup indices, never on timing.
@@ -15,41 +15,20 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "reduce_device.hpp"
+
 namespace red {
 
 constexpr int kBlock = 256;            // threads per workgroup
 constexpr int kWave = 64;              // CDNA wavefront width
 constexpr int kWaves = kBlock / kWave; // wavefronts per workgroup
 
-// ---------------------------------------------------------------------------
-// Operators.  The identity of IEEE addition is -0.0 (x + -0.0 == x for every
-// x, +0 included).  Under maxNum / minNum a quiet NaN is the identity:
-// fmaxf(NaN, x) == x, and the result stays NaN only if every operand is NaN.
-// ---------------------------------------------------------------------------
-struct OpSum {
-    static __device__ __forceinline__ float identity() { return -0.0f; }
-    static __device__ __forceinline__ float apply(float a, float b) { return a + b; }
-};
-
-struct OpMax {
-    static __device__ __forceinline__ float identity() { return __builtin_nanf(""); }
-    static __device__ __forceinline__ float apply(float a, float b) { return fmaxf(a, b); }
-    // Lowered to v_max3_f32.
-    static __device__ __forceinline__ float apply3(float a, float b, float c)
-    {
-        return fmaxf(fmaxf(a, b), c);
-    }
-};
-
-struct OpMin {
-    static __device__ __forceinline__ float identity() { return __builtin_nanf(""); }
-    static __device__ __forceinline__ float apply(float a, float b) { return fminf(a, b); }
-    // Lowered to v_min3_f32.
-    static __device__ __forceinline__ float apply3(float a, float b, float c)
-    {
-        return fminf(fminf(a, b), c);
-    }
-};
+// Operators and the wave reduction come from the public device header, so
+// the library's kernels and kernels written against include/ share them.
+using red_dev::OpMax;
+using red_dev::OpMin;
+using red_dev::OpSum;
+using red_dev::wave_reduce;
 
 // ---------------------------------------------------------------------------
 // Per-thread accumulators.
@@ -159,59 +138,14 @@ __device__ __forceinline__ uint4 load_stream(const uint4* p)
     return make_uint4(v.x, v.y, v.z, v.w);
 }
 
-// ---------------------------------------------------------------------------
-// Wave64 reduction with DPP.
-//
-// GFX9 DPP controls used: row_shr:k (0x110 + k) reads lane i-k of the same
-// 16-lane row; row_bcast:15 (0x142) feeds lane 15 of each row to the next
-// row; row_bcast:31 (0x143) feeds lane 31 to rows 2 and 3.  A lane whose
-// source is outside the row, or whose row is masked off, receives `old`,
-// which is set to the operator's identity (bound_ctrl off).
-//
-// After the four row shifts, lane 15 of each row holds that row's total;
-// the two broadcasts fold row 0 into row 1, row 2 into row 3, then rows
-// 0..1 into rows 2..3, leaving the wave total in lane 63.  Must be called
-// with all 64 lanes active.
-// ---------------------------------------------------------------------------
-template <class Op, int CTRL, int ROW_MASK>
-__device__ __forceinline__ float dpp_fold(float v)
-{
-    const int t = __builtin_amdgcn_update_dpp(__float_as_int(Op::identity()),
-                                              __float_as_int(v), CTRL,
-                                              ROW_MASK, 0xf, false);
-    return Op::apply(v, __int_as_float(t));
-}
-
-template <class Op>
-__device__ __forceinline__ float wave_reduce(float v)
-{
-    v = dpp_fold<Op, 0x111, 0xf>(v); // row_shr:1
-    v = dpp_fold<Op, 0x112, 0xf>(v); // row_shr:2
-    v = dpp_fold<Op, 0x114, 0xf>(v); // row_shr:4
-    v = dpp_fold<Op, 0x118, 0xf>(v); // row_shr:8
-    v = dpp_fold<Op, 0x142, 0xa>(v); // row_bcast:15 -> rows 1, 3
-    v = dpp_fold<Op, 0x143, 0xc>(v); // row_bcast:31 -> rows 2, 3
-    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
-}
-
-// ---------------------------------------------------------------------------
-// Workgroup reduction: every wave reduces with DPP, lane 0 of wave w writes
-// lds[w], and after the barrier every thread folds lds[0..kWaves) in wave
-// order.  Returns the same value in every thread.  `lds` must not be reused
-// before another barrier.
-// ---------------------------------------------------------------------------
+// Workgroup reduction over the kWaves waves of a library workgroup: every
+// wave reduces with DPP, lane 0 of wave w writes lds[w], and after the
+// barrier every thread folds lds[0..kWaves) in wave order.  `lds` must not
+// be reused before another barrier.
 template <class Op>
 __device__ __forceinline__ float block_reduce(float v, float* lds)
 {
-    const float w = wave_reduce<Op>(v);
-    if ((threadIdx.x & (kWave - 1)) == 0)
-        lds[threadIdx.x / kWave] = w;
-    __syncthreads();
-    float r = lds[0];
-#pragma unroll
-    for (int k = 1; k < kWaves; ++k)
-        r = Op::apply(r, lds[k]);
-    return r;
+    return red_dev::block_reduce<Op, kWaves>(v, lds);
 }
 
 } // namespace red
