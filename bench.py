@@ -57,6 +57,7 @@ HBM_PEAK_GBS = 8000.0  # MI355X HBM3E peak, 8 TB/s
 COLD_BYTES = 1 << 30   # other traffic between two reads of the same copy
 PROFILES = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "fp32_reductions_amd", "csrc")
+DEVICE_HEADERS = ["device.hpp", "../../include/reduce_device.hpp"]
 
 
 def log(msg: str) -> None:
@@ -152,6 +153,10 @@ class Rotor:
         return len(self.copies)
 
 
+# The column kernel; a second kernel runs only when the plan splits the rows.
+COLRED = "colred_kernel<{0}, true> (+ colred_finish_kernel<{0}> if rows are split)"
+
+
 def up(torch, a):
     if a.dtype == np.uint16:
         a = a.view(np.int16)
@@ -191,7 +196,7 @@ def wl_vec16m(torch, red, orc, steps):
         "one fp32 vector of 2^24 elements, uniform[-1,1), seed 1; sum, max, min, "
         "then sum, max, min with accum into a destination preset to 3.25",
         {"n": n, "calls_per_step": 6, "cold_copies": len(xs)},
-        calls, ["sum"], ["reduce1d.hip", "device.hpp"], cpu)
+        calls, ["sum"], ["reduce1d.hip"] + DEVICE_HEADERS, cpu)
 
 
 def wl_vec16m_fused(torch, red, orc, steps):
@@ -217,7 +222,7 @@ def wl_vec16m_fused(torch, red, orc, steps):
         "from one read (fused call), then again with accum into destinations preset "
         "to 3.25",
         {"n": n, "calls_per_step": 2, "cold_copies": len(xs)},
-        calls, ["sum_max_min"], ["reduce1d.hip", "device.hpp"], cpu)
+        calls, ["sum_max_min"], ["reduce1d.hip"] + DEVICE_HEADERS, cpu)
 
 
 def wl_vec1g(torch, red, orc, steps):
@@ -238,7 +243,7 @@ def wl_vec1g(torch, red, orc, steps):
         "one fp32 vector of 2^30+7 elements, normal(0,1) with 1% of entries "
         "scaled by 1e6, seed 3; sum, max, min",
         {"n": n, "calls_per_step": 3, "cold_copies": 1},
-        calls, ["sum"], ["reduce1d.hip", "device.hpp"], cpu)
+        calls, ["sum"], ["reduce1d.hip"] + DEVICE_HEADERS, cpu)
 
 
 def wl_colprod4k(torch, red, orc, steps):
@@ -250,9 +255,9 @@ def wl_colprod4k(torch, red, orc, steps):
     is_ = Rotor(up(torch, i), 1, 2 * nbytes)
     of = torch.zeros(C, dtype=torch.float32, device="cuda")
     oi = torch.zeros(C, dtype=torch.int32, device="cuda")
-    calls = [Call("colprod_f32", "colprod_kernel<TraitsF32> + colprod_finish_kernel<TraitsF32>", nbytes,
+    calls = [Call("colprod_f32", COLRED.format("TraitsF32, OpMul<float>"), nbytes,
                   lambda k: red.plan("colprod_f32", fs.next(), of)),
-             Call("colprod_i32", "colprod_kernel<TraitsI32> + colprod_finish_kernel<TraitsI32>", nbytes,
+             Call("colprod_i32", COLRED.format("TraitsI32, OpMul<unsigned int>"), nbytes,
                   lambda k: red.plan("colprod_i32", is_.next(), oi))]
     cpu = [(nbytes, lambda: orc.colprod_f32(f, R, C, C)),
            (nbytes, lambda: orc.colprod_i32(i, R, C, C))]
@@ -261,7 +266,7 @@ def wl_colprod4k(torch, red, orc, steps):
         "column products of a 4096 x 16384 fp32 tile, uniform[0.999,1.001), and "
         "an int32 tile of the same shape, values in {-3..3}\\{0}, seed 2",
         {"R": R, "C": C, "calls_per_step": 2, "cold_copies": len(fs)},
-        calls, ["colprod_f32"], ["colprod.hip", "device.hpp"], cpu)
+        calls, ["colprod_f32"], ["colprod.hip"] + DEVICE_HEADERS, cpu)
 
 
 def wl_colprod_int(torch, red, orc, steps):
@@ -276,9 +281,9 @@ def wl_colprod_int(torch, red, orc, steps):
     us = Rotor(up(torch, u), 1, hb + ub)
     oh = torch.zeros(h.shape[1], dtype=torch.int16, device="cuda")
     ou = torch.zeros(u.shape[1], dtype=torch.int32, device="cuda")
-    calls = [Call("colprod_i16", "colprod_kernel<TraitsU16> + colprod_finish_kernel<TraitsU16>", hb,
+    calls = [Call("colprod_i16", COLRED.format("TraitsU16, OpMul<unsigned int>"), hb,
                   lambda k: red.plan("colprod_i16", hs.next(), oh)),
-             Call("colprod_u32", "colprod_kernel<TraitsI32> + colprod_finish_kernel<TraitsI32>", ub,
+             Call("colprod_u32", COLRED.format("TraitsI32, OpMul<unsigned int>"), ub,
                   lambda k: red.plan("colprod_u32", us.next(), ou))]
     cpu = [(hb, lambda: orc.colprod_u16(h.view(np.uint16), 2048, 32768, 32768)),
            (ub, lambda: orc.colprod_u32(u.view(np.uint32), 4096, 16384, 16384))]
@@ -287,7 +292,7 @@ def wl_colprod_int(torch, red, orc, steps):
         "column products of a 2048 x 32768 int16 tile and a 4096 x 16384 uint32 tile, "
         "values uniform over {-3, -1, 1, 3} (seeds 51, 52)",
         {"calls_per_step": 2, "cold_copies": [len(hs), len(us)]},
-        calls, ["colprod_i16"], ["colprod.hip", "device.hpp"], cpu)
+        calls, ["colprod_i16"], ["colprod.hip"] + DEVICE_HEADERS, cpu)
 
 
 def wl_rows1000(torch, red, orc, steps):
@@ -305,13 +310,13 @@ def wl_rows1000(torch, red, orc, steps):
     o2 = torch.zeros(rows, dtype=torch.float32, device="cuda")
     ob = torch.zeros(C, dtype=torch.bfloat16, device="cuda")
     oh = torch.zeros(C, dtype=torch.float16, device="cuda")
-    calls = [Call("rows_sum", "rows_wave_kernel<OpSum>", rbytes,
+    calls = [Call("rows_sum", "rows_wave2_kernel<OpSum>", rbytes,
                   lambda k: red.plan("sum_rows_f32", xs.next(), o1)),
-             Call("rows_max", "rows_wave_kernel<OpMax>", rbytes,
+             Call("rows_max", "rows_wave2_kernel<OpMax>", rbytes,
                   lambda k: red.plan("max_rows_f32", xs.next(), o2)),
-             Call("colprod_bf16", "colprod_kernel<TraitsBF16> + colprod_finish_kernel<TraitsBF16>", tbytes,
+             Call("colprod_bf16", COLRED.format("TraitsBF16, OpMul<float>"), tbytes,
                   lambda k: red.plan("colprod_bf16", bs.next(), ob)),
-             Call("colprod_f16", "colprod_kernel<TraitsF16> + colprod_finish_kernel<TraitsF16>", tbytes,
+             Call("colprod_f16", COLRED.format("TraitsF16, OpMul<float>"), tbytes,
                   lambda k: red.plan("colprod_f16", hs.next(), oh))]
     cpu = [(rbytes, lambda: orc.rows_sum_f32(x, rows, n, n)),
            (rbytes, lambda: orc.rows_max_f32(x, rows, n, n)),
@@ -323,7 +328,7 @@ def wl_rows1000(torch, red, orc, steps):
         "products of 2048 x 32768 bf16 and f16 tiles, uniform[0.99,1.01), seed 4",
         {"rows": rows, "n": n, "R": R, "C": C, "calls_per_step": 4,
          "cold_copies": [len(xs), len(bs), len(hs)]},
-        calls, ["rows_sum"], ["rows.hip", "device.hpp"], cpu)
+        calls, ["rows_sum"], ["rows.hip"] + DEVICE_HEADERS, cpu)
 
 
 def wl_cols4k(torch, red, orc, steps):
@@ -333,7 +338,7 @@ def wl_cols4k(torch, red, orc, steps):
     nbytes = 4 * R * C + 4 * C
     ts = Rotor(up(torch, t), 3, 3 * nbytes)
     outs = [torch.zeros(C, dtype=torch.float32, device="cuda") for _ in range(3)]
-    calls = [Call(op + "_cols", "colred_kernel<TraitsF32, Op%s> + colred_finish_kernel" % op.capitalize(),
+    calls = [Call(op + "_cols", COLRED.format("TraitsF32, Op%s" % op.capitalize()),
                   nbytes, lambda k, op=op, j=j: red.plan(op + "_cols_f32", ts.next(), outs[j]))
              for j, op in enumerate(("sum", "max", "min"))]
     cpu = [(nbytes, lambda: orc.cols_sum_f32(t, R, C, C)),
@@ -343,7 +348,7 @@ def wl_cols4k(torch, red, orc, steps):
         "cols4k",
         "column sum, max and min of a 4096 x 16384 fp32 tile, uniform[-1,1), seed 60",
         {"R": R, "C": C, "calls_per_step": 3, "cold_copies": len(ts)},
-        calls, ["sum_cols"], ["colprod.hip", "device.hpp"], cpu)
+        calls, ["sum_cols"], ["colprod.hip"] + DEVICE_HEADERS, cpu)
 
 
 def wl_rows32(torch, red, orc, steps):
@@ -359,7 +364,7 @@ def wl_rows32(torch, red, orc, steps):
                   lambda k: red.plan("max_rows_f32", ad, o[1])),
              Call("rows_min", "rows_thread_kernel<OpMin>", rbytes,
                   lambda k: red.plan("min_rows_f32", ad, o[2])),
-             Call("colprod_tile16", "colprod_kernel<TraitsF32>", 16 * 16 * 4 + 64,
+             Call("colprod_tile16", COLRED.format("TraitsF32, OpMul<float>"), 16 * 16 * 4 + 64,
                   lambda k: red.plan("colprod_f32", td, ot))]
     cpu = [(rbytes, lambda: orc.rows_page_sum_f32(a, rows, n, n)),
            (rbytes, lambda: orc.rows_max_f32(a, rows, n, n)),
@@ -370,7 +375,7 @@ def wl_rows32(torch, red, orc, steps):
         "4096 rows x 32 fp32, uniform[-1,1), seed 0: row sum, max, min (one "
         "thread per row); one 16 x 16 fp32 tile column product",
         {"rows": rows, "n": n, "calls_per_step": 4, "cold_copies": 1},
-        calls, ["rows_sum"], ["rows.hip", "device.hpp"], cpu)
+        calls, ["rows_sum"], ["rows.hip"] + DEVICE_HEADERS, cpu)
 
 
 def wl_copycal(torch, red, orc, steps):

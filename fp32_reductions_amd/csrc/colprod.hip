@@ -10,10 +10,12 @@
 // Layout of the work:
 //  * each lane owns V consecutive columns, V = 16 bytes / sizeof(T) (4 for
 //    f32 / i32, 8 for f16 / bf16), so one 16-byte load per row feeds all of
-//    them and a wave reads 1 KiB of a row contiguously;
-//  * a workgroup (4 waves) covers one block of 64*V columns and a slice of
-//    rows; its waves take interleaved rows of the slice and combine their
-//    partial products in LDS in wave order;
+//    them; 16 lanes cover 256 contiguous bytes of a row and a wave reads
+//    four rows per load;
+//  * a workgroup (256 threads = 16 row groups of 16 lanes) covers one block
+//    of 16*V columns and a slice of rows; its row groups take interleaved
+//    rows of the slice and combine their partial products in LDS in
+//    row-group order;
 //  * when the grid needs more workgroups than there are column blocks, the
 //    rows are split into S slices (blockIdx.y); each workgroup stores its
 //    partial row in the workspace, and a second kernel multiplies the S
@@ -36,7 +38,11 @@
 namespace red {
 namespace {
 
-constexpr int kRowsInFlight = 8; // 16-byte loads in flight per lane
+#ifndef RED_COLPROD_UNROLL
+#define RED_COLPROD_UNROLL 8
+#endif
+constexpr int kRowsInFlight = RED_COLPROD_UNROLL; // 16-byte loads in flight per lane
+constexpr int kLanesPerRow = 16;                  // lanes sharing one row of a column block
 
 struct TraitsF32 {
     using T = float;
@@ -152,6 +158,16 @@ struct OpMul {
 // Op combines accumulators (OpMul for TCOLPROD; OpSum / OpMax / OpMin for
 // the column sum / max / min).  Under accum (never for products) the old
 // dst[j] is folded in first.
+//
+// A workgroup owns kCols = 16 * V columns (256 bytes of each row) and the
+// rows of its slice.  Its 256 threads form 16 row groups of 16 lanes: row
+// group g reads rows g, g + 16, g + 32, ... of the slice, each lane one
+// 16-byte vector per row, with kRowsInFlight rows in flight.  The 16 row
+// groups' partial products are combined in LDS in row-group order.
+// (Measured on MI355X for a 4096 x 16384 fp32 tile read from HBM: 40.6 us
+// per call with 256 such workgroups and no second pass, against 44.1 us
+// for workgroups of 256 columns whose waves each read 1 KiB of a row, split
+// four ways over the rows and finished by a second kernel.)
 template <class Tr, class Op, bool VEC>
 __global__ __launch_bounds__(kBlock) void colred_kernel(
     const typename Tr::T* __restrict__ src, uint64_t R, uint64_t C,
@@ -161,16 +177,17 @@ __global__ __launch_bounds__(kBlock) void colred_kernel(
     using T = typename Tr::T;
     using A = typename Tr::A;
     constexpr int V = Tr::V;
-    constexpr int kCols = kWave * V; // columns per workgroup
+    constexpr int kCols = kLanesPerRow * V;         // columns per workgroup
+    constexpr int kGroups = kBlock / kLanesPerRow;  // row groups per workgroup
 
-    __shared__ A lds[kWaves][kCols];
+    __shared__ A lds[kGroups][kCols];
 
-    const uint32_t lane = threadIdx.x & (kWave - 1);
-    const uint32_t wave = threadIdx.x / kWave;
+    const uint32_t g = threadIdx.x / kLanesPerRow;
+    const uint32_t q = threadIdx.x % kLanesPerRow;
     const uint64_t cb = blockIdx.x;
     const uint32_t S = gridDim.y;
     const uint64_t s = blockIdx.y;
-    const uint64_t j0 = cb * kCols + (uint64_t)lane * V;
+    const uint64_t j0 = cb * kCols + (uint64_t)q * V;
     const uint64_t r0 = s * rows_per_split;
     const uint64_t r1 = (r0 + rows_per_split < R) ? r0 + rows_per_split : R;
 
@@ -181,15 +198,15 @@ __global__ __launch_bounds__(kBlock) void colred_kernel(
 
     if (j0 < C) {
         const T* __restrict__ col = src + j0;
-        uint64_t r = r0 + wave;
+        uint64_t r = r0 + g;
         if (VEC && j0 + V <= C) {
-            for (; r + (uint64_t)kWaves * (kRowsInFlight - 1) < r1;
-                 r += (uint64_t)kWaves * kRowsInFlight) {
+            for (; r + (uint64_t)kGroups * (kRowsInFlight - 1) < r1;
+                 r += (uint64_t)kGroups * kRowsInFlight) {
                 uint4 v[kRowsInFlight];
 #pragma unroll
                 for (int u = 0; u < kRowsInFlight; ++u)
                     v[u] = load_stream(reinterpret_cast<const uint4*>(
-                        col + (r + (uint64_t)u * kWaves) * ld));
+                        col + (r + (uint64_t)u * kGroups) * ld));
 #pragma unroll
                 for (int u = 0; u < kRowsInFlight; ++u) {
                     A a[V];
@@ -199,7 +216,7 @@ __global__ __launch_bounds__(kBlock) void colred_kernel(
                         acc[k] = Op::apply(acc[k], a[k]);
                 }
             }
-            for (; r < r1; r += kWaves) {
+            for (; r < r1; r += kGroups) {
                 A a[V];
                 Tr::unpack(load_stream(reinterpret_cast<const uint4*>(col + r * ld)), a);
 #pragma unroll
@@ -207,7 +224,7 @@ __global__ __launch_bounds__(kBlock) void colred_kernel(
                     acc[k] = Op::apply(acc[k], a[k]);
             }
         } else {
-            for (; r < r1; r += kWaves) {
+            for (; r < r1; r += kGroups) {
 #pragma unroll
                 for (int k = 0; k < V; ++k)
                     if (j0 + k < C)
@@ -216,16 +233,17 @@ __global__ __launch_bounds__(kBlock) void colred_kernel(
         }
     }
 
-    // Combine the four waves' partial rows in wave order.
+    // Combine the row groups' partial rows in row-group order.
 #pragma unroll
     for (int k = 0; k < V; ++k)
-        lds[wave][lane * V + k] = acc[k];
+        lds[g][q * V + k] = acc[k];
     __syncthreads();
 
-    for (uint32_t c = threadIdx.x; c < (uint32_t)kCols; c += kBlock) {
+    if (threadIdx.x < (uint32_t)kCols) {
+        const uint32_t c = threadIdx.x;
         A p = lds[0][c];
 #pragma unroll
-        for (int w = 1; w < kWaves; ++w)
+        for (int w = 1; w < kGroups; ++w)
             p = Op::apply(p, lds[w][c]);
         const uint64_t j = cb * kCols + c;
         if (j < C) {
@@ -293,7 +311,7 @@ ColprodPlan colprod_plan(ColType t, size_t R, size_t C, const DeviceInfo& dev,
                          const Workspace& ws)
 {
     ColprodPlan p;
-    const uint64_t cols = (uint64_t)kWave * (16 / colprod_elem_size(t));
+    const uint64_t cols = (uint64_t)kLanesPerRow * (16 / colprod_elem_size(t));
     p.col_blocks = (unsigned)((C + cols - 1) / cols);
     const uint64_t target = (uint64_t)dev.cus * kColprodWgPerCu;
     uint64_t S = 1;
