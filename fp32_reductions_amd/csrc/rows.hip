@@ -11,11 +11,12 @@
 //    (0,1)+=(2,3), (4,5)+=(6,7), (0,1)+=(4,5), result = slot 0 + slot 1.
 //    accum adds the old destination into slot 0 first ("How inputs change
 //    the algorithm").  max / min use four slots folded with max3 / min3.
-//  * rows_wave2 (64 < n <= 1024): one wave64 per pair of rows; each lane
-//    issues its four non-temporal 16-byte loads of both rows, keeps one
-//    multi-wide accumulator per row, then two DPP wave reduces; lane 0
-//    stores.  Each workgroup walks a contiguous range of rows.  No LDS, no
-//    second pass.
+//  * rows_seg (64 < n <= 1024): 16, 32 or 64 lanes per row (by n), each
+//    lane holding up to two or four non-temporal 16-byte loads of a row, and
+//    2 to 16 rows per wave, every load issued before any row is reduced;
+//    one multi-wide accumulator per row, a DPP reduction over each lane
+//    segment; the segment's last lane stores.  Each workgroup walks a
+//    contiguous range of rows.  No LDS, no second pass.
 //  * rows_wave: the same with one row per wave and any n, looping over the
 //    row four vectors per lane at a time.
 //  * rows_block: one 256-thread workgroup per row, for few very long rows.
@@ -164,8 +165,7 @@ __device__ __forceinline__ float row_lane_part(const float* __restrict__ p,
     return acc.collapse();
 }
 
-// Two rows per wave at a time when both are short enough for one sweep:
-// all of both rows' loads are issued before either row is reduced.
+// Rows of at most kPairRowMax elements go to the segmented kernel below.
 constexpr uint64_t kPairRowMax = (uint64_t)kWave * kRowUnroll * 4; // 1024 elements
 
 template <class Op>
@@ -186,54 +186,81 @@ __global__ __launch_bounds__(kBlock) void rows_wave_kernel(
     }
 }
 
-// Rows of at most kPairRowMax elements: each workgroup owns a contiguous
-// range of rows (a multiple of 8), and in every step its four waves take
-// the next eight rows, two consecutive rows per wave, loading both before
-// reducing either.
-template <class Op>
-__global__ __launch_bounds__(kBlock) void rows_wave2_kernel(
+// Reduction over segments of G consecutive lanes (G = 16, 32 or 64) with the
+// DPP steps of the wave reduction: the row shifts total each 16-lane row,
+// row_bcast:15 joins rows (0,1) and (2,3), row_bcast:31 joins the halves.
+// The segment's total lands in its last lane.
+template <class Op, int G>
+__device__ __forceinline__ float segment_reduce(float v)
+{
+    static_assert(G == 16 || G == 32 || G == 64, "segments of 16, 32 or 64 lanes");
+    v = red_dev::dpp_fold<Op, 0x111, 0xf>(v); // row_shr:1
+    v = red_dev::dpp_fold<Op, 0x112, 0xf>(v); // row_shr:2
+    v = red_dev::dpp_fold<Op, 0x114, 0xf>(v); // row_shr:4
+    v = red_dev::dpp_fold<Op, 0x118, 0xf>(v); // row_shr:8
+    if constexpr (G >= 32)
+        v = red_dev::dpp_fold<Op, 0x142, 0xa>(v); // row_bcast:15 -> rows 1, 3
+    if constexpr (G == 64)
+        v = red_dev::dpp_fold<Op, 0x143, 0xc>(v); // row_bcast:31 -> rows 2, 3
+    return v;
+}
+
+// Rows of at most kPairRowMax elements.  G lanes share a row (G = 16 for
+// n <= 256, 32 for n <= 512, 64 above), each holding up to U 16-byte
+// vectors of it; a wave covers 64 / G rows per pass and P passes per step.
+// Every load of a step -- vectors, and the scalars before the row's first
+// 16-byte boundary and after its last whole vector -- is issued before any
+// row is reduced.  Each workgroup owns a contiguous range of rows, a
+// multiple of the rows its four waves cover in one step.  Lane 0 of a
+// segment carries the old value under accum; the segment's last lane
+// stores.
+template <class Op, int G, int U, int P>
+__global__ __launch_bounds__(kBlock) void rows_seg_kernel(
     const float* __restrict__ x, uint64_t rows, uint64_t n, uint64_t ld,
     float* __restrict__ out, int accum, uint64_t rows_per_wg)
 {
+    static_assert(U % 2 == 0, "vectors are folded in pairs");
+    constexpr int kSegs = kWave / G;         // rows per pass of a wave
+    constexpr int kRowsPerWave = kSegs * P;  // rows per step of a wave
     const uint32_t lane = threadIdx.x & (kWave - 1);
+    const uint32_t seg = lane / G;
+    const uint32_t q = lane % G;
     const uint64_t b0 = (uint64_t)blockIdx.x * rows_per_wg;
     const uint64_t b1 = (b0 + rows_per_wg < rows) ? b0 + rows_per_wg : rows;
-    for (uint64_t r = b0 + 2 * (threadIdx.x / kWave); r < b1; r += 2 * kWaves) {
-        const bool second = r + 1 < b1; // uniform across the wave
-        const float* __restrict__ p0 = x + r * ld;
-        const float* __restrict__ p1 = second ? p0 + ld : p0;
-        const uint32_t h0 = head_count(p0, n), h1 = head_count(p1, n);
-        const uint64_t nv0 = (n - h0) / 4, nv1 = (n - h1) / 4;
-        const float4* __restrict__ v0 = reinterpret_cast<const float4*>(p0 + h0);
-        const float4* __restrict__ v1 = reinterpret_cast<const float4*>(p1 + h1);
-        float4 a[kRowUnroll], b[kRowUnroll];
+    for (uint64_t base = b0 + (uint64_t)(threadIdx.x / kWave) * kRowsPerWave; base < b1;
+         base += (uint64_t)kWaves * kRowsPerWave) {
+        float4 v[P][U];
+        float hv[P], tv[P];
 #pragma unroll
-        for (int u = 0; u < kRowUnroll; ++u) {
-            const uint64_t idx = lane + (uint64_t)u * kWave;
-            a[u] = idx < nv0 ? load_stream(v0 + idx) : identity4<Op>();
-            b[u] = (second && idx < nv1) ? load_stream(v1 + idx) : identity4<Op>();
-        }
-        Acc<Op> acc0((lane == 0 && accum) ? out[r] : Op::identity());
-        Acc<Op> acc1((lane == 0 && accum && second) ? out[r + 1] : Op::identity());
+        for (int p = 0; p < P; ++p) {
+            const uint64_t r = base + (uint64_t)p * kSegs + seg;
+            const bool valid = r < b1;
+            const float* __restrict__ row = x + (valid ? r : base) * ld;
+            const uint32_t h = head_count(row, n);
+            const uint64_t nv = (n - h) / 4;
+            const uint64_t tail = h + 4 * nv + q;
+            const float4* __restrict__ rv = reinterpret_cast<const float4*>(row + h);
 #pragma unroll
-        for (int u = 0; u < kRowUnroll; u += 2) {
-            acc0.fold2(a[u], a[u + 1]);
-            acc1.fold2(b[u], b[u + 1]);
+            for (int u = 0; u < U; ++u) {
+                const uint64_t idx = q + (uint64_t)u * G;
+                v[p][u] = (valid && idx < nv) ? load_stream(rv + idx) : identity4<Op>();
+            }
+            hv[p] = (valid && q < h) ? row[q] : Op::identity();
+            tv[p] = (valid && tail < n) ? row[tail] : Op::identity();
         }
-        if (lane < h0)
-            acc0.fold_scalar(p0[lane]);
-        if (lane < h1)
-            acc1.fold_scalar(p1[lane]);
-        if (h0 + 4 * nv0 + lane < n)
-            acc0.fold_scalar(p0[h0 + 4 * nv0 + lane]);
-        if (h1 + 4 * nv1 + lane < n)
-            acc1.fold_scalar(p1[h1 + 4 * nv1 + lane]);
-        const float t0 = wave_reduce<Op>(acc0.collapse());
-        const float t1 = wave_reduce<Op>(acc1.collapse());
-        if (lane == 0) {
-            out[r] = t0;
-            if (second)
-                out[r + 1] = t1;
+#pragma unroll
+        for (int p = 0; p < P; ++p) {
+            const uint64_t r = base + (uint64_t)p * kSegs + seg;
+            const bool valid = r < b1;
+            Acc<Op> acc((q == 0 && accum && valid) ? out[r] : Op::identity());
+#pragma unroll
+            for (int u = 0; u < U; u += 2)
+                acc.fold2(v[p][u], v[p][u + 1]);
+            acc.fold_scalar(hv[p]); // the identity where a lane has none
+            acc.fold_scalar(tv[p]);
+            const float t = segment_reduce<Op, G>(acc.collapse());
+            if (valid && q == G - 1)
+                out[r] = t;
         }
     }
 }
@@ -263,6 +290,23 @@ __host__ inline unsigned cap_grid(uint64_t g)
     return (unsigned)(g < kMaxRowGrid ? (g ? g : 1) : kMaxRowGrid);
 }
 
+// Contiguous row ranges, a multiple of the rows a workgroup covers in one
+// step, for at most kRowsWgPerCu workgroups per CU.  (Measured on MI355X
+// for 65536 rows of 1000 from HBM: 39.9 us at 16 per CU, 40.5 at 4, 41.5
+// at 8; one workgroup per 8 rows took 41.0 us.)
+template <class Op, int G, int U, int P>
+void launch_seg(const float* x, uint64_t rows, uint64_t n, uint64_t ld,
+                float* out, int accum, const DeviceInfo& dev, hipStream_t stream)
+{
+    constexpr uint64_t kStepRows = (uint64_t)kWaves * (kWave / G) * P;
+    const uint64_t steps = (rows + kStepRows - 1) / kStepRows;
+    const uint64_t cap = (uint64_t)dev.cus * kRowsWgPerCu;
+    const uint64_t grid = steps < cap ? steps : cap;
+    const uint64_t per = (steps + grid - 1) / grid * kStepRows;
+    rows_seg_kernel<Op, G, U, P><<<(unsigned)((rows + per - 1) / per), kBlock, 0, stream>>>(
+        x, rows, n, ld, out, accum, per);
+}
+
 template <class Op>
 hipError_t launch_rows_op(const float* x, size_t rows, size_t n, size_t ld,
                           float* out, int accum, const DeviceInfo& dev,
@@ -278,16 +322,16 @@ hipError_t launch_rows_op(const float* x, size_t rows, size_t n, size_t ld,
             rows_thread_kernel<Op, false><<<grid, kBlock, 0, stream>>>(
                 x, rows, (uint32_t)n, ld, out, accum);
     } else if (n <= kPairRowMax) {
-        // Contiguous row ranges, a multiple of 8 rows each, for at most
-        // kRowsWgPerCu workgroups per CU.  (Measured on MI355X for 65536
-        // rows of 1000 from HBM: 39.9 us at 16 per CU, 40.5 at 4, 41.5 at
-        // 8; one workgroup per 8 rows took 41.0 us.)
-        const uint64_t steps = (rows + 2 * kWaves - 1) / (2 * kWaves);
-        const uint64_t cap = (uint64_t)dev.cus * kRowsWgPerCu;
-        const uint64_t grid = steps < cap ? steps : cap;
-        const uint64_t per = (steps + grid - 1) / grid * (2 * kWaves);
-        rows_wave2_kernel<Op><<<(unsigned)((rows + per - 1) / per), kBlock, 0, stream>>>(
-            x, rows, n, ld, out, accum, per);
+        // <G lanes per row, U vectors per lane and row, P rows per segment>:
+        // 4 * G * U >= n covers the row; U * P = 8 loads per lane in flight.
+        if (n <= 128)
+            launch_seg<Op, 16, 2, 4>(x, rows, n, ld, out, accum, dev, stream);
+        else if (n <= 256)
+            launch_seg<Op, 16, 4, 2>(x, rows, n, ld, out, accum, dev, stream);
+        else if (n <= 512)
+            launch_seg<Op, 32, 4, 2>(x, rows, n, ld, out, accum, dev, stream);
+        else
+            launch_seg<Op, 64, 4, 2>(x, rows, n, ld, out, accum, dev, stream);
     } else if (n <= kWaveRowMax || rows >= (size_t)dev.cus * kRowsWavePerCu) {
         const unsigned grid = cap_grid((rows + kWaves - 1) / kWaves);
         rows_wave_kernel<Op><<<grid, kBlock, 0, stream>>>(x, rows, n, ld, out,

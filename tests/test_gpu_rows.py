@@ -103,6 +103,13 @@ SHAPES = [  # (rows, n, ld, element offset of the base pointer)
     (300, 64, 64, 0), (300, 64, 67, 3), (257, 65, 65, 0), (100, 100, 103, 1),
     (70, 1000, 1000, 2), (3, 4097, 4100, 0), (1, 16385, 16385, 0),
     (2, 100003, 100010, 1), (4096, 31, 32, 0), (2049, 250, 256, 0),
+    # every lanes-per-row / rows-per-wave choice of the 64 < n <= 1024 kernel,
+    # at its boundaries, with row counts that leave ragged workgroup steps
+    (1, 65, 65, 0), (17, 127, 127, 1), (33, 128, 128, 0), (63, 129, 131, 3),
+    (100, 200, 200, 2), (65, 255, 255, 1), (129, 256, 256, 0), (7, 257, 260, 0),
+    (1000, 300, 300, 3), (31, 511, 511, 2), (4099, 512, 512, 0), (9, 513, 515, 1),
+    (70, 700, 701, 0), (5, 1023, 1023, 3), (300, 1024, 1024, 0),
+    (300000, 100, 100, 0), (70001, 384, 384, 1),
 ]
 
 
