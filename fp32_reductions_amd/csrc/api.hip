@@ -169,8 +169,12 @@ int reduce_rows(OpKind op, const float* x, size_t rows, size_t n, size_t ld,
     int st = current_device(&dev, &info);
     if (st != RED_OK)
         return st;
-    return hip_status(red::launch_rows(op, x, rows, n, ld, out, accum, info,
-                                       static_cast<hipStream_t>(stream)));
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    Workspace ws;
+    if (red::rows_chunks(x, rows, n, info) > 1 &&
+        (st = stream_workspace(dev, s, &ws)) != RED_OK)
+        return st;
+    return hip_status(red::launch_rows(op, x, rows, n, ld, out, accum, info, ws, s));
 }
 
 // Column reductions share validation: ld >= C, extents, grid limit,

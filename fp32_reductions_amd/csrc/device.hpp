@@ -138,6 +138,70 @@ __device__ __forceinline__ uint4 load_stream(const uint4* p)
     return make_uint4(v.x, v.y, v.z, v.w);
 }
 
+// ---------------------------------------------------------------------------
+// Streaming one contiguous vector in chunks.
+//
+// The vector's whole 16-byte vectors are cut into `chunks` contiguous
+// chunks of whole sweeps (kSweep vectors: kStreamUnroll loads in flight per
+// thread); a workgroup streams chunk `chunk` into its threads'
+// accumulators.  The scalars before the first 16-byte boundary and after
+// the last whole vector go to thread 0 of chunk 0.  The last chunks may be
+// short or empty.
+// ---------------------------------------------------------------------------
+#ifndef RED_STREAM_UNROLL
+#define RED_STREAM_UNROLL 8
+#endif
+constexpr int kStreamUnroll = RED_STREAM_UNROLL;                 // loads in flight per thread
+constexpr uint64_t kSweep = (uint64_t)kBlock * kStreamUnroll;    // vectors per workgroup sweep
+
+// Elements before the first 16-byte boundary of x (x is 4-byte aligned).
+__host__ __device__ inline uint32_t head_count(const float* x, uint64_t n)
+{
+    const uint32_t mis = (uint32_t)(((uintptr_t)x >> 2) & 3u);
+    const uint64_t h = (4u - mis) & 3u;
+    return (uint32_t)(h < n ? h : n);
+}
+
+// Whole sweeps of the vector x[0, n).
+__host__ __device__ inline uint64_t sweep_count(const float* x, uint64_t n)
+{
+    return ((n - head_count(x, n)) / 4 + kSweep - 1) / kSweep;
+}
+
+template <class AccT>
+__device__ __forceinline__ void stream_chunk(const float* __restrict__ x,
+                                             uint64_t n, uint64_t chunk,
+                                             uint64_t chunks, AccT& acc)
+{
+    const uint32_t head = head_count(x, n);
+    const uint64_t nvec = (n - head) / 4;
+    const float4* __restrict__ xv = reinterpret_cast<const float4*>(x + head);
+
+    const uint64_t per_chunk = (nvec + chunks - 1) / chunks;
+    const uint64_t per = (per_chunk + kSweep - 1) / kSweep * kSweep;
+    const uint64_t b0 = chunk * per;
+    const uint64_t b1 = (b0 + per < nvec) ? b0 + per : nvec;
+
+    uint64_t i = b0 + threadIdx.x;
+    for (; i + (uint64_t)(kStreamUnroll - 1) * kBlock < b1; i += kSweep) {
+        float4 v[kStreamUnroll];
+#pragma unroll
+        for (int u = 0; u < kStreamUnroll; ++u)
+            v[u] = load_stream(xv + i + (uint64_t)u * kBlock);
+#pragma unroll
+        for (int u = 0; u < kStreamUnroll; u += 2)
+            acc.fold2(v[u], v[u + 1]);
+    }
+    for (; i < b1; i += kBlock)
+        acc.fold1(load_stream(xv + i));
+    if (chunk == 0 && threadIdx.x == 0) {
+        for (uint32_t k = 0; k < head; ++k)
+            acc.fold_scalar(x[k]);
+        for (uint64_t k = head + 4 * nvec; k < n; ++k)
+            acc.fold_scalar(x[k]);
+    }
+}
+
 // Workgroup reduction over the kWaves waves of a library workgroup: every
 // wave reduces with DPP, lane 0 of wave w writes lds[w], and after the
 // barrier every thread folds lds[0..kWaves) in wave order.  `lds` must not

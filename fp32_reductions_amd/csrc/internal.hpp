@@ -57,9 +57,13 @@ hipError_t launch_fill_u32(unsigned* p, size_t count, unsigned value,
                            hipStream_t stream);
 
 // ---- segmented rows (rows.hip) --------------------------------------------
+// Chunks per row of the split row kernel for this problem: 0 when another
+// row kernel runs, 1 when it needs no partials, K > 1 when it writes
+// rows * K partials to the workspace.
+uint32_t rows_chunks(const float* x, size_t rows, size_t n, const DeviceInfo& dev);
 hipError_t launch_rows(OpKind op, const float* x, size_t rows, size_t n,
                        size_t ld, float* out, int accum, const DeviceInfo& dev,
-                       hipStream_t stream);
+                       const Workspace& ws, hipStream_t stream);
 
 // ---- column product (colprod.hip) -----------------------------------------
 // U16 carries int16 and uint16 (same bits); uint32 runs as I32 (same bits).

@@ -27,66 +27,15 @@
 #include "device.hpp"
 #include "internal.hpp"
 
-#ifndef RED_STREAM_UNROLL
-#define RED_STREAM_UNROLL 8
-#endif
-
 namespace red {
 namespace {
-
-constexpr int kUnroll = RED_STREAM_UNROLL;         // 16-byte loads in flight per thread
-constexpr uint64_t kSweep = (uint64_t)kBlock * kUnroll; // vectors per workgroup sweep
-
-// Elements before the first 16-byte boundary of x (x is 4-byte aligned).
-__host__ __device__ inline uint32_t head_count(const float* x, uint64_t n)
-{
-    const uint32_t mis = (uint32_t)(((uintptr_t)x >> 2) & 3u);
-    const uint64_t h = (4u - mis) & 3u;
-    return (uint32_t)(h < n ? h : n);
-}
-
-// Per-thread streaming: this workgroup's contiguous chunk of whole vectors,
-// plus (workgroup 0, thread 0) the scalar head and tail, folded into `acc`.
-template <class AccT>
-__device__ __forceinline__ void stream_part(const float* __restrict__ x,
-                                            uint64_t n, AccT& acc)
-{
-    const uint32_t head = head_count(x, n);
-    const uint64_t nvec = (n - head) / 4;
-    const float4* __restrict__ xv = reinterpret_cast<const float4*>(x + head);
-
-    // Chunk of whole sweeps; the last chunks may be short or empty.
-    const uint64_t per_wg = (nvec + gridDim.x - 1) / gridDim.x;
-    const uint64_t per = (per_wg + kSweep - 1) / kSweep * kSweep;
-    const uint64_t b0 = (uint64_t)blockIdx.x * per;
-    const uint64_t b1 = (b0 + per < nvec) ? b0 + per : nvec;
-
-    uint64_t i = b0 + threadIdx.x;
-    for (; i + (uint64_t)(kUnroll - 1) * kBlock < b1; i += kSweep) {
-        float4 v[kUnroll];
-#pragma unroll
-        for (int u = 0; u < kUnroll; ++u)
-            v[u] = load_stream(xv + i + (uint64_t)u * kBlock);
-#pragma unroll
-        for (int u = 0; u < kUnroll; u += 2)
-            acc.fold2(v[u], v[u + 1]);
-    }
-    for (; i < b1; i += kBlock)
-        acc.fold1(load_stream(xv + i));
-    if (blockIdx.x == 0 && threadIdx.x == 0) {
-        for (uint32_t k = 0; k < head; ++k)
-            acc.fold_scalar(x[k]);
-        for (uint64_t k = head + 4 * nvec; k < n; ++k)
-            acc.fold_scalar(x[k]);
-    }
-}
 
 template <class Op>
 __device__ __forceinline__ float thread_part(const float* __restrict__ x,
                                              uint64_t n)
 {
     Acc<Op> acc(Op::identity());
-    stream_part(x, n, acc);
+    stream_chunk(x, n, blockIdx.x, gridDim.x, acc);
     return acc.collapse();
 }
 
@@ -159,7 +108,7 @@ __global__ __launch_bounds__(kBlock) void reduce1d_summaxmin_stream_kernel(
 {
     __shared__ float lds[3][kWaves];
     AccSumMaxMin acc;
-    stream_part(x, n, acc);
+    stream_chunk(x, n, blockIdx.x, gridDim.x, acc);
     const float rs = block_reduce<OpSum>(acc.sum.collapse(), lds[0]);
     const float rx = block_reduce<OpMax>(acc.max.collapse(), lds[1]);
     const float rn = block_reduce<OpMin>(acc.min.collapse(), lds[2]);
@@ -280,8 +229,7 @@ hipError_t launch_reduce1d_summaxmin(const float* x, size_t n, float* out,
 
 unsigned reduce1d_grid(const float* x, size_t n, const DeviceInfo& dev)
 {
-    const uint64_t nvec = (n - head_count(x, n)) / 4;
-    uint64_t g = (nvec + kSweep - 1) / kSweep;
+    uint64_t g = sweep_count(x, n);
     const uint64_t cap = (uint64_t)dev.cus * kStreamWgPerCu;
     if (g > cap)
         g = cap;

@@ -1,7 +1,8 @@
 // rows.hip -- segmented reduction: out[r] = reduce(x[r*ld .. r*ld + n)).
 //
-// Three kernels, picked by the host from (rows, n) alone so that a given
-// problem always runs the same code and gives the same bits:
+// Four kernels, picked by the host from (rows, n) and the CU count alone, so
+// that a given problem on a given device always runs the same code and
+// gives the same bits:
 //
 //  * rows_thread (n <= 64): one thread per row, running the thread-scope
 //    algorithm of the TVM TIRx page "reduction -> sm100_packed" (section
@@ -17,9 +18,12 @@
 //    one multi-wide accumulator per row, a DPP reduction over each lane
 //    segment; the segment's last lane stores.  Each workgroup walks a
 //    contiguous range of rows.  No LDS, no second pass.
-//  * rows_wave: the same with one row per wave and any n, looping over the
-//    row four vectors per lane at a time.
-//  * rows_block: one 256-thread workgroup per row, for few very long rows.
+//  * rows_wave (1024 < n <= 4096, at least 8 rows per CU): one row per
+//    wave, looping over the row four vectors per lane at a time.
+//  * rows_split: rows longer than 4096 elements, or too few rows to give
+//    every CU waves: each row is cut into K contiguous chunks streamed like
+//    the 1-D vector, one workgroup per chunk, and a second kernel folds each
+//    row's K partials in index order (no second kernel when K = 1).
 #include "device.hpp"
 #include "internal.hpp"
 
@@ -27,18 +31,17 @@ namespace red {
 namespace {
 
 constexpr uint64_t kThreadRowMax = 64; // rows this short go one per thread
-constexpr uint64_t kWaveRowMax = 16384;
+#ifndef RED_ROWS_WAVE_MAX
+#define RED_ROWS_WAVE_MAX 4096
+#endif
+// Longest row one wave reduces; longer rows go to the split kernel.
+// (Measured on MI355X, 256 MiB of rows from HBM: 8192-element rows 43.4 us
+// one wave per row, 41.3 us split; 16384-element rows 50.3 vs 43.0 us.)
+constexpr uint64_t kWaveRowMax = RED_ROWS_WAVE_MAX;
 #ifndef RED_ROWS_WG_PER_CU
 #define RED_ROWS_WG_PER_CU 16
 #endif
 constexpr uint64_t kRowsWgPerCu = RED_ROWS_WG_PER_CU;
-
-__device__ __forceinline__ uint32_t head_count(const float* p, uint64_t n)
-{
-    const uint32_t mis = (uint32_t)(((uintptr_t)p >> 2) & 3u);
-    const uint64_t h = (4u - mis) & 3u;
-    return (uint32_t)(h < n ? h : n);
-}
 
 // ---- one thread per row: the page's exact order ---------------------------
 
@@ -265,19 +268,54 @@ __global__ __launch_bounds__(kBlock) void rows_seg_kernel(
     }
 }
 
+// Long rows, or too few rows to fill the GPU one wave per row: row r is
+// cut into K contiguous chunks of whole sweeps, one workgroup per (row,
+// chunk) streaming exactly as the 1-D kernel streams a vector.  With K = 1
+// the workgroup writes out[r] itself (the old value folded first under
+// accum); otherwise it writes partials[r * K + k] and rows_split_finish
+// folds each row's K partials in index order.
 template <class Op>
-__global__ __launch_bounds__(kBlock) void rows_block_kernel(
+__global__ __launch_bounds__(kBlock) void rows_split_kernel(
     const float* __restrict__ x, uint64_t rows, uint64_t n, uint64_t ld,
+    float* __restrict__ out, int accum, uint32_t K,
+    float* __restrict__ partials)
+{
+    __shared__ float lds[kWaves];
+    const uint64_t units = rows * K;
+    for (uint64_t b = blockIdx.x; b < units; b += gridDim.x) {
+        const uint64_t r = b / K;
+        const uint32_t k = (uint32_t)(b % K);
+        Acc<Op> acc(Op::identity());
+        stream_chunk(x + r * ld, n, k, K, acc);
+        const float total = block_reduce<Op>(acc.collapse(), lds);
+        if (threadIdx.x == 0) {
+            if (K == 1)
+                out[r] = accum ? Op::apply(out[r], total) : total;
+            else
+                partials[b] = total;
+        }
+        __syncthreads(); // lds is rewritten by the next unit
+    }
+}
+
+// One workgroup per row: the old value (under accum) first, then the row's
+// K partials in index order, combined by the workgroup tree.
+template <class Op>
+__global__ __launch_bounds__(kBlock) void rows_split_finish_kernel(
+    const float* __restrict__ partials, uint64_t rows, uint32_t K,
     float* __restrict__ out, int accum)
 {
     __shared__ float lds[kWaves];
     for (uint64_t r = blockIdx.x; r < rows; r += gridDim.x) {
-        const float first = (threadIdx.x == 0 && accum) ? out[r] : Op::identity();
-        const float v = row_lane_part<Op, kBlock>(x + r * ld, n, threadIdx.x, first);
+        float v = Op::identity();
+        if (threadIdx.x == 0 && accum)
+            v = out[r];
+        for (uint32_t k = threadIdx.x; k < K; k += kBlock)
+            v = Op::apply(v, partials[r * K + k]);
         const float total = block_reduce<Op>(v, lds);
         if (threadIdx.x == 0)
             out[r] = total;
-        __syncthreads(); // lds is rewritten by the next row
+        __syncthreads();
     }
 }
 
@@ -310,7 +348,7 @@ void launch_seg(const float* x, uint64_t rows, uint64_t n, uint64_t ld,
 template <class Op>
 hipError_t launch_rows_op(const float* x, size_t rows, size_t n, size_t ld,
                           float* out, int accum, const DeviceInfo& dev,
-                          hipStream_t stream)
+                          const Workspace& ws, hipStream_t stream)
 {
     if (n <= kThreadRowMax) {
         const unsigned grid = cap_grid((rows + kBlock - 1) / kBlock);
@@ -332,27 +370,48 @@ hipError_t launch_rows_op(const float* x, size_t rows, size_t n, size_t ld,
             launch_seg<Op, 32, 4, 2>(x, rows, n, ld, out, accum, dev, stream);
         else
             launch_seg<Op, 64, 4, 2>(x, rows, n, ld, out, accum, dev, stream);
-    } else if (n <= kWaveRowMax || rows >= (size_t)dev.cus * kRowsWavePerCu) {
+    } else if (n <= kWaveRowMax && rows >= (size_t)dev.cus * kRowsWavePerCu) {
         const unsigned grid = cap_grid((rows + kWaves - 1) / kWaves);
         rows_wave_kernel<Op><<<grid, kBlock, 0, stream>>>(x, rows, n, ld, out,
                                                           accum);
     } else {
-        rows_block_kernel<Op><<<cap_grid(rows), kBlock, 0, stream>>>(
-            x, rows, n, ld, out, accum);
+        const uint32_t K = rows_chunks(x, rows, n, dev);
+        if (K > 1 && (size_t)rows * K * sizeof(float) > ws.partial_bytes)
+            return hipErrorInvalidValue;
+        float* partials = static_cast<float*>(ws.partials);
+        rows_split_kernel<Op><<<cap_grid(rows * K), kBlock, 0, stream>>>(
+            x, rows, n, ld, out, accum, K, partials);
+        if (K > 1)
+            rows_split_finish_kernel<Op><<<cap_grid(rows), kBlock, 0, stream>>>(
+                partials, rows, K, out, accum);
     }
     return hipGetLastError();
 }
 
 } // namespace
 
+uint32_t rows_chunks(const float* x, size_t rows, size_t n, const DeviceInfo& dev)
+{
+    if (n <= kPairRowMax || (n <= kWaveRowMax && rows >= (size_t)dev.cus * kRowsWavePerCu))
+        return 0; // not the split kernel
+    const uint64_t target = (uint64_t)dev.cus * kStreamWgPerCu;
+    if (rows >= target)
+        return 1;
+    uint64_t K = (target + rows - 1) / rows;
+    const uint64_t sweeps = sweep_count(x, n); // the first row's; others differ by < 1
+    if (K > sweeps)
+        K = sweeps;
+    return (uint32_t)(K < 1 ? 1 : K);
+}
+
 hipError_t launch_rows(OpKind op, const float* x, size_t rows, size_t n,
                        size_t ld, float* out, int accum, const DeviceInfo& dev,
-                       hipStream_t stream)
+                       const Workspace& ws, hipStream_t stream)
 {
     switch (op) {
-    case OpKind::Sum: return launch_rows_op<OpSum>(x, rows, n, ld, out, accum, dev, stream);
-    case OpKind::Max: return launch_rows_op<OpMax>(x, rows, n, ld, out, accum, dev, stream);
-    case OpKind::Min: return launch_rows_op<OpMin>(x, rows, n, ld, out, accum, dev, stream);
+    case OpKind::Sum: return launch_rows_op<OpSum>(x, rows, n, ld, out, accum, dev, ws, stream);
+    case OpKind::Max: return launch_rows_op<OpMax>(x, rows, n, ld, out, accum, dev, ws, stream);
+    case OpKind::Min: return launch_rows_op<OpMin>(x, rows, n, ld, out, accum, dev, ws, stream);
     }
     return hipErrorInvalidValue;
 }

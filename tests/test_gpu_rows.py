@@ -110,6 +110,9 @@ SHAPES = [  # (rows, n, ld, element offset of the base pointer)
     (1000, 300, 300, 3), (31, 511, 511, 2), (4099, 512, 512, 0), (9, 513, 515, 1),
     (70, 700, 701, 0), (5, 1023, 1023, 3), (300, 1024, 1024, 0),
     (300000, 100, 100, 0), (70001, 384, 384, 1),
+    # long rows: split into chunks per row (with and without a second pass)
+    (5, 300000, 300001, 1), (600, 20000, 20000, 0), (100, 5000, 5003, 2),
+    (3000, 2000, 2000, 0), (1, (1 << 22) + 3, (1 << 22) + 3, 0), (37, 65536, 65540, 3),
 ]
 
 
