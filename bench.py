@@ -310,9 +310,9 @@ def wl_rows1000(torch, red, orc, steps):
     o2 = torch.zeros(rows, dtype=torch.float32, device="cuda")
     ob = torch.zeros(C, dtype=torch.bfloat16, device="cuda")
     oh = torch.zeros(C, dtype=torch.float16, device="cuda")
-    calls = [Call("rows_sum", "rows_wave2_kernel<OpSum>", rbytes,
+    calls = [Call("rows_sum", "rows_seg_kernel<OpSum, 64, 4, 2>", rbytes,
                   lambda k: red.plan("sum_rows_f32", xs.next(), o1)),
-             Call("rows_max", "rows_wave2_kernel<OpMax>", rbytes,
+             Call("rows_max", "rows_seg_kernel<OpMax, 64, 4, 2>", rbytes,
                   lambda k: red.plan("max_rows_f32", xs.next(), o2)),
              Call("colprod_bf16", COLRED.format("TraitsBF16, OpMul<float>"), tbytes,
                   lambda k: red.plan("colprod_bf16", bs.next(), ob)),
@@ -358,11 +358,11 @@ def wl_rows32(torch, red, orc, steps):
     o = [torch.zeros(rows, dtype=torch.float32, device="cuda") for _ in range(3)]
     ot = torch.zeros(16, dtype=torch.float32, device="cuda")
     rbytes = 4 * rows * n + 4 * rows
-    calls = [Call("rows_sum", "rows_thread_kernel<OpSum>", rbytes,
+    calls = [Call("rows_sum", "rows_tile_kernel<OpSum>", rbytes,
                   lambda k: red.plan("sum_rows_f32", ad, o[0])),
-             Call("rows_max", "rows_thread_kernel<OpMax>", rbytes,
+             Call("rows_max", "rows_tile_kernel<OpMax>", rbytes,
                   lambda k: red.plan("max_rows_f32", ad, o[1])),
-             Call("rows_min", "rows_thread_kernel<OpMin>", rbytes,
+             Call("rows_min", "rows_tile_kernel<OpMin>", rbytes,
                   lambda k: red.plan("min_rows_f32", ad, o[2])),
              Call("colprod_tile16", COLRED.format("TraitsF32, OpMul<float>"), 16 * 16 * 4 + 64,
                   lambda k: red.plan("colprod_f32", td, ot))]
@@ -373,7 +373,7 @@ def wl_rows32(torch, red, orc, steps):
     return Workload(
         "rows32",
         "4096 rows x 32 fp32, uniform[-1,1), seed 0: row sum, max, min (one "
-        "thread per row); one 16 x 16 fp32 tile column product",
+        "thread per row, rows staged in LDS); one 16 x 16 fp32 tile column product",
         {"rows": rows, "n": n, "calls_per_step": 4, "cold_copies": 1},
         calls, ["rows_sum"], ["rows.hip"] + DEVICE_HEADERS, cpu)
 
