@@ -4,11 +4,11 @@
 // per compute unit); each thread streams its share of the chunk in sweeps
 // of eight non-temporal 16-byte (dwordx4) loads in flight into a per-thread
 // multi-wide accumulator, which collapses along a fixed tree; the wave
-// reduces with DPP and the workgroup through LDS.  (Measured on MI355X: contiguous chunks at two workgroups per CU
-// stream at ~7.1 TB/s for 1 GiB; a grid-stride walk with eight workgroups
-// per CU stayed near 5 TB/s.)
+// reduces with DPP and the workgroup through LDS.  (Measured on MI355X:
+// contiguous chunks at two workgroups per CU stream at ~7.1 TB/s for 1 GiB;
+// a grid-stride walk with eight workgroups per CU stayed near 5 TB/s.)
 //
-// The cross-workgroup step takes one of two forms:
+// The cross-workgroup step takes one of three forms:
 //  * deterministic (default): every workgroup stores its partial; a second,
 //    one-workgroup kernel combines the partials in index order (folding the
 //    old destination first under accum) and writes the scalar.  (Measured
@@ -70,6 +70,35 @@ struct AccSumMaxMin {
     }
 };
 
+// The workgroup sum, max and min of (vs, vx, vn) behind one barrier: each
+// is folded exactly as block_reduce folds it (DPP within the wave, then the
+// waves in order), so the results equal three block_reduce calls bit for
+// bit.  Only thread 0's results are meaningful.
+__device__ __forceinline__ void block_reduce_sum_max_min(float vs, float vx,
+                                                         float vn,
+                                                         float (*lds)[kWaves],
+                                                         float* r)
+{
+    const float ws = wave_reduce<OpSum>(vs);
+    const float wx = wave_reduce<OpMax>(vx);
+    const float wn = wave_reduce<OpMin>(vn);
+    if ((threadIdx.x & (kWave - 1)) == 0) {
+        lds[0][threadIdx.x / kWave] = ws;
+        lds[1][threadIdx.x / kWave] = wx;
+        lds[2][threadIdx.x / kWave] = wn;
+    }
+    __syncthreads();
+    r[0] = lds[0][0];
+    r[1] = lds[1][0];
+    r[2] = lds[2][0];
+#pragma unroll
+    for (int k = 1; k < kWaves; ++k) {
+        r[0] = OpSum::apply(r[0], lds[0][k]);
+        r[1] = OpMax::apply(r[1], lds[1][k]);
+        r[2] = OpMin::apply(r[2], lds[2][k]);
+    }
+}
+
 // First pass: each workgroup writes its partial to partials[blockIdx.x].
 template <class Op>
 __global__ __launch_bounds__(kBlock) void reduce1d_stream_kernel(
@@ -109,13 +138,13 @@ __global__ __launch_bounds__(kBlock) void reduce1d_summaxmin_stream_kernel(
     __shared__ float lds[3][kWaves];
     AccSumMaxMin acc;
     stream_chunk(x, n, blockIdx.x, gridDim.x, acc);
-    const float rs = block_reduce<OpSum>(acc.sum.collapse(), lds[0]);
-    const float rx = block_reduce<OpMax>(acc.max.collapse(), lds[1]);
-    const float rn = block_reduce<OpMin>(acc.min.collapse(), lds[2]);
+    float r[3];
+    block_reduce_sum_max_min(acc.sum.collapse(), acc.max.collapse(),
+                             acc.min.collapse(), lds, r);
     if (threadIdx.x == 0) {
-        partials[blockIdx.x] = rs;
-        partials[gridDim.x + blockIdx.x] = rx;
-        partials[2 * gridDim.x + blockIdx.x] = rn;
+        partials[blockIdx.x] = r[0];
+        partials[gridDim.x + blockIdx.x] = r[1];
+        partials[2 * gridDim.x + blockIdx.x] = r[2];
     }
 }
 
@@ -137,13 +166,12 @@ __global__ __launch_bounds__(kBlock) void reduce1d_summaxmin_finish_kernel(
         vx = OpMax::apply(vx, partials[G + k]);
         vn = OpMin::apply(vn, partials[2 * G + k]);
     }
-    const float ts = block_reduce<OpSum>(vs, lds[0]);
-    const float tx = block_reduce<OpMax>(vx, lds[1]);
-    const float tn = block_reduce<OpMin>(vn, lds[2]);
+    float t[3];
+    block_reduce_sum_max_min(vs, vx, vn, lds, t);
     if (threadIdx.x == 0) {
-        out[0] = ts;
-        out[1] = tx;
-        out[2] = tn;
+        out[0] = t[0];
+        out[1] = t[1];
+        out[2] = t[2];
     }
 }
 

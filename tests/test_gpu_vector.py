@@ -269,3 +269,33 @@ def test_fused_special_values(red, orc):
                  [2.0 ** -149, -(2.0 ** -149), 0.0] * 5):
         x = np.array(vals, np.float32)
         check_fused(red, orc, x, dev(x), False, (0.0, 0.0, 0.0), "special %s" % vals[:3])
+
+
+def test_workspace_allocation_failure(red, vec16m):
+    """A failed workspace allocation is reported as RED_ERR_NOMEM, nothing
+    is enqueued, and the next call on that stream allocates normally.  The
+    failure is forced from the host (RED_TEST_FAIL_ALLOC=1 makes the library
+    skip hipMalloc for a new stream's workspace)."""
+    import os
+    say("workspace allocation failure on a new stream")
+    _, xd = vec16m
+    ref = run(red, "sum", xd)
+    s = torch.cuda.Stream()
+    out = torch.full((1,), 7.0, dtype=torch.float32, device="cuda")
+    torch.cuda.synchronize()
+    os.environ["RED_TEST_FAIL_ALLOC"] = "1"
+    try:
+        with pytest.raises(red.ReduceError) as err:
+            red.sum_f32(xd, out, stream=s)
+        assert err.value.status == red.RED_ERR_NOMEM
+        # The atomic variant needs no workspace and still runs.
+        red.sum_f32_atomic(xd, out, stream=s)
+        s.synchronize()
+        check_sum(host(out)[0], *oracle.get().sum_f32(workloads.vec16m()), "atomic")
+    finally:
+        del os.environ["RED_TEST_FAIL_ALLOC"]
+    out.fill_(7.0)
+    torch.cuda.synchronize()
+    red.sum_f32(xd, out, stream=s)
+    s.synchronize()
+    assert host(out)[0].tobytes() == np.float32(ref).tobytes()
