@@ -142,8 +142,13 @@ int red_min_f32_atomic(const float* x, size_t n, float* out, int accum,
  * Rows of at most 64 elements are reduced one per thread in exactly the
  * single-precision order of the TVM page's "Algorithm" section (8 slots,
  * chunks of 8, leftovers into slot i mod 8, the 8 -> 4 -> 2 -> 1 tree,
- * accum into slot 0 first); longer rows one per wavefront (or one per
- * workgroup for few, very long rows).  Same tolerances as the 1-D calls.
+ * accum into slot 0 first).  Longer rows are shared by 16, 32 or 64 lanes
+ * (up to 1024 elements) or by a wavefront (up to 4096); rows longer still,
+ * or too few rows to occupy the device, are cut into chunks reduced by
+ * separate workgroups whose partials a second kernel folds in index order
+ * (that case uses the stream's workspace).  Every choice depends only on
+ * (rows, n, ld, alignment of x) and the device's compute-unit count, so
+ * the results are deterministic.  Same tolerances as the 1-D calls.
  * ------------------------------------------------------------------- */
 int red_sum_rows_f32(const float* x, size_t rows, size_t n, size_t ld,
                      float* out, int accum, red_stream_t stream);
