@@ -41,6 +41,11 @@ HIPFLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     # Let float atomicAdd lower to the hardware global_atomic_add_f32.
     "-munsafe-fp-atomics",
+    # Preload the first kernel arguments into SGPRs at wave launch (gfx940+
+    # kernarg preload), so a kernel's first loads need not wait for a
+    # kernel-argument fetch.  The code object keeps the compatible prologue
+    # that fetches them itself where the firmware does not preload.
+    "-mllvm", "-amdgpu-kernarg-preload-count=16",
     "-I" + INCLUDE,
 ]
 

@@ -141,12 +141,13 @@ __device__ __forceinline__ uint4 load_stream(const uint4* p)
 // ---------------------------------------------------------------------------
 // Streaming one contiguous vector in chunks.
 //
-// The vector's whole 16-byte vectors are cut into `chunks` contiguous
-// chunks of whole sweeps (kSweep vectors: kStreamUnroll loads in flight per
-// thread); a workgroup streams chunk `chunk` into its threads'
+// The vector's whole 16-byte vectors are cut into contiguous chunks of
+// `per` vectors each (a multiple of the sweep kSweep: kStreamUnroll loads in
+// flight per thread); a workgroup streams chunk `chunk` into its threads'
 // accumulators.  The scalars before the first 16-byte boundary and after
 // the last whole vector go to thread 0 of chunk 0.  The last chunks may be
-// short or empty.
+// short or empty.  The host computes `per` (chunk_vectors below), so the
+// kernel does no 64-bit division before its first load.
 // ---------------------------------------------------------------------------
 #ifndef RED_STREAM_UNROLL
 #define RED_STREAM_UNROLL 8
@@ -168,17 +169,23 @@ __host__ __device__ inline uint64_t sweep_count(const float* x, uint64_t n)
     return ((n - head_count(x, n)) / 4 + kSweep - 1) / kSweep;
 }
 
+// Vectors per chunk when nvec whole vectors are cut into `chunks` chunks:
+// ceil(nvec / chunks) rounded up to whole sweeps.
+__host__ inline uint64_t chunk_vectors(uint64_t nvec, uint64_t chunks)
+{
+    const uint64_t per_chunk = (nvec + chunks - 1) / chunks;
+    return (per_chunk + kSweep - 1) / kSweep * kSweep;
+}
+
 template <class AccT>
 __device__ __forceinline__ void stream_chunk(const float* __restrict__ x,
-                                             uint64_t n, uint64_t chunk,
-                                             uint64_t chunks, AccT& acc)
+                                             uint64_t n, uint64_t per,
+                                             uint64_t chunk, AccT& acc)
 {
     const uint32_t head = head_count(x, n);
     const uint64_t nvec = (n - head) / 4;
     const float4* __restrict__ xv = reinterpret_cast<const float4*>(x + head);
 
-    const uint64_t per_chunk = (nvec + chunks - 1) / chunks;
-    const uint64_t per = (per_chunk + kSweep - 1) / kSweep * kSweep;
     const uint64_t b0 = chunk * per;
     const uint64_t b1 = (b0 + per < nvec) ? b0 + per : nvec;
 
@@ -188,6 +195,10 @@ __device__ __forceinline__ void stream_chunk(const float* __restrict__ x,
 #pragma unroll
         for (int u = 0; u < kStreamUnroll; ++u)
             v[u] = load_stream(xv + i + (uint64_t)u * kBlock);
+        // All loads of the sweep are issued before the first fold (left to
+        // itself the scheduler interleaves max3 / min3 folds with the loads
+        // and waits for the first load before issuing the rest).
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int u = 0; u < kStreamUnroll; u += 2)
             acc.fold2(v[u], v[u + 1]);
@@ -200,6 +211,56 @@ __device__ __forceinline__ void stream_chunk(const float* __restrict__ x,
         for (uint64_t k = head + 4 * nvec; k < n; ++k)
             acc.fold_scalar(x[k]);
     }
+}
+
+// Folding, in index order, the values v[t], v[t + kBlock], v[t + 2 kBlock],
+// ... (t = threadIdx.x, indices below count >= 1) into a starting value,
+// with every load of the first kFinishBatch rounds issued before the first
+// fold, so the fold waits for one memory round trip rather than one per
+// round.  Lanes past the end load v[0] and fold the identity instead, which
+// keeps the loads unconditional (a conditional load would be sunk next to
+// its fold).  The result is the plain sequential fold, bit for bit.
+constexpr int kFinishBatch = 4;
+
+__device__ __forceinline__ void load_strided(const float* __restrict__ v,
+                                             uint64_t count,
+                                             float (&p)[kFinishBatch])
+{
+#pragma unroll
+    for (int b = 0; b < kFinishBatch; ++b) {
+        const uint64_t k = threadIdx.x + (uint64_t)b * kBlock;
+        p[b] = v[k < count ? k : 0];
+    }
+}
+
+template <class Op>
+__device__ __forceinline__ float fold_loaded(float first,
+                                             const float (&p)[kFinishBatch],
+                                             const float* __restrict__ v,
+                                             uint64_t count)
+{
+    float r = first;
+#pragma unroll
+    for (int b = 0; b < kFinishBatch; ++b) {
+        const uint64_t k = threadIdx.x + (uint64_t)b * kBlock;
+        r = Op::apply(r, k < count ? p[b] : Op::identity());
+    }
+    for (uint64_t k = threadIdx.x + (uint64_t)kFinishBatch * kBlock; k < count; k += kBlock)
+        r = Op::apply(r, v[k]);
+    return r;
+}
+
+template <class Op>
+__device__ __forceinline__ float fold_strided(float first,
+                                              const float* __restrict__ v,
+                                              uint64_t count)
+{
+    float p[kFinishBatch];
+    load_strided(v, count, p);
+    // Keep the instruction scheduler from moving any use (and its wait)
+    // above the last load.
+    __builtin_amdgcn_sched_barrier(0);
+    return fold_loaded<Op>(first, p, v, count);
 }
 
 // Workgroup reduction over the kWaves waves of a library workgroup: every

@@ -32,10 +32,10 @@ namespace {
 
 template <class Op>
 __device__ __forceinline__ float thread_part(const float* __restrict__ x,
-                                             uint64_t n)
+                                             uint64_t n, uint64_t per)
 {
     Acc<Op> acc(Op::identity());
-    stream_chunk(x, n, blockIdx.x, gridDim.x, acc);
+    stream_chunk(x, n, per, blockIdx.x, acc);
     return acc.collapse();
 }
 
@@ -100,31 +100,32 @@ __device__ __forceinline__ void block_reduce_sum_max_min(float vs, float vx,
 }
 
 // First pass: each workgroup writes its partial to partials[blockIdx.x].
+// `per` is the chunk length in 16-byte vectors (chunk_vectors).
 template <class Op>
 __global__ __launch_bounds__(kBlock) void reduce1d_stream_kernel(
-    const float* __restrict__ x, uint64_t n, float* __restrict__ partials)
+    const float* __restrict__ x, uint64_t n, uint64_t per,
+    float* __restrict__ partials)
 {
     __shared__ float lds[kWaves];
-    const float r = block_reduce<Op>(thread_part<Op>(x, n), lds);
+    const float r = block_reduce<Op>(thread_part<Op>(x, n, per), lds);
     if (threadIdx.x == 0)
         partials[blockIdx.x] = r;
 }
 
 // Second pass, one workgroup: combine the G partials in index order (each
 // thread folds partials t, t + 256, ..., then the workgroup tree), with the
-// old destination in the first slot under accum.  The kernel boundary makes
-// the first pass's stores visible; no atomics are involved.
+// old destination in the first slot under accum.  The old value and the
+// partials are all requested before the first fold.  The kernel boundary
+// makes the first pass's stores visible; no atomics are involved.
 template <class Op>
 __global__ __launch_bounds__(kBlock) void reduce1d_finish_kernel(
     const float* __restrict__ partials, unsigned G, float* __restrict__ out,
     int accum)
 {
     __shared__ float lds[kWaves];
-    float v = Op::identity();
-    if (threadIdx.x == 0 && accum)
-        v = *out;
-    for (unsigned k = threadIdx.x; k < G; k += kBlock)
-        v = Op::apply(v, partials[k]);
+    const float o = *out; // read unconditionally, so it is requested first
+    const float old = (threadIdx.x == 0 && accum) ? o : Op::identity();
+    const float v = fold_strided<Op>(old, partials, G);
     const float total = block_reduce<Op>(v, lds);
     if (threadIdx.x == 0)
         *out = total;
@@ -133,11 +134,12 @@ __global__ __launch_bounds__(kBlock) void reduce1d_finish_kernel(
 // Fused first pass: partials[b], partials[G + b], partials[2G + b] receive
 // workgroup b's sum, max and min.
 __global__ __launch_bounds__(kBlock) void reduce1d_summaxmin_stream_kernel(
-    const float* __restrict__ x, uint64_t n, float* __restrict__ partials)
+    const float* __restrict__ x, uint64_t n, uint64_t per,
+    float* __restrict__ partials)
 {
     __shared__ float lds[3][kWaves];
     AccSumMaxMin acc;
-    stream_chunk(x, n, blockIdx.x, gridDim.x, acc);
+    stream_chunk(x, n, per, blockIdx.x, acc);
     float r[3];
     block_reduce_sum_max_min(acc.sum.collapse(), acc.max.collapse(),
                              acc.min.collapse(), lds, r);
@@ -155,17 +157,16 @@ __global__ __launch_bounds__(kBlock) void reduce1d_summaxmin_finish_kernel(
     int accum)
 {
     __shared__ float lds[3][kWaves];
-    float vs = OpSum::identity(), vx = OpMax::identity(), vn = OpMin::identity();
-    if (threadIdx.x == 0 && accum) {
-        vs = out[0];
-        vx = out[1];
-        vn = out[2];
-    }
-    for (unsigned k = threadIdx.x; k < G; k += kBlock) {
-        vs = OpSum::apply(vs, partials[k]);
-        vx = OpMax::apply(vx, partials[G + k]);
-        vn = OpMin::apply(vn, partials[2 * G + k]);
-    }
+    const bool first = threadIdx.x == 0 && accum;
+    const float os = out[0], ox = out[1], on = out[2]; // requested first
+    float ps[kFinishBatch], px[kFinishBatch], pn[kFinishBatch];
+    load_strided(partials, G, ps);
+    load_strided(partials + G, G, px);
+    load_strided(partials + 2 * G, G, pn);
+    __builtin_amdgcn_sched_barrier(0); // every load above is issued before any fold
+    const float vs = fold_loaded<OpSum>(first ? os : OpSum::identity(), ps, partials, G);
+    const float vx = fold_loaded<OpMax>(first ? ox : OpMax::identity(), px, partials + G, G);
+    const float vn = fold_loaded<OpMin>(first ? on : OpMin::identity(), pn, partials + 2 * G, G);
     float t[3];
     block_reduce_sum_max_min(vs, vx, vn, lds, t);
     if (threadIdx.x == 0) {
@@ -196,10 +197,10 @@ __device__ void atomic_fold_cas(float* out, float r)
 
 template <class Op>
 __global__ __launch_bounds__(kBlock) void reduce1d_atomic_kernel(
-    const float* __restrict__ x, uint64_t n, float* __restrict__ out)
+    const float* __restrict__ x, uint64_t n, uint64_t per, float* __restrict__ out)
 {
     __shared__ float lds[kWaves];
-    const float r = block_reduce<Op>(thread_part<Op>(x, n), lds);
+    const float r = block_reduce<Op>(thread_part<Op>(x, n, per), lds);
     if (threadIdx.x == 0) {
         if constexpr (__is_same(Op, OpSum))
             unsafeAtomicAdd(out, r); // hardware global_atomic_add_f32
@@ -221,7 +222,8 @@ hipError_t launch_det(const float* x, size_t n, float* out, int accum,
                       unsigned grid, const Workspace& ws, hipStream_t stream)
 {
     float* partials = static_cast<float*>(ws.partials);
-    reduce1d_stream_kernel<Op><<<grid, kBlock, 0, stream>>>(x, n, partials);
+    const uint64_t per = chunk_vectors((n - head_count(x, n)) / 4, grid);
+    reduce1d_stream_kernel<Op><<<grid, kBlock, 0, stream>>>(x, n, per, partials);
     reduce1d_finish_kernel<Op><<<1, kBlock, 0, stream>>>(partials, grid, out, accum);
     return hipGetLastError();
 }
@@ -236,7 +238,8 @@ hipError_t launch_atomic(const float* x, size_t n, float* out, int accum,
         fill_u32_kernel<<<1, 64, 0, stream>>>(
             reinterpret_cast<unsigned*>(out), 1, ident);
     }
-    reduce1d_atomic_kernel<Op><<<grid, kBlock, 0, stream>>>(x, n, out);
+    const uint64_t per = chunk_vectors((n - head_count(x, n)) / 4, grid);
+    reduce1d_atomic_kernel<Op><<<grid, kBlock, 0, stream>>>(x, n, per, out);
     return hipGetLastError();
 }
 
@@ -250,7 +253,8 @@ hipError_t launch_reduce1d_summaxmin(const float* x, size_t n, float* out,
     if ((size_t)grid * 3 * sizeof(float) > ws.partial_bytes)
         return hipErrorInvalidValue;
     float* partials = static_cast<float*>(ws.partials);
-    reduce1d_summaxmin_stream_kernel<<<grid, kBlock, 0, stream>>>(x, n, partials);
+    const uint64_t per = chunk_vectors((n - head_count(x, n)) / 4, grid);
+    reduce1d_summaxmin_stream_kernel<<<grid, kBlock, 0, stream>>>(x, n, per, partials);
     reduce1d_summaxmin_finish_kernel<<<1, kBlock, 0, stream>>>(partials, grid, out, accum);
     return hipGetLastError();
 }

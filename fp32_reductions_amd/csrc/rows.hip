@@ -167,12 +167,15 @@ __global__ __launch_bounds__(kTileThreads) void rows_tile_kernel(
             const float4* __restrict__ src = reinterpret_cast<const float4*>(x + r0 * n);
             const uint32_t nv = total / 4;
             for (uint32_t f0 = 0; f0 < nv; f0 += kTileBatch * kTileThreads) {
+                // Unconditional loads (past the end: vector 0 again, not
+                // stored) so that the whole batch is in flight at once.
                 float4 v[kTileBatch];
 #pragma unroll
                 for (int b = 0; b < kTileBatch; ++b) {
                     const uint32_t f = f0 + b * kTileThreads + t;
-                    v[b] = f < nv ? load_stream(src + f) : make_float4(0.f, 0.f, 0.f, 0.f);
+                    v[b] = load_stream(src + (f < nv ? f : 0));
                 }
+                __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                 for (int b = 0; b < kTileBatch; ++b) {
                     const uint32_t f = f0 + b * kTileThreads + t;
@@ -202,9 +205,11 @@ __global__ __launch_bounds__(kTileThreads) void rows_tile_kernel(
 #pragma unroll
                 for (int b = 0; b < 2 * kTileBatch; ++b) {
                     const uint32_t e = e0 + b * kTileThreads + t;
-                    const uint32_t row = (uint32_t)(((uint64_t)e * inv_n) >> 32);
-                    v[b] = e < total ? x[(r0 + row) * ld + (e - row * n)] : 0.0f;
+                    const uint32_t ec = e < total ? e : 0; // past the end: element 0 again
+                    const uint32_t row = (uint32_t)(((uint64_t)ec * inv_n) >> 32);
+                    v[b] = x[(r0 + row) * ld + (ec - row * n)];
                 }
+                __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                 for (int b = 0; b < 2 * kTileBatch; ++b) {
                     const uint32_t e = e0 + b * kTileThreads + t;
@@ -246,12 +251,20 @@ __device__ __forceinline__ float row_lane_part(const float* __restrict__ p,
     const float4* __restrict__ pv = reinterpret_cast<const float4*>(p + head);
     Acc<Op> acc(first);
     for (uint64_t base = lane; base < nvec; base += (uint64_t)LANES * kRowUnroll) {
+        // Every lane loads kRowUnroll vectors (past the end it reloads
+        // vector `base`, then folds the identity instead), so all loads are
+        // issued before the first fold.
         float4 v[kRowUnroll];
 #pragma unroll
         for (int u = 0; u < kRowUnroll; ++u) {
             const uint64_t idx = base + (uint64_t)u * LANES;
-            v[u] = idx < nvec ? load_stream(pv + idx) : identity4<Op>();
+            v[u] = load_stream(pv + (idx < nvec ? idx : base));
         }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int u = 0; u < kRowUnroll; ++u)
+            if (base + (uint64_t)u * LANES >= nvec)
+                v[u] = identity4<Op>();
 #pragma unroll
         for (int u = 0; u < kRowUnroll; u += 2)
             acc.fold2(v[u], v[u + 1]);
@@ -373,7 +386,7 @@ __global__ __launch_bounds__(kBlock) void rows_seg_kernel(
 template <class Op>
 __global__ __launch_bounds__(kBlock) void rows_split_kernel(
     const float* __restrict__ x, uint64_t rows, uint64_t n, uint64_t ld,
-    float* __restrict__ out, int accum, uint32_t K,
+    float* __restrict__ out, int accum, uint32_t K, uint64_t per,
     float* __restrict__ partials)
 {
     __shared__ float lds[kWaves];
@@ -382,7 +395,7 @@ __global__ __launch_bounds__(kBlock) void rows_split_kernel(
         const uint64_t r = b / K;
         const uint32_t k = (uint32_t)(b % K);
         Acc<Op> acc(Op::identity());
-        stream_chunk(x + r * ld, n, k, K, acc);
+        stream_chunk(x + r * ld, n, per, k, acc);
         const float total = block_reduce<Op>(acc.collapse(), lds);
         if (threadIdx.x == 0) {
             if (K == 1)
@@ -403,11 +416,9 @@ __global__ __launch_bounds__(kBlock) void rows_split_finish_kernel(
 {
     __shared__ float lds[kWaves];
     for (uint64_t r = blockIdx.x; r < rows; r += gridDim.x) {
-        float v = Op::identity();
-        if (threadIdx.x == 0 && accum)
-            v = out[r];
-        for (uint32_t k = threadIdx.x; k < K; k += kBlock)
-            v = Op::apply(v, partials[r * K + k]);
+        const float o = out[r]; // read unconditionally, so it is requested first
+        const float v = fold_strided<Op>((threadIdx.x == 0 && accum) ? o : Op::identity(),
+                                         partials + r * K, K);
         const float total = block_reduce<Op>(v, lds);
         if (threadIdx.x == 0)
             out[r] = total;
@@ -487,8 +498,11 @@ hipError_t launch_rows_op(const float* x, size_t rows, size_t n, size_t ld,
         if (K > 1 && (size_t)rows * K * sizeof(float) > ws.partial_bytes)
             return hipErrorInvalidValue;
         float* partials = static_cast<float*>(ws.partials);
+        // Chunk length from the longest whole-vector count a row can have
+        // (rows that start off a 16-byte boundary have at most as many).
+        const uint64_t per = chunk_vectors(n / 4, K);
         rows_split_kernel<Op><<<cap_grid(rows * K), kBlock, 0, stream>>>(
-            x, rows, n, ld, out, accum, K, partials);
+            x, rows, n, ld, out, accum, K, per, partials);
         if (K > 1)
             rows_split_finish_kernel<Op><<<cap_grid(rows), kBlock, 0, stream>>>(
                 partials, rows, K, out, accum);
