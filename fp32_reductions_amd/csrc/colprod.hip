@@ -224,6 +224,26 @@ __global__ __launch_bounds__(kBlock) void colred_kernel(
                     acc[k] = Op::apply(acc[k], a[k]);
             }
         } else {
+            // Element-wise loads (rows not 16-byte aligned, or the ragged
+            // last column block): kRowsInFlight rows of V elements are all
+            // requested before any is folded.  Columns past C reload
+            // column j0 and are not folded.
+            for (; r + (uint64_t)kGroups * (kRowsInFlight - 1) < r1;
+                 r += (uint64_t)kGroups * kRowsInFlight) {
+                T v[kRowsInFlight][V];
+#pragma unroll
+                for (int u = 0; u < kRowsInFlight; ++u)
+#pragma unroll
+                    for (int k = 0; k < V; ++k)
+                        v[u][k] = col[(r + (uint64_t)u * kGroups) * ld + (j0 + k < C ? k : 0)];
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int u = 0; u < kRowsInFlight; ++u)
+#pragma unroll
+                    for (int k = 0; k < V; ++k)
+                        if (j0 + k < C)
+                            acc[k] = Op::apply(acc[k], Tr::widen(v[u][k]));
+            }
             for (; r < r1; r += kGroups) {
 #pragma unroll
                 for (int k = 0; k < V; ++k)
