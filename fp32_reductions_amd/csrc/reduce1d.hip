@@ -12,7 +12,7 @@
 //  * deterministic (default): every workgroup stores its partial; a second,
 //    one-workgroup kernel combines the partials in index order (folding the
 //    old destination first under accum) and writes the scalar.  (Measured
-//    on MI355X for 64 MiB: 13.5 us per call, against 15-16 us for a single
+//    on MI355X for 64 MiB: 13.1 us per call, against 15-16 us for a single
 //    kernel whose last-arriving workgroup finishes behind atomic counters.)
 //  * fused: sum, max and min of the same vector from one read of it; each
 //    result is bit-identical to the single-operation call's;
