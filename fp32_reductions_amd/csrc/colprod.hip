@@ -187,7 +187,7 @@ __global__ __launch_bounds__(kBlock) void colred_kernel(
     const uint64_t cb = blockIdx.x;
     const uint32_t S = gridDim.y;
     const uint64_t s = blockIdx.y;
-    const uint64_t j0 = cb * kCols + (uint64_t)q * V;
+    const uint64_t jb = cb * kCols; // first column of the block
     const uint64_t r0 = s * rows_per_split;
     const uint64_t r1 = (r0 + rows_per_split < R) ? r0 + rows_per_split : R;
 
@@ -196,67 +196,79 @@ __global__ __launch_bounds__(kBlock) void colred_kernel(
     for (int k = 0; k < V; ++k)
         acc[k] = Op::identity();
 
-    if (j0 < C) {
-        const T* __restrict__ col = src + j0;
-        uint64_t r = r0 + g;
-        if (VEC && j0 + V <= C) {
-            for (; r + (uint64_t)kGroups * (kRowsInFlight - 1) < r1;
-                 r += (uint64_t)kGroups * kRowsInFlight) {
-                uint4 v[kRowsInFlight];
+    uint64_t r = r0 + g;
+    if (VEC && jb + kCols <= C) {
+        // Lane q owns columns jb + qV .. jb + qV + V - 1: one 16-byte vector
+        // per row.
+        const T* __restrict__ col = src + jb + (uint64_t)q * V;
+        for (; r + (uint64_t)kGroups * (kRowsInFlight - 1) < r1;
+             r += (uint64_t)kGroups * kRowsInFlight) {
+            uint4 v[kRowsInFlight];
 #pragma unroll
-                for (int u = 0; u < kRowsInFlight; ++u)
-                    v[u] = load_stream(reinterpret_cast<const uint4*>(
-                        col + (r + (uint64_t)u * kGroups) * ld));
+            for (int u = 0; u < kRowsInFlight; ++u)
+                v[u] = load_stream(reinterpret_cast<const uint4*>(
+                    col + (r + (uint64_t)u * kGroups) * ld));
 #pragma unroll
-                for (int u = 0; u < kRowsInFlight; ++u) {
-                    A a[V];
-                    Tr::unpack(v[u], a);
-#pragma unroll
-                    for (int k = 0; k < V; ++k)
-                        acc[k] = Op::apply(acc[k], a[k]);
-                }
-            }
-            for (; r < r1; r += kGroups) {
+            for (int u = 0; u < kRowsInFlight; ++u) {
                 A a[V];
-                Tr::unpack(load_stream(reinterpret_cast<const uint4*>(col + r * ld)), a);
+                Tr::unpack(v[u], a);
 #pragma unroll
                 for (int k = 0; k < V; ++k)
                     acc[k] = Op::apply(acc[k], a[k]);
             }
-        } else {
-            // Element-wise loads (rows not 16-byte aligned, or the ragged
-            // last column block): kRowsInFlight rows of V elements are all
-            // requested before any is folded.  Columns past C reload
-            // column j0 and are not folded.
-            for (; r + (uint64_t)kGroups * (kRowsInFlight - 1) < r1;
-                 r += (uint64_t)kGroups * kRowsInFlight) {
-                T v[kRowsInFlight][V];
+        }
+        for (; r < r1; r += kGroups) {
+            A a[V];
+            Tr::unpack(load_stream(reinterpret_cast<const uint4*>(col + r * ld)), a);
 #pragma unroll
-                for (int u = 0; u < kRowsInFlight; ++u)
+            for (int k = 0; k < V; ++k)
+                acc[k] = Op::apply(acc[k], a[k]);
+        }
 #pragma unroll
-                    for (int k = 0; k < V; ++k)
-                        v[u][k] = col[(r + (uint64_t)u * kGroups) * ld + (j0 + k < C ? k : 0)];
-                __builtin_amdgcn_sched_barrier(0);
+        for (int k = 0; k < V; ++k)
+            lds[g][q * V + k] = acc[k];
+    } else {
+        // Rows not 16-byte aligned, or the ragged last column block:
+        // element loads, lane q owning columns jb + q + 16k, so that each
+        // load instruction of a row group reads 16 consecutive elements.
+        // kRowsInFlight rows are requested before any is folded; columns
+        // at or past C reload column jb (always valid) and are not folded.
+        const T* __restrict__ blk = src + jb;
+        uint32_t off[V];
+        bool ok[V];
 #pragma unroll
-                for (int u = 0; u < kRowsInFlight; ++u)
+        for (int k = 0; k < V; ++k) {
+            const uint32_t c = q + (uint32_t)kLanesPerRow * k;
+            ok[k] = jb + c < C;
+            off[k] = ok[k] ? c : 0u;
+        }
+        for (; r + (uint64_t)kGroups * (kRowsInFlight - 1) < r1;
+             r += (uint64_t)kGroups * kRowsInFlight) {
+            T v[kRowsInFlight][V];
 #pragma unroll
-                    for (int k = 0; k < V; ++k)
-                        if (j0 + k < C)
-                            acc[k] = Op::apply(acc[k], Tr::widen(v[u][k]));
-            }
-            for (; r < r1; r += kGroups) {
+            for (int u = 0; u < kRowsInFlight; ++u)
 #pragma unroll
                 for (int k = 0; k < V; ++k)
-                    if (j0 + k < C)
-                        acc[k] = Op::apply(acc[k], Tr::widen(col[r * ld + k]));
-            }
-        }
-    }
-
-    // Combine the row groups' partial rows in row-group order.
+                    v[u][k] = blk[(r + (uint64_t)u * kGroups) * ld + off[k]];
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int k = 0; k < V; ++k)
-        lds[g][q * V + k] = acc[k];
+            for (int u = 0; u < kRowsInFlight; ++u)
+#pragma unroll
+                for (int k = 0; k < V; ++k)
+                    if (ok[k])
+                        acc[k] = Op::apply(acc[k], Tr::widen(v[u][k]));
+        }
+        for (; r < r1; r += kGroups) {
+#pragma unroll
+            for (int k = 0; k < V; ++k)
+                if (ok[k])
+                    acc[k] = Op::apply(acc[k], Tr::widen(blk[r * ld + off[k]]));
+        }
+#pragma unroll
+        for (int k = 0; k < V; ++k)
+            lds[g][q + kLanesPerRow * k] = acc[k];
+    }
+    // Combine the row groups' partial rows in row-group order.
     __syncthreads();
 
     if (threadIdx.x < (uint32_t)kCols) {
