@@ -100,16 +100,23 @@ __device__ __forceinline__ void block_reduce_sum_max_min(float vs, float vx,
 }
 
 // First pass: each workgroup writes its partial to partials[blockIdx.x].
-// `per` is the chunk length in 16-byte vectors (chunk_vectors).
+// `per` is the chunk length in 16-byte vectors (chunk_vectors).  A grid of
+// one workgroup (short vectors) is the whole call: it writes *out itself,
+// with the old value folded first under accum, exactly as the finish
+// kernel would, and no second kernel is launched.
 template <class Op>
 __global__ __launch_bounds__(kBlock) void reduce1d_stream_kernel(
     const float* __restrict__ x, uint64_t n, uint64_t per,
-    float* __restrict__ partials)
+    float* __restrict__ partials, float* __restrict__ out, int accum)
 {
     __shared__ float lds[kWaves];
     const float r = block_reduce<Op>(thread_part<Op>(x, n, per), lds);
-    if (threadIdx.x == 0)
-        partials[blockIdx.x] = r;
+    if (threadIdx.x == 0) {
+        if (gridDim.x == 1)
+            *out = accum ? Op::apply(*out, r) : r;
+        else
+            partials[blockIdx.x] = r;
+    }
 }
 
 // Second pass, one workgroup: combine the G partials in index order (each
@@ -135,7 +142,7 @@ __global__ __launch_bounds__(kBlock) void reduce1d_finish_kernel(
 // workgroup b's sum, max and min.
 __global__ __launch_bounds__(kBlock) void reduce1d_summaxmin_stream_kernel(
     const float* __restrict__ x, uint64_t n, uint64_t per,
-    float* __restrict__ partials)
+    float* __restrict__ partials, float* __restrict__ out, int accum)
 {
     __shared__ float lds[3][kWaves];
     AccSumMaxMin acc;
@@ -144,9 +151,15 @@ __global__ __launch_bounds__(kBlock) void reduce1d_summaxmin_stream_kernel(
     block_reduce_sum_max_min(acc.sum.collapse(), acc.max.collapse(),
                              acc.min.collapse(), lds, r);
     if (threadIdx.x == 0) {
-        partials[blockIdx.x] = r[0];
-        partials[gridDim.x + blockIdx.x] = r[1];
-        partials[2 * gridDim.x + blockIdx.x] = r[2];
+        if (gridDim.x == 1) { // the whole call, as for the single operations
+            out[0] = accum ? OpSum::apply(out[0], r[0]) : r[0];
+            out[1] = accum ? OpMax::apply(out[1], r[1]) : r[1];
+            out[2] = accum ? OpMin::apply(out[2], r[2]) : r[2];
+        } else {
+            partials[blockIdx.x] = r[0];
+            partials[gridDim.x + blockIdx.x] = r[1];
+            partials[2 * gridDim.x + blockIdx.x] = r[2];
+        }
     }
 }
 
@@ -223,8 +236,9 @@ hipError_t launch_det(const float* x, size_t n, float* out, int accum,
 {
     float* partials = static_cast<float*>(ws.partials);
     const uint64_t per = chunk_vectors((n - head_count(x, n)) / 4, grid);
-    reduce1d_stream_kernel<Op><<<grid, kBlock, 0, stream>>>(x, n, per, partials);
-    reduce1d_finish_kernel<Op><<<1, kBlock, 0, stream>>>(partials, grid, out, accum);
+    reduce1d_stream_kernel<Op><<<grid, kBlock, 0, stream>>>(x, n, per, partials, out, accum);
+    if (grid > 1)
+        reduce1d_finish_kernel<Op><<<1, kBlock, 0, stream>>>(partials, grid, out, accum);
     return hipGetLastError();
 }
 
@@ -254,8 +268,9 @@ hipError_t launch_reduce1d_summaxmin(const float* x, size_t n, float* out,
         return hipErrorInvalidValue;
     float* partials = static_cast<float*>(ws.partials);
     const uint64_t per = chunk_vectors((n - head_count(x, n)) / 4, grid);
-    reduce1d_summaxmin_stream_kernel<<<grid, kBlock, 0, stream>>>(x, n, per, partials);
-    reduce1d_summaxmin_finish_kernel<<<1, kBlock, 0, stream>>>(partials, grid, out, accum);
+    reduce1d_summaxmin_stream_kernel<<<grid, kBlock, 0, stream>>>(x, n, per, partials, out, accum);
+    if (grid > 1)
+        reduce1d_summaxmin_finish_kernel<<<1, kBlock, 0, stream>>>(partials, grid, out, accum);
     return hipGetLastError();
 }
 
