@@ -25,7 +25,7 @@
  *            (early return for zero valid rows or columns; supported element
  *            types half, float, bfloat16, int16, uint16, int32, uint32).
  *
- * Readings where the pages are silent (each is restated in the design doc):
+ * Readings where the pages are silent:
  *   - n == 0 (1-D and rows) is treated like TCOLPROD's empty tile: nothing
  *     is written, not even under accum.
  *   - max / min follow IEEE-754-2008 maxNum / minNum: a NaN operand is
