@@ -1,12 +1,10 @@
 // reduce1d.hip -- 1-D fp32 vector -> scalar (sum / max / min, accum).
 //
-// The vector is cut into one contiguous chunk per workgroup (two workgroups
-// per compute unit); each thread streams its share of the chunk in sweeps
-// of eight non-temporal 16-byte (dwordx4) loads in flight into a per-thread
+// Two workgroups per compute unit share the vector's 32 KiB sweeps in
+// grid-stride order; each thread streams its share with eight
+// non-temporal 16-byte (dwordx4) loads in flight into a per-thread
 // multi-wide accumulator, which collapses along a fixed tree; the wave
-// reduces with DPP and the workgroup through LDS.  (Measured on MI355X:
-// contiguous chunks at two workgroups per CU stream at ~7.1 TB/s for 1 GiB;
-// a grid-stride walk with eight workgroups per CU stayed near 5 TB/s.)
+// reduces with DPP and the workgroup through LDS.
 //
 // The cross-workgroup step takes one of three forms:
 //  * deterministic (default): every workgroup stores its partial; a second,
@@ -32,10 +30,10 @@ namespace {
 
 template <class Op>
 __device__ __forceinline__ float thread_part(const float* __restrict__ x,
-                                             uint64_t n, uint64_t per)
+                                             uint64_t n)
 {
     Acc<Op> acc(Op::identity());
-    stream_chunk(x, n, per, blockIdx.x, acc);
+    stream_chunk(x, n, blockIdx.x, gridDim.x, acc);
     return acc.collapse();
 }
 
@@ -100,17 +98,17 @@ __device__ __forceinline__ void block_reduce_sum_max_min(float vs, float vx,
 }
 
 // First pass: each workgroup writes its partial to partials[blockIdx.x].
-// `per` is the chunk length in 16-byte vectors (chunk_vectors).  A grid of
+// A grid of
 // one workgroup (short vectors) is the whole call: it writes *out itself,
 // with the old value folded first under accum, exactly as the finish
 // kernel would, and no second kernel is launched.
 template <class Op>
 __global__ __launch_bounds__(kBlock) void reduce1d_stream_kernel(
-    const float* __restrict__ x, uint64_t n, uint64_t per,
-    float* __restrict__ partials, float* __restrict__ out, int accum)
+    const float* __restrict__ x, uint64_t n, float* __restrict__ partials,
+    float* __restrict__ out, int accum)
 {
     __shared__ float lds[kWaves];
-    const float r = block_reduce<Op>(thread_part<Op>(x, n, per), lds);
+    const float r = block_reduce<Op>(thread_part<Op>(x, n), lds);
     if (threadIdx.x == 0) {
         if (gridDim.x == 1)
             *out = accum ? Op::apply(*out, r) : r;
@@ -141,12 +139,12 @@ __global__ __launch_bounds__(kBlock) void reduce1d_finish_kernel(
 // Fused first pass: partials[b], partials[G + b], partials[2G + b] receive
 // workgroup b's sum, max and min.
 __global__ __launch_bounds__(kBlock) void reduce1d_summaxmin_stream_kernel(
-    const float* __restrict__ x, uint64_t n, uint64_t per,
-    float* __restrict__ partials, float* __restrict__ out, int accum)
+    const float* __restrict__ x, uint64_t n, float* __restrict__ partials,
+    float* __restrict__ out, int accum)
 {
     __shared__ float lds[3][kWaves];
     AccSumMaxMin acc;
-    stream_chunk(x, n, per, blockIdx.x, acc);
+    stream_chunk(x, n, blockIdx.x, gridDim.x, acc);
     float r[3];
     block_reduce_sum_max_min(acc.sum.collapse(), acc.max.collapse(),
                              acc.min.collapse(), lds, r);
@@ -210,10 +208,10 @@ __device__ void atomic_fold_cas(float* out, float r)
 
 template <class Op>
 __global__ __launch_bounds__(kBlock) void reduce1d_atomic_kernel(
-    const float* __restrict__ x, uint64_t n, uint64_t per, float* __restrict__ out)
+    const float* __restrict__ x, uint64_t n, float* __restrict__ out)
 {
     __shared__ float lds[kWaves];
-    const float r = block_reduce<Op>(thread_part<Op>(x, n, per), lds);
+    const float r = block_reduce<Op>(thread_part<Op>(x, n), lds);
     if (threadIdx.x == 0) {
         if constexpr (__is_same(Op, OpSum))
             unsafeAtomicAdd(out, r); // hardware global_atomic_add_f32
@@ -235,8 +233,7 @@ hipError_t launch_det(const float* x, size_t n, float* out, int accum,
                       unsigned grid, const Workspace& ws, hipStream_t stream)
 {
     float* partials = static_cast<float*>(ws.partials);
-    const uint64_t per = chunk_vectors((n - head_count(x, n)) / 4, grid);
-    reduce1d_stream_kernel<Op><<<grid, kBlock, 0, stream>>>(x, n, per, partials, out, accum);
+    reduce1d_stream_kernel<Op><<<grid, kBlock, 0, stream>>>(x, n, partials, out, accum);
     if (grid > 1)
         reduce1d_finish_kernel<Op><<<1, kBlock, 0, stream>>>(partials, grid, out, accum);
     return hipGetLastError();
@@ -252,8 +249,7 @@ hipError_t launch_atomic(const float* x, size_t n, float* out, int accum,
         fill_u32_kernel<<<1, 64, 0, stream>>>(
             reinterpret_cast<unsigned*>(out), 1, ident);
     }
-    const uint64_t per = chunk_vectors((n - head_count(x, n)) / 4, grid);
-    reduce1d_atomic_kernel<Op><<<grid, kBlock, 0, stream>>>(x, n, per, out);
+    reduce1d_atomic_kernel<Op><<<grid, kBlock, 0, stream>>>(x, n, out);
     return hipGetLastError();
 }
 
@@ -267,8 +263,7 @@ hipError_t launch_reduce1d_summaxmin(const float* x, size_t n, float* out,
     if ((size_t)grid * 3 * sizeof(float) > ws.partial_bytes)
         return hipErrorInvalidValue;
     float* partials = static_cast<float*>(ws.partials);
-    const uint64_t per = chunk_vectors((n - head_count(x, n)) / 4, grid);
-    reduce1d_summaxmin_stream_kernel<<<grid, kBlock, 0, stream>>>(x, n, per, partials, out, accum);
+    reduce1d_summaxmin_stream_kernel<<<grid, kBlock, 0, stream>>>(x, n, partials, out, accum);
     if (grid > 1)
         reduce1d_summaxmin_finish_kernel<<<1, kBlock, 0, stream>>>(partials, grid, out, accum);
     return hipGetLastError();

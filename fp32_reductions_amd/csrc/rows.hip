@@ -23,9 +23,9 @@
 //  * rows_wave (1024 < n <= 4096, at least 8 rows per CU): one row per
 //    wave, looping over the row four vectors per lane at a time.
 //  * rows_split: rows longer than 4096 elements, or too few rows to give
-//    every CU waves: each row is cut into K contiguous chunks streamed like
-//    the 1-D vector, one workgroup per chunk, and a second kernel folds each
-//    row's K partials in index order (no second kernel when K = 1).
+//    every CU waves: K workgroups share each row, streaming it like the 1-D
+//    vector, and a second kernel folds each row's K partials in index order
+//    (no second kernel when K = 1).
 #include "device.hpp"
 #include "internal.hpp"
 
@@ -377,16 +377,17 @@ __global__ __launch_bounds__(kBlock) void rows_seg_kernel(
     }
 }
 
-// Long rows, or too few rows to fill the GPU one wave per row: row r is
-// cut into K contiguous chunks of whole sweeps, one workgroup per (row,
-// chunk) streaming exactly as the 1-D kernel streams a vector.  With K = 1
+// Long rows, or too few rows to fill the GPU one wave per row: K
+// workgroups share row r's sweeps in grid-stride order (workgroup k takes
+// sweeps k, k + K, ...), streaming exactly as the 1-D kernel streams a
+// vector.  With K = 1
 // the workgroup writes out[r] itself (the old value folded first under
 // accum); otherwise it writes partials[r * K + k] and rows_split_finish
 // folds each row's K partials in index order.
 template <class Op>
 __global__ __launch_bounds__(kBlock) void rows_split_kernel(
     const float* __restrict__ x, uint64_t rows, uint64_t n, uint64_t ld,
-    float* __restrict__ out, int accum, uint32_t K, uint64_t per,
+    float* __restrict__ out, int accum, uint32_t K,
     float* __restrict__ partials)
 {
     __shared__ float lds[kWaves];
@@ -395,7 +396,7 @@ __global__ __launch_bounds__(kBlock) void rows_split_kernel(
         const uint64_t r = b / K;
         const uint32_t k = (uint32_t)(b % K);
         Acc<Op> acc(Op::identity());
-        stream_chunk(x + r * ld, n, per, k, acc);
+        stream_chunk(x + r * ld, n, k, K, acc);
         const float total = block_reduce<Op>(acc.collapse(), lds);
         if (threadIdx.x == 0) {
             if (K == 1)
@@ -498,11 +499,8 @@ hipError_t launch_rows_op(const float* x, size_t rows, size_t n, size_t ld,
         if (K > 1 && (size_t)rows * K * sizeof(float) > ws.partial_bytes)
             return hipErrorInvalidValue;
         float* partials = static_cast<float*>(ws.partials);
-        // Chunk length from the longest whole-vector count a row can have
-        // (rows that start off a 16-byte boundary have at most as many).
-        const uint64_t per = chunk_vectors(n / 4, K);
         rows_split_kernel<Op><<<cap_grid(rows * K), kBlock, 0, stream>>>(
-            x, rows, n, ld, out, accum, K, per, partials);
+            x, rows, n, ld, out, accum, K, partials);
         if (K > 1)
             rows_split_finish_kernel<Op><<<cap_grid(rows), kBlock, 0, stream>>>(
                 partials, rows, K, out, accum);
