@@ -187,22 +187,55 @@ __global__ __launch_bounds__(kBlock) void reduce1d_summaxmin_finish_kernel(
     }
 }
 
-// Fold r into *out with maxNum / minNum semantics by compare-and-swap.
-// Ends when the CAS succeeds or the stored value already is the result.
+// Folding a workgroup's max / min into *out with device-scope atomics.
+//
+// Integer atomics order fp32 bit patterns like the floats themselves: for
+// a non-negative r (sign bit clear) a signed-integer max (max) or min
+// (min) of the two patterns is the float max / min, whatever the sign of
+// the stored value; for a negative r the unsigned-integer min (max) or max
+// (min) is.  So each workgroup needs one atomic, with no retry, provided
+// the stored value is a number or a NaN that loses every comparison: a
+// NaN with the sign bit set for max, clear for min.  The identity written
+// when accum is off is such a NaN; an old value that is a NaN of the
+// other sign (possible only under accum) is replaced by compare-and-swap
+// first.  A NaN partial (every element of the workgroup's share NaN) is
+// skipped, as maxNum / minNum ignore NaN operands.  Before its atomic a
+// workgroup reads the stored value and skips the atomic when it would not
+// change it.  +0 and -0 compare as the integers they are (max keeps +0,
+// min keeps -0), an allowed choice for equal zeros.
 template <class Op>
-__device__ void atomic_fold_cas(float* out, float r)
+constexpr unsigned kLosingNaN = __is_same(Op, OpMax) ? 0xffc00000u : 0x7fc00000u;
+
+template <class Op>
+__device__ void atomic_fold_extreme(float* out, float r)
 {
+    if (__builtin_isnan(r))
+        return;
     unsigned* p = reinterpret_cast<unsigned*>(out);
-    unsigned cur = __hip_atomic_load(p, __ATOMIC_RELAXED,
-                                     __HIP_MEMORY_SCOPE_AGENT);
-    for (;;) {
-        const unsigned want = __float_as_uint(Op::apply(__uint_as_float(cur), r));
-        if (want == cur)
+    unsigned cur = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // An old NaN of the winning sign: swap it for r (retrying while some
+    // other workgroup changes the value first).
+    while (__builtin_isnan(__uint_as_float(cur)) && (cur & 0x80000000u) != (kLosingNaN<Op> & 0x80000000u)) {
+        if (__hip_atomic_compare_exchange_strong(p, &cur, __float_as_uint(r), __ATOMIC_RELAXED,
+                                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
             return;
-        if (__hip_atomic_compare_exchange_strong(
-                p, &cur, want, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
-                __HIP_MEMORY_SCOPE_AGENT))
-            return;
+    }
+    if (__float_as_uint(Op::apply(__uint_as_float(cur), r)) == cur)
+        return; // r would not change the stored value
+    const unsigned bits = __float_as_uint(r);
+    const bool neg = (bits & 0x80000000u) != 0;
+    if constexpr (__is_same(Op, OpMax)) {
+        if (!neg)
+            __hip_atomic_fetch_max(reinterpret_cast<int*>(out), (int)bits, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+        else
+            __hip_atomic_fetch_min(p, bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    } else {
+        if (!neg)
+            __hip_atomic_fetch_min(reinterpret_cast<int*>(out), (int)bits, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+        else
+            __hip_atomic_fetch_max(p, bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 }
 
@@ -216,7 +249,7 @@ __global__ __launch_bounds__(kBlock) void reduce1d_atomic_kernel(
         if constexpr (__is_same(Op, OpSum))
             unsafeAtomicAdd(out, r); // hardware global_atomic_add_f32
         else
-            atomic_fold_cas<Op>(out, r);
+            atomic_fold_extreme<Op>(out, r);
     }
 }
 
@@ -244,8 +277,9 @@ hipError_t launch_atomic(const float* x, size_t n, float* out, int accum,
                          unsigned grid, hipStream_t stream)
 {
     if (!accum) {
-        const unsigned ident = __builtin_bit_cast(
-            unsigned, __is_same(Op, OpSum) ? -0.0f : __builtin_nanf(""));
+        // -0.0 for the sum; for max / min the NaN that loses every
+        // integer comparison of atomic_fold_extreme.
+        const unsigned ident = __is_same(Op, OpSum) ? 0x80000000u : kLosingNaN<Op>;
         fill_u32_kernel<<<1, 64, 0, stream>>>(
             reinterpret_cast<unsigned*>(out), 1, ident);
     }

@@ -120,8 +120,10 @@ int red_sum_max_min_f32(const float* x, size_t n, float* out, int accum,
  * accum == 0 the library first sets *out to the identity (-0.0 for sum, a
  * quiet NaN for max / min) on `stream`.  sum uses the hardware fp32 atomic
  * add, so its rounding order -- and its last bits -- vary from run to run
- * (same error bound); max / min use a compare-and-swap loop and are exact.
- * No workspace is used. */
+ * (same error bound); max / min fold each workgroup's result with one
+ * integer atomic max / min on the fp32 bit pattern and are exact (an old
+ * NaN under accum is replaced first by compare-and-swap; equal zeros of
+ * both signs give +0 for max and -0 for min).  No workspace is used. */
 int red_sum_f32_atomic(const float* x, size_t n, float* out, int accum,
                        red_stream_t stream);
 int red_max_f32_atomic(const float* x, size_t n, float* out, int accum,

@@ -299,3 +299,46 @@ def test_workspace_allocation_failure(red, vec16m):
     red.sum_f32(xd, out, stream=s)
     s.synchronize()
     assert host(out)[0].tobytes() == np.float32(ref).tobytes()
+
+
+def _f32_from_bits(u):
+    return np.array([u], np.uint32).view(np.float32)[0]
+
+
+@pytest.mark.parametrize("op", ["max", "min"])
+def test_atomic_extremes(red, orc, op):
+    """The atomic max / min fold every workgroup's partial with one integer
+    atomic on the fp32 bit pattern (signed for a non-negative partial,
+    unsigned for a negative one).  Cover partials of both signs and of one
+    sign only, NaN shares, signed zeros, and every kind of old value under
+    accum: numbers, infinities, zeros, and NaNs of either sign and with
+    payloads (the NaN that wins the integer comparison is swapped out by
+    compare-and-swap first)."""
+    say("atomic %s: signs, NaN, zeros, old values" % op)
+    n = 1 << 20  # 128 workgroups
+    rng = np.random.default_rng(77)
+    base = rng.standard_normal(n).astype(np.float32)
+    arrays = {
+        "mixed": base,
+        "all_negative": -np.abs(base) - np.float32(0.5),
+        "all_positive": np.abs(base) + np.float32(0.5),
+        "first_half_nan": np.where(np.arange(n) < n // 2, np.float32(np.nan), base),
+        "all_nan": np.full(n, np.nan, np.float32),
+        "zeros": np.where(rng.random(n) < 0.5, np.float32(0.0), np.float32(-0.0)),
+        "neg_zeros": np.full(n, -0.0, np.float32),
+    }
+    olds = [0.0, -0.0, 1.5, -1.5, 1e30, -1e30, float("inf"), float("-inf"),
+            _f32_from_bits(0x7fc00000), _f32_from_bits(0xffc00000),
+            _f32_from_bits(0x7f800001), _f32_from_bits(0xffffffff)]
+    fn = getattr(red, op + "_f32_atomic")
+    for name, x in arrays.items():
+        xd = dev(x)
+        got = run(red, op, xd, atomic=True)
+        check(orc, op, x, got, what="atomic %s %s" % (op, name))
+        for old in olds:
+            old = np.float32(old)
+            out = dev(np.array([old], np.float32))  # keeps the NaN's sign and payload
+            fn(xd, out, accum=True)
+            got = host(out)[0]
+            check(orc, op, x, got, True, old, "atomic %s %s old=%08x" % (
+                op, name, int(np.array([old]).view(np.uint32)[0])))

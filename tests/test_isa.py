@@ -13,8 +13,8 @@ tests pin properties the design relies on but no parity test can see:
   is "flush nothing");
 * the streaming kernels read with non-temporal 16-byte loads, max / min fold
   with the three-input v_max3_f32 / v_min3_f32, the wave reduction uses the
-  DPP row shifts and row broadcasts, and the atomic sum uses the hardware
-  float atomic add.
+  DPP row shifts and row broadcasts, the atomic sum uses the hardware
+  float atomic add and the atomic max / min the integer atomics.
 """
 from __future__ import annotations
 
@@ -169,5 +169,7 @@ def test_wave_reduction_uses_dpp(code):
 def test_atomic_sum_uses_hardware_float_add(code):
     for name, txt in kernels(code, r"reduce1d_atomic_kernel<red_dev::OpSum>").items():
         assert "global_atomic_add_f32" in txt, name
-    for name, txt in kernels(code, r"reduce1d_atomic_kernel<red_dev::Op(Max|Min)>").items():
-        assert "global_atomic_cmpswap" in txt, name
+    for name, txt in kernels(code, r"reduce1d_atomic_kernel<red_dev::OpMax>").items():
+        assert "global_atomic_smax" in txt and "global_atomic_umin" in txt, name
+    for name, txt in kernels(code, r"reduce1d_atomic_kernel<red_dev::OpMin>").items():
+        assert "global_atomic_smin" in txt and "global_atomic_umax" in txt, name
