@@ -1,0 +1,174 @@
+"""Seeded random parity sweep over every entry point.
+
+Sizes are drawn log-uniformly so that the cases fall on both sides of
+every kernel-selection boundary (1-D: one or many workgroups, partial last
+sweep; rows: n up to 16, 64, 128, 256, 512, 1024 and 4096 elements, few and
+many rows, split rows; columns: ragged last column block, row splits,
+16-byte-aligned and unaligned rows), with random base misalignment, row
+padding (filled with NaN, which must never be read) and accum.  Every
+result is checked against the CPU oracle: bit-exact for max / min, the
+page-order sum of rows of at most 64 elements and the integer products;
+the stated tolerances otherwise.  The generator seed is fixed, so a
+failure names a reproducible case."""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from gpu_helpers import (COLPROD_16_TOL, COLPROD_F32_TOL, check_exact, check_rel,
+                         check_sum, dev, host, say)
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def red():
+    import fp32_reductions_amd as red
+    return red
+
+
+@pytest.fixture(scope="module")
+def orc():
+    return oracle.get()
+
+
+def log_uniform(rng, lo, hi):
+    return int(round(math.exp(rng.uniform(math.log(lo), math.log(hi)))))
+
+
+def upload_padded(x2d, off, fill=np.nan):
+    """(rows, ld) fp32 host matrix -> device view starting `off` elements
+    into a larger buffer."""
+    rows, ld = x2d.shape
+    flat = np.full(rows * ld + off + 8, fill, np.float32)
+    flat[off:off + rows * ld] = x2d.reshape(-1)
+    return dev(flat)[off:off + rows * ld].view(rows, ld)
+
+
+def test_random_1d(red, orc):
+    rng = np.random.default_rng(9001)
+    for case in range(60):
+        n = log_uniform(rng, 1, 3_000_000)
+        off = int(rng.integers(0, 4))
+        op = ("sum", "max", "min")[case % 3]
+        accum = bool(rng.integers(0, 2))
+        variant = ("", "_atomic", "fused")[int(rng.integers(0, 3))]
+        old = np.float32(rng.uniform(-4, 4))
+        x = rng.standard_normal(n).astype(np.float32)
+        if rng.random() < 0.2:
+            x[rng.integers(0, n, max(1, n // 100))] = np.nan
+        what = "1d case %d n=%d off=%d op=%s accum=%s variant=%s" % (case, n, off, op, accum, variant)
+        say(what)
+        xd = dev(np.concatenate([np.zeros(off, np.float32), x]))[off:]
+        if variant == "fused":
+            out = dev(np.array([old, old, old], np.float32))
+            red.sum_max_min_f32(xd, out, accum=accum)
+            got = host(out)[("sum", "max", "min").index(op)]
+        else:
+            out = dev(np.array([old], np.float32))
+            getattr(red, op + "_f32" + variant)(xd, out, accum=accum)
+            got = host(out)[0]
+        if op == "sum":
+            s, a = orc.sum_f32(x, accum, old)
+            check_sum(got, s, a, what)
+        else:
+            check_exact(got, getattr(orc, op + "_f32")(x, accum, old), what)
+
+
+def test_random_rows(red, orc):
+    rng = np.random.default_rng(9002)
+    for case in range(60):
+        n = log_uniform(rng, 1, 20000)
+        rows = max(1, min(log_uniform(rng, 1, 200000), 4_000_000 // max(n, 1)))
+        ld = n + int(rng.integers(0, 2)) * int(rng.integers(0, 9))
+        off = int(rng.integers(0, 4))
+        op = ("sum", "max", "min")[case % 3]
+        accum = bool(rng.integers(0, 2))
+        what = "rows case %d rows=%d n=%d ld=%d off=%d op=%s accum=%s" % (
+            case, rows, n, ld, off, op, accum)
+        say(what)
+        x = np.full((rows, ld), np.nan, np.float32)
+        x[:, :n] = rng.uniform(-1, 1, (rows, n)).astype(np.float32)
+        old = rng.uniform(-3, 3, rows).astype(np.float32)
+        xd = upload_padded(x, off)
+        out = dev(old.copy())
+        getattr(red, op + "_rows_f32")(xd, out, n=n, accum=accum)
+        got = host(out)
+        if op == "sum":
+            if n <= 64:
+                want = orc.rows_page_sum_f32(x, rows, n, ld, accum, old)
+                assert (got.view(np.uint32) == want.view(np.uint32)).all(), what
+            s, a = orc.rows_sum_f32(x, rows, n, ld, accum, old)
+            assert (np.abs(got.astype(np.float64) - s) <= 1e-6 * a).all(), what
+        else:
+            want = getattr(orc, "rows_%s_f32" % op)(x, rows, n, ld, accum, old)
+            eq = (got.view(np.uint32) == want.view(np.uint32)) | ((got == 0) & (want == 0))
+            assert eq.all(), what
+
+
+COL_KINDS = ["f32", "bf16", "f16", "i32", "sum", "max", "min"]
+
+
+def test_random_columns(red, orc):
+    rng = np.random.default_rng(9003)
+    for case in range(70):
+        kind = COL_KINDS[case % len(COL_KINDS)]
+        C = log_uniform(rng, 1, 40000)
+        # products are held to their tolerance for R <= 4096
+        rmax = 20000 if kind in ("i32", "sum", "max", "min") else 4096
+        R = max(1, min(log_uniform(rng, 1, rmax), 3_000_000 // C))
+        ld = C + int(rng.integers(0, 2)) * int(rng.integers(0, 17))
+        off = int(rng.integers(0, 4))
+        what = "cols case %d kind=%s R=%d C=%d ld=%d off=%d" % (case, kind, R, C, ld, off)
+        say(what)
+        if kind == "i32":
+            src = rng.integers(-(2 ** 31), 2 ** 31, (R, ld), dtype=np.int64).astype(np.int32)
+            flat = np.zeros(R * ld + off + 8, np.int32)
+            flat[off:off + R * ld] = src.reshape(-1)
+            sd = dev(flat)[off:off + R * ld].view(R, ld)
+            out = torch.zeros(C, dtype=torch.int32, device="cuda")
+            red.colprod_i32(sd, out, C=C)
+            want = orc.colprod_i32(src, R, C, ld)
+            assert (host(out) == want).all(), what
+            continue
+        # factors near 1, so that no product leaves the normal range of fp16
+        lo, hi = (0.75, 1.25) if R <= 16 else ((0.99, 1.01) if R <= 2000 else (0.999, 1.001))
+        vals = np.full((R, ld), np.nan, np.float32)
+        if kind in ("sum", "max", "min"):
+            vals[:, :C] = rng.uniform(-1, 1, (R, C)).astype(np.float32)
+        else:
+            vals[:, :C] = rng.uniform(lo, hi, (R, C)).astype(np.float32)
+        if kind in ("f32", "sum", "max", "min"):
+            sd = upload_padded(vals, off)
+            out = torch.zeros(C, dtype=torch.float32, device="cuda")
+            if kind == "f32":
+                red.colprod_f32(sd, out, C=C)
+                check_rel(host(out), orc.colprod_f32(vals, R, C, ld), COLPROD_F32_TOL, what)
+            else:
+                accum = bool(rng.integers(0, 2))
+                old = rng.uniform(-3, 3, C).astype(np.float32)
+                out = dev(old.copy())
+                getattr(red, kind + "_cols_f32")(sd, out, C=C, accum=accum)
+                got = host(out)
+                if kind == "sum":
+                    s, a = orc.cols_sum_f32(vals, R, C, ld, accum, old)
+                    assert (np.abs(got.astype(np.float64) - s) <= 1e-6 * a).all(), what
+                else:
+                    want = getattr(orc, "cols_%s_f32" % kind)(vals, R, C, ld, accum, old)
+                    eq = (got.view(np.uint32) == want.view(np.uint32)) | ((got == 0) & (want == 0))
+                    assert eq.all(), what
+        else:
+            tdt = torch.bfloat16 if kind == "bf16" else torch.float16
+            h = torch.from_numpy(vals).to(tdt)           # exact RNE conversion; NaN padding stays NaN
+            bits = h.view(torch.int16).numpy().view(np.uint16)
+            flat = np.zeros(R * ld + off + 8, np.uint16)
+            flat[off:off + R * ld] = bits.reshape(-1)
+            sd = dev(flat.view(np.int16))[off:off + R * ld].view(R, ld).view(tdt)
+            out = torch.zeros(C, dtype=tdt, device="cuda")
+            getattr(red, "colprod_" + kind)(sd, out, C=C)
+            got = host(out.float())
+            want = getattr(orc, "colprod_" + kind)(bits, R, C, ld)
+            check_rel(got, want, COLPROD_16_TOL, what)
