@@ -28,6 +28,7 @@
  *   - Every call is asynchronous with respect to the host: it validates its
  *     arguments, enqueues kernels on `stream` and returns.  `stream` is a
  *     hipStream_t passed as an opaque pointer; NULL means the null stream.
+ *     It must belong to the current HIP device, as the buffers must.
  *     Results are visible after the stream is synchronised.
  *   - The return value is a status code (enum red_status).  Errors are
  *     reported synchronously and never abort.  A status other than RED_OK
