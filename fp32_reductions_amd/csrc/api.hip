@@ -89,6 +89,13 @@ int stream_workspace(int dev, hipStream_t stream, Workspace* ws)
 
 int hip_status(hipError_t e) { return e == hipSuccess ? RED_OK : RED_ERR_HIP; }
 
+// Called right before a call's launches: drops an error an earlier,
+// unrelated HIP call left on this thread, so that the status returned after
+// the launches (hipGetLastError) reports this call's own launches.  A
+// sticky error (a fault of an earlier kernel) is reported again by the
+// launches themselves.
+void clear_stale_error() { (void)hipGetLastError(); }
+
 int check_1d(const float* x, size_t n, const float* out)
 {
     if (!x || !out)
@@ -116,6 +123,7 @@ int reduce1d(OpKind op, const float* x, size_t n, float* out, int accum,
     const hipStream_t s = static_cast<hipStream_t>(stream);
     if ((st = stream_workspace(dev, s, &ws)) != RED_OK)
         return st;
+    clear_stale_error();
     return hip_status(red::launch_reduce1d(op, x, n, out, accum, info, ws, s));
 }
 
@@ -135,6 +143,7 @@ int reduce1d_summaxmin(const float* x, size_t n, float* out, int accum,
     const hipStream_t s = static_cast<hipStream_t>(stream);
     if ((st = stream_workspace(dev, s, &ws)) != RED_OK)
         return st;
+    clear_stale_error();
     return hip_status(red::launch_reduce1d_summaxmin(x, n, out, accum, info, ws, s));
 }
 
@@ -150,6 +159,7 @@ int reduce1d_atomic(OpKind op, const float* x, size_t n, float* out, int accum,
     DeviceInfo info;
     if ((st = current_device(&dev, &info)) != RED_OK)
         return st;
+    clear_stale_error();
     return hip_status(red::launch_reduce1d_atomic(
         op, x, n, out, accum, info, static_cast<hipStream_t>(stream)));
 }
@@ -174,6 +184,7 @@ int reduce_rows(OpKind op, const float* x, size_t rows, size_t n, size_t ld,
     if (red::rows_chunks(x, rows, n, info) > 1 &&
         (st = stream_workspace(dev, s, &ws)) != RED_OK)
         return st;
+    clear_stale_error();
     return hip_status(red::launch_rows(op, x, rows, n, ld, out, accum, info, ws, s));
 }
 
@@ -186,8 +197,10 @@ int check_cols(ColType t, const void* src, size_t R, size_t C, size_t ld,
     if (!src || !dst || ld < C || !extent_ok(R, ld, C, es) ||
         C > SIZE_MAX / sizeof(float))
         return RED_ERR_INVALID;
-    // A launch holds at most 2^32 - 1 work-items per grid dimension.
-    const size_t cols_per_wg = 64 * (16 / es);
+    // A launch holds at most 2^32 - 1 work-items per grid dimension: the
+    // column kernel's workgroups of 256 threads each cover 16 lanes x
+    // (16 / es) columns.
+    const size_t cols_per_wg = 16 * (16 / es);
     if ((C + cols_per_wg - 1) / cols_per_wg >= (size_t(1) << 24))
         return RED_ERR_INVALID;
     if (!aligned(src, es) || !aligned(dst, es))
@@ -212,6 +225,7 @@ int cols(OpKind op, const float* src, size_t R, size_t C, size_t ld, float* dst,
     if ((st = stream_workspace(dev, s, &ws)) != RED_OK)
         return st;
     const red::ColprodPlan plan = red::colprod_plan(ColType::F32, R, C, info, ws);
+    clear_stale_error();
     return hip_status(red::launch_cols(op, src, R, C, ld, dst, accum, plan, ws, s));
 }
 
@@ -232,6 +246,7 @@ int colprod(ColType t, const void* src, size_t R, size_t C, size_t ld,
     if ((st = stream_workspace(dev, s, &ws)) != RED_OK)
         return st;
     const red::ColprodPlan plan = red::colprod_plan(t, R, C, info, ws);
+    clear_stale_error();
     return hip_status(red::launch_colprod(t, src, R, C, ld, dst, plan, ws, s));
 }
 

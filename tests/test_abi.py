@@ -130,6 +130,7 @@ def test_cols_validation(lib, name):
     assert f(A16, 4, 4, 4, None, 0, None) == RED_ERR_INVALID
     assert f(A16, 4, 5, 4, A16, 0, None) == RED_ERR_INVALID      # ld < C
     assert f(A16, 1 << 40, 1 << 30, 1 << 30, A16, 0, None) == RED_ERR_INVALID
+    assert f(A16, 1, 1 << 30, 1 << 30, A16, 0, None) == RED_ERR_INVALID  # 2^24 column blocks
     assert f(A16 + 2, 4, 4, 4, A16, 0, None) == RED_ERR_ALIGN
     assert f(A16, 4, 4, 4, A16 + 1, 0, None) == RED_ERR_ALIGN
 
@@ -148,6 +149,9 @@ def test_colprod_validation(lib, name, es):
     assert f(A16, 4, 5, 4, A16, None) == RED_ERR_INVALID      # ld < C
     assert f(A16, 1 << 40, 1 << 30, 1 << 30, A16, None) == RED_ERR_INVALID
     assert f(A16, 2, 1 << 40, 1 << 40, A16, None) == RED_ERR_INVALID  # grid limit
+    # exactly 2^24 column blocks of 16 lanes x 16 bytes: one too many
+    C = (1 << 24) * 16 * (16 // es)
+    assert f(A16, 1, C, C, A16, None) == RED_ERR_INVALID
     assert f(A16 + 1, 4, 4, 4, A16, None) == RED_ERR_ALIGN
     assert f(A16, 4, 4, 4, A16 + 1, None) == RED_ERR_ALIGN
     if es == 4:
