@@ -155,8 +155,9 @@ class Rotor:
         return len(self.copies)
 
 
-# The column kernel; a second kernel runs only when the plan splits the rows.
-COLRED = "colred_kernel<{0}, true> (+ colred_finish_kernel<{0}> if rows are split)"
+# The column kernel (16 row groups per 256-byte column block at these
+# shapes); a second kernel runs only when the plan splits the rows.
+COLRED = "colred_kernel<{0}, true, 16> (+ colred_finish_kernel<{0}> if rows are split)"
 
 
 def up(torch, a):
@@ -400,7 +401,7 @@ def wl_rows32(torch, red, orc, steps):
                   lambda k: red.plan("max_rows_f32", ad, o[1])),
              Call("rows_min", "rows_tile_kernel<OpMin>", rbytes,
                   lambda k: red.plan("min_rows_f32", ad, o[2])),
-             Call("colprod_tile16", COLRED.format("TraitsF32, OpMul<float>"), 16 * 16 * 4 + 64,
+             Call("colprod_tile16", "colred_narrow_kernel<TraitsF32, OpMul<float>>", 16 * 16 * 4 + 64,
                   lambda k: red.plan("colprod_f32", td, ot))]
     cpu = [(rbytes, lambda: orc.rows_page_sum_f32(a, rows, n, n)),
            (rbytes, lambda: orc.rows_max_f32(a, rows, n, n)),

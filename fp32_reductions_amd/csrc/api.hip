@@ -224,7 +224,7 @@ int cols(OpKind op, const float* src, size_t R, size_t C, size_t ld, float* dst,
     const hipStream_t s = static_cast<hipStream_t>(stream);
     if ((st = stream_workspace(dev, s, &ws)) != RED_OK)
         return st;
-    const red::ColprodPlan plan = red::colprod_plan(ColType::F32, R, C, info, ws);
+    const red::ColprodPlan plan = red::colprod_plan(ColType::F32, src, R, C, ld, info, ws);
     clear_stale_error();
     return hip_status(red::launch_cols(op, src, R, C, ld, dst, accum, plan, ws, s));
 }
@@ -245,7 +245,7 @@ int colprod(ColType t, const void* src, size_t R, size_t C, size_t ld,
     const hipStream_t s = static_cast<hipStream_t>(stream);
     if ((st = stream_workspace(dev, s, &ws)) != RED_OK)
         return st;
-    const red::ColprodPlan plan = red::colprod_plan(t, R, C, info, ws);
+    const red::ColprodPlan plan = red::colprod_plan(t, src, R, C, ld, info, ws);
     clear_stale_error();
     return hip_status(red::launch_colprod(t, src, R, C, ld, dst, plan, ws, s));
 }

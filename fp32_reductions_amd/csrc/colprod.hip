@@ -18,9 +18,13 @@
 //    row-group order;
 //  * when the grid needs more workgroups than there are column blocks, the
 //    rows are split into S slices (blockIdx.y); each workgroup stores its
-//    partial row in the workspace, and a second kernel multiplies the S
-//    partial rows of each column in slice order, narrows once to T and
-//    writes dst;
+//    partial row in the workspace, and a second kernel combines the S
+//    partial rows of each column in a fixed order (strided runs per thread,
+//    then a pairwise tree in LDS), narrows once to T and writes dst;
+//  * rows narrower than 256 bytes (16-byte aligned, with C * sizeof(T) a
+//    multiple of 16) would leave most of those lanes idle: a narrow-row
+//    kernel reads whole rows instead, 256 / W rows of W vectors per step,
+//    each workgroup walking sweeps of eight steps grid-stride;
 //  * tile loads are non-temporal: each element is read once.
 //
 // Column sum / max / min of an fp32 tile reduce each column by the TVM
@@ -159,16 +163,21 @@ struct OpMul {
 // the column sum / max / min).  Under accum (never for products) the old
 // dst[j] is folded in first.
 //
-// A workgroup owns kCols = 16 * V columns (256 bytes of each row) and the
-// rows of its slice.  Its 256 threads form 16 row groups of 16 lanes: row
-// group g reads rows g, g + 16, g + 32, ... of the slice, each lane one
-// 16-byte vector per row, with kRowsInFlight rows in flight.  The 16 row
-// groups' partial products are combined in LDS in row-group order.
+// A column block is kCols = 16 * V columns (256 bytes of each row).  A
+// workgroup's 256 threads form 16 row groups of 16 lanes, GPB row groups
+// per column block, so that it owns 16 / GPB adjacent column blocks and the
+// rows of its slice: row group gr of a block reads rows gr, gr + GPB,
+// gr + 2 GPB, ... of the slice, each lane one 16-byte vector per row, with
+// kRowsInFlight rows in flight.  The GPB partial products of a block are
+// combined in LDS in row-group order (GPB = 1 stores straight from the
+// lanes).  GPB = 16 (one block per workgroup, a wave reading 256 bytes of
+// four rows) serves tiles of many rows; GPB = 4 and 1 give short, wide
+// tiles fewer and longer-lived workgroups, a wave reading 1 KiB of a row.
 // (Measured on MI355X for a 4096 x 16384 fp32 tile read from HBM: 40.6 us
-// per call with 256 such workgroups and no second pass, against 44.1 us
-// for workgroups of 256 columns whose waves each read 1 KiB of a row, split
-// four ways over the rows and finished by a second kernel.)
-template <class Tr, class Op, bool VEC>
+// per call with 256 workgroups of GPB = 16 and no second pass, against
+// 44.1 us for workgroups of 256 columns whose waves each read 1 KiB of a
+// row, split four ways over the rows and finished by a second kernel.)
+template <class Tr, class Op, bool VEC, int GPB>
 __global__ __launch_bounds__(kBlock) void colred_kernel(
     const typename Tr::T* __restrict__ src, uint64_t R, uint64_t C,
     uint64_t ld, typename Tr::T* __restrict__ dst,
@@ -177,37 +186,44 @@ __global__ __launch_bounds__(kBlock) void colred_kernel(
     using T = typename Tr::T;
     using A = typename Tr::A;
     constexpr int V = Tr::V;
-    constexpr int kCols = kLanesPerRow * V;         // columns per workgroup
+    constexpr int kCols = kLanesPerRow * V;         // columns per block
     constexpr int kGroups = kBlock / kLanesPerRow;  // row groups per workgroup
+    constexpr int kBlocksPerWg = kGroups / GPB;
+    static_assert(kGroups % GPB == 0, "row groups split evenly over blocks");
 
-    __shared__ A lds[kGroups][kCols];
+    __shared__ A lds[GPB > 1 ? kGroups : 1][kCols];
 
     const uint32_t g = threadIdx.x / kLanesPerRow;
     const uint32_t q = threadIdx.x % kLanesPerRow;
-    const uint64_t cb = blockIdx.x;
+    const uint32_t gr = g % GPB;                      // row group within the block
+    const uint64_t cb = (uint64_t)blockIdx.x * kBlocksPerWg + g / GPB;
     const uint32_t S = gridDim.y;
     const uint64_t s = blockIdx.y;
     const uint64_t jb = cb * kCols; // first column of the block
     const uint64_t r0 = s * rows_per_split;
     const uint64_t r1 = (r0 + rows_per_split < R) ? r0 + rows_per_split : R;
+    const bool full = VEC && jb + kCols <= C;
 
     A acc[V];
 #pragma unroll
     for (int k = 0; k < V; ++k)
         acc[k] = Op::identity();
 
-    uint64_t r = r0 + g;
-    if (VEC && jb + kCols <= C) {
+    uint64_t r = r0 + gr;
+    if (jb >= C) {
+        // A block past the last column (the workgroup's last blocks when
+        // 16 / GPB does not divide the block count): nothing to read.
+    } else if (full) {
         // Lane q owns columns jb + qV .. jb + qV + V - 1: one 16-byte vector
         // per row.
         const T* __restrict__ col = src + jb + (uint64_t)q * V;
-        for (; r + (uint64_t)kGroups * (kRowsInFlight - 1) < r1;
-             r += (uint64_t)kGroups * kRowsInFlight) {
+        for (; r + (uint64_t)GPB * (kRowsInFlight - 1) < r1;
+             r += (uint64_t)GPB * kRowsInFlight) {
             uint4 v[kRowsInFlight];
 #pragma unroll
             for (int u = 0; u < kRowsInFlight; ++u)
                 v[u] = load_stream(reinterpret_cast<const uint4*>(
-                    col + (r + (uint64_t)u * kGroups) * ld));
+                    col + (r + (uint64_t)u * GPB) * ld));
 #pragma unroll
             for (int u = 0; u < kRowsInFlight; ++u) {
                 A a[V];
@@ -217,16 +233,13 @@ __global__ __launch_bounds__(kBlock) void colred_kernel(
                     acc[k] = Op::apply(acc[k], a[k]);
             }
         }
-        for (; r < r1; r += kGroups) {
+        for (; r < r1; r += GPB) {
             A a[V];
             Tr::unpack(load_stream(reinterpret_cast<const uint4*>(col + r * ld)), a);
 #pragma unroll
             for (int k = 0; k < V; ++k)
                 acc[k] = Op::apply(acc[k], a[k]);
         }
-#pragma unroll
-        for (int k = 0; k < V; ++k)
-            lds[g][q * V + k] = acc[k];
     } else {
         // Rows not 16-byte aligned, or the ragged last column block:
         // element loads, lane q owning columns jb + q + 16k, so that each
@@ -242,14 +255,14 @@ __global__ __launch_bounds__(kBlock) void colred_kernel(
             ok[k] = jb + c < C;
             off[k] = ok[k] ? c : 0u;
         }
-        for (; r + (uint64_t)kGroups * (kRowsInFlight - 1) < r1;
-             r += (uint64_t)kGroups * kRowsInFlight) {
+        for (; r + (uint64_t)GPB * (kRowsInFlight - 1) < r1;
+             r += (uint64_t)GPB * kRowsInFlight) {
             T v[kRowsInFlight][V];
 #pragma unroll
             for (int u = 0; u < kRowsInFlight; ++u)
 #pragma unroll
                 for (int k = 0; k < V; ++k)
-                    v[u][k] = blk[(r + (uint64_t)u * kGroups) * ld + off[k]];
+                    v[u][k] = blk[(r + (uint64_t)u * GPB) * ld + off[k]];
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int u = 0; u < kRowsInFlight; ++u)
@@ -258,27 +271,145 @@ __global__ __launch_bounds__(kBlock) void colred_kernel(
                     if (ok[k])
                         acc[k] = Op::apply(acc[k], Tr::widen(v[u][k]));
         }
-        for (; r < r1; r += kGroups) {
+        for (; r < r1; r += GPB) {
 #pragma unroll
             for (int k = 0; k < V; ++k)
                 if (ok[k])
                     acc[k] = Op::apply(acc[k], Tr::widen(blk[r * ld + off[k]]));
         }
-#pragma unroll
-        for (int k = 0; k < V; ++k)
-            lds[g][q + kLanesPerRow * k] = acc[k];
     }
-    // Combine the row groups' partial rows in row-group order.
+
+    if constexpr (GPB == 1) {
+        // One row group per block: each lane holds its columns' results.
+        if (jb < C) {
+#pragma unroll
+            for (int k = 0; k < V; ++k) {
+                const uint64_t j = jb + (full ? (uint64_t)q * V + k
+                                              : (uint64_t)q + (uint64_t)kLanesPerRow * k);
+                if (j < C) {
+                    if (S == 1)
+                        dst[j] = Tr::narrow(accum ? Op::apply(Tr::widen(dst[j]), acc[k]) : acc[k]);
+                    else
+                        partials[s * C + j] = acc[k];
+                }
+            }
+        }
+    } else {
+#pragma unroll
+        for (int k = 0; k < V; ++k) {
+            if (full)
+                lds[g][q * V + k] = acc[k];
+            else
+                lds[g][q + kLanesPerRow * k] = acc[k];
+        }
+        // Combine each block's row groups' partial rows in row-group order.
+        __syncthreads();
+        for (uint32_t i = threadIdx.x; i < (uint32_t)(kBlocksPerWg * kCols); i += kBlock) {
+            const uint32_t b = i / kCols;
+            const uint32_t c = i % kCols;
+            A p = lds[b * GPB][c];
+#pragma unroll
+            for (int w = 1; w < GPB; ++w)
+                p = Op::apply(p, lds[b * GPB + w][c]);
+            const uint64_t j = ((uint64_t)blockIdx.x * kBlocksPerWg + b) * kCols + c;
+            if (j < C) {
+                if (S == 1)
+                    dst[j] = Tr::narrow(accum ? Op::apply(Tr::widen(dst[j]), p) : p);
+                else
+                    partials[s * C + j] = p;
+            }
+        }
+    }
+}
+
+// Narrow rows (a row of ld elements spans W < 16 aligned 16-byte vectors,
+// and C * sizeof(T) is a multiple of 16): the column-block layout above
+// would leave most lanes idle, so a workgroup reads whole rows instead.
+// Thread t owns vector cv = t % W of row offset ro = t / W; RB = 256 / W
+// rows form one step, read as RB * W consecutive vectors (threads past
+// RB * W and vectors of padding columns stay idle).  Steps are taken eight
+// at a time as sweeps of 8 * RB rows, and workgroup s walks sweeps s,
+// s + S, s + 2S, ... (grid-stride, as the 1-D stream).  Each thread folds
+// its rows in increasing order; the RB row offsets are then combined in LDS
+// by a fixed pairwise tree, and the RB threads of row offset 0 store the
+// workgroup's partial row (or dst when S == 1).
+template <class Tr, class Op>
+__global__ __launch_bounds__(kBlock) void colred_narrow_kernel(
+    const typename Tr::T* __restrict__ src, uint64_t R, uint64_t C,
+    uint64_t ld, uint32_t W, typename Tr::T* __restrict__ dst,
+    typename Tr::A* __restrict__ partials, int accum)
+{
+    using T = typename Tr::T;
+    using A = typename Tr::A;
+    constexpr int V = Tr::V;
+
+    __shared__ A lds[kBlock][V];
+
+    const uint32_t RB = kBlock / W;
+    const uint32_t t = threadIdx.x;
+    const uint32_t ro = t / W;
+    const uint32_t cv = t - ro * W;
+    const bool live = ro < RB && (uint64_t)cv * V < C;
+    const uint32_t S = gridDim.x;
+    const uint64_t s = blockIdx.x;
+
+    A acc[V];
+#pragma unroll
+    for (int k = 0; k < V; ++k)
+        acc[k] = Op::identity();
+
+    if (live) {
+        const T* __restrict__ col = src + (uint64_t)cv * V;
+        const uint64_t sweep = (uint64_t)kRowsInFlight * RB;
+        uint64_t r = s * sweep + ro;
+        for (; r + (uint64_t)(kRowsInFlight - 1) * RB < R; r += (uint64_t)S * sweep) {
+            uint4 v[kRowsInFlight];
+#pragma unroll
+            for (int u = 0; u < kRowsInFlight; ++u)
+                v[u] = load_stream(reinterpret_cast<const uint4*>(
+                    col + (r + (uint64_t)u * RB) * ld));
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int u = 0; u < kRowsInFlight; ++u) {
+                A a[V];
+                Tr::unpack(v[u], a);
+#pragma unroll
+                for (int k = 0; k < V; ++k)
+                    acc[k] = Op::apply(acc[k], a[k]);
+            }
+        }
+        // The sweep that reaches past R (if it is this workgroup's) is the
+        // last one: its remaining rows are read one step at a time.
+        for (; r < R; r += RB) {
+            A a[V];
+            Tr::unpack(load_stream(reinterpret_cast<const uint4*>(col + r * ld)), a);
+#pragma unroll
+            for (int k = 0; k < V; ++k)
+                acc[k] = Op::apply(acc[k], a[k]);
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < V; ++k)
+        lds[t][k] = acc[k];
+
+    uint32_t half = 1;
+    while (half * 2 < RB)
+        half *= 2;
+    for (; half >= 1; half /= 2) {
+        __syncthreads();
+        if (ro < half && ro + half < RB) {
+#pragma unroll
+            for (int k = 0; k < V; ++k)
+                lds[t][k] = Op::apply(lds[t][k], lds[t + half * W][k]);
+        }
+    }
     __syncthreads();
 
-    if (threadIdx.x < (uint32_t)kCols) {
-        const uint32_t c = threadIdx.x;
-        A p = lds[0][c];
+    if (ro == 0 && live) {
 #pragma unroll
-        for (int w = 1; w < kGroups; ++w)
-            p = Op::apply(p, lds[w][c]);
-        const uint64_t j = cb * kCols + c;
-        if (j < C) {
+        for (int k = 0; k < V; ++k) {
+            const uint64_t j = (uint64_t)cv * V + k;
+            const A p = lds[t][k];
             if (S == 1)
                 dst[j] = Tr::narrow(accum ? Op::apply(Tr::widen(dst[j]), p) : p);
             else
@@ -287,20 +418,55 @@ __global__ __launch_bounds__(kBlock) void colred_kernel(
     }
 }
 
-// Second pass (S > 1): one thread per column combines the S partial rows in
-// slice order (after the old dst[j] under accum) and narrows once to T.
+// Second pass (S > 1).  Workgroup b takes FC consecutive columns (FC a power
+// of two chosen by the host so that each thread has few slices to read);
+// its threads form H = 256 / FC slice groups.  Thread (h, c) folds slices
+// h, h + H, h + 2H, ... of its column in increasing order with eight loads
+// in flight, the H values of a column are combined in LDS by a fixed
+// pairwise tree, and the result is folded after the old dst[j] under accum
+// and narrowed once to T.
 template <class Tr, class Op>
 __global__ __launch_bounds__(kBlock) void colred_finish_kernel(
     const typename Tr::A* __restrict__ partials, uint32_t S, uint64_t C,
-    typename Tr::T* __restrict__ dst, int accum)
+    uint32_t fc_log2, typename Tr::T* __restrict__ dst, int accum)
 {
-    const uint64_t j = (uint64_t)blockIdx.x * kBlock + threadIdx.x;
-    if (j >= C)
-        return;
-    typename Tr::A p = accum ? Op::apply(Tr::widen(dst[j]), partials[j]) : partials[j];
-    for (uint32_t k = 1; k < S; ++k)
-        p = Op::apply(p, partials[(uint64_t)k * C + j]);
-    dst[j] = Tr::narrow(p);
+    using A = typename Tr::A;
+    constexpr int kBatch = 8;
+    __shared__ A lds[kBlock];
+
+    const uint32_t FC = 1u << fc_log2;
+    const uint32_t H = kBlock >> fc_log2;
+    const uint32_t c = threadIdx.x & (FC - 1);
+    const uint32_t h = threadIdx.x >> fc_log2;
+    const uint64_t j = (uint64_t)blockIdx.x * FC + c;
+
+    A p = Op::identity();
+    if (j < C) {
+        for (uint32_t k = h; k < S; k += kBatch * H) {
+            A v[kBatch];
+#pragma unroll
+            for (int u = 0; u < kBatch; ++u) {
+                const uint32_t sl = k + u * H;
+                v[u] = partials[(uint64_t)(sl < S ? sl : k) * C + j];
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int u = 0; u < kBatch; ++u)
+                if (k + u * H < S)
+                    p = Op::apply(p, v[u]);
+        }
+    }
+    lds[threadIdx.x] = p;
+    for (uint32_t half = H / 2; half >= 1; half /= 2) {
+        __syncthreads();
+        if (h < half)
+            lds[threadIdx.x] = Op::apply(lds[threadIdx.x], lds[threadIdx.x + half * FC]);
+    }
+    __syncthreads();
+    if (h == 0 && j < C) {
+        const A q = lds[threadIdx.x];
+        dst[j] = Tr::narrow(accum ? Op::apply(Tr::widen(dst[j]), q) : q);
+    }
 }
 
 template <class Tr, class Op>
@@ -310,20 +476,29 @@ hipError_t launch_typed(const void* src, size_t R, size_t C, size_t ld,
 {
     using T = typename Tr::T;
     using A = typename Tr::A;
-    const dim3 grid(plan.col_blocks, plan.splits);
     const bool vec = (((uintptr_t)src & 15u) == 0) && ((ld * sizeof(T)) % 16 == 0);
     const T* s = static_cast<const T*>(src);
     T* d = static_cast<T*>(dst);
     A* part = static_cast<A*>(ws.partials);
-    if (vec)
-        colred_kernel<Tr, Op, true><<<grid, kBlock, 0, stream>>>(
-            s, R, C, ld, d, part, plan.rows_per_split, accum);
-    else
-        colred_kernel<Tr, Op, false><<<grid, kBlock, 0, stream>>>(
-            s, R, C, ld, d, part, plan.rows_per_split, accum);
+    if (plan.narrow_w) {
+        colred_narrow_kernel<Tr, Op><<<plan.splits, kBlock, 0, stream>>>(
+            s, R, C, ld, plan.narrow_w, d, part, accum);
+    } else {
+        const unsigned per_wg = kBlock / kLanesPerRow / plan.group_rows;
+        const dim3 grid((plan.col_blocks + per_wg - 1) / per_wg, plan.splits);
+        auto go = [&](auto kern) {
+            kern<<<grid, kBlock, 0, stream>>>(s, R, C, ld, d, part, plan.rows_per_split, accum);
+        };
+        if (plan.group_rows == 1)
+            vec ? go(colred_kernel<Tr, Op, true, 1>) : go(colred_kernel<Tr, Op, false, 1>);
+        else if (plan.group_rows == 4)
+            vec ? go(colred_kernel<Tr, Op, true, 4>) : go(colred_kernel<Tr, Op, false, 4>);
+        else
+            vec ? go(colred_kernel<Tr, Op, true, 16>) : go(colred_kernel<Tr, Op, false, 16>);
+    }
     if (plan.splits > 1)
-        colred_finish_kernel<Tr, Op><<<(unsigned)((C + kBlock - 1) / kBlock), kBlock, 0, stream>>>(
-            part, plan.splits, C, d, accum);
+        colred_finish_kernel<Tr, Op><<<plan.finish_blocks, kBlock, 0, stream>>>(
+            part, plan.splits, C, plan.finish_cols_log2, d, accum);
     return hipGetLastError();
 }
 
@@ -338,31 +513,88 @@ size_t colprod_elem_size(ColType t)
 // the partial-row traffic grows relative to the tile.
 constexpr uint64_t kMinRowsPerSplit = 32;
 constexpr uint64_t kMaxSplits = 65535; // gridDim.y limit
+// Workgroups per compute unit for the narrow-row kernel (grid-stride).
+#ifndef RED_COLPROD_NARROW_WG_PER_CU
+#define RED_COLPROD_NARROW_WG_PER_CU 2
+#endif
+constexpr uint64_t kNarrowWgPerCu = RED_COLPROD_NARROW_WG_PER_CU;
+// Row groups per column block, from the fewest the planner may choose
+// (1, 4 or 16).
+#ifndef RED_COLPROD_MIN_GROUP_ROWS
+#define RED_COLPROD_MIN_GROUP_ROWS 1
+#endif
+constexpr uint64_t kMinGroupRows = RED_COLPROD_MIN_GROUP_ROWS;
+// Second pass: at most this many slices per thread when the column count
+// allows it.
+constexpr uint64_t kFinishSlicesPerThread = 8;
 
-ColprodPlan colprod_plan(ColType t, size_t R, size_t C, const DeviceInfo& dev,
-                         const Workspace& ws)
+ColprodPlan colprod_plan(ColType t, const void* src, size_t R, size_t C, size_t ld,
+                         const DeviceInfo& dev, const Workspace& ws)
 {
     ColprodPlan p;
-    const uint64_t cols = (uint64_t)kLanesPerRow * (16 / colprod_elem_size(t));
-    p.col_blocks = (unsigned)((C + cols - 1) / cols);
-    const uint64_t target = (uint64_t)dev.cus * kColprodWgPerCu;
+    const uint64_t es = colprod_elem_size(t);
+    const bool vec = (((uintptr_t)src & 15u) == 0) && ((ld * es) % 16 == 0);
     uint64_t S = 1;
-    if (p.col_blocks < target)
-        S = (target + p.col_blocks - 1) / p.col_blocks;
-    const uint64_t s_rows = (R + kMinRowsPerSplit - 1) / kMinRowsPerSplit;
-    if (S > s_rows)
-        S = s_rows;
-    if (S > kMaxSplits)
-        S = kMaxSplits;
-    // The workspace bounds S * C partial values.
-    while (S > 1 && S * C * 4 > ws.partial_bytes)
-        S = (S + 1) / 2;
-    if (S < 1)
-        S = 1;
-    p.rows_per_split = (R + S - 1) / S;
-    S = (R + p.rows_per_split - 1) / p.rows_per_split; // no empty slice
+    if (vec && (C * es) % 16 == 0 && ld * es < (uint64_t)kLanesPerRow * 16) {
+        // Narrow rows: one workgroup spans whole rows; the grid-stride walk
+        // covers every sweep whatever S is.
+        p.narrow_w = (unsigned)(ld * es / 16);
+        p.col_blocks = 1;
+        const uint64_t rows_per_step = kBlock / p.narrow_w;
+        const uint64_t sweep = rows_per_step * kRowsInFlight;
+        const uint64_t sweeps = (R + sweep - 1) / sweep;
+        S = (uint64_t)dev.cus * kNarrowWgPerCu;
+        if (S > sweeps)
+            S = sweeps;
+        while (S > 1 && S * C * 4 > ws.partial_bytes)
+            S = (S + 1) / 2;
+        if (S < 1)
+            S = 1;
+        p.rows_per_split = R;
+    } else {
+        const uint64_t cols = (uint64_t)kLanesPerRow * (16 / es);
+        p.col_blocks = (unsigned)((C + cols - 1) / cols);
+        const uint64_t target = (uint64_t)dev.cus * kColprodWgPerCu;
+        // Fewest row groups per block that still give the grid `target`
+        // workgroups; tiles with fewer blocks than that keep 16 and split
+        // their rows instead.
+        const uint64_t groups = kBlock / kLanesPerRow;
+        p.group_rows = (unsigned)groups;
+        for (uint64_t g = kMinGroupRows; g < groups; g *= 4) {
+            if ((p.col_blocks * g + groups - 1) / groups >= target) {
+                p.group_rows = (unsigned)g;
+                break;
+            }
+        }
+        const uint64_t wgs = (p.col_blocks * p.group_rows + groups - 1) / groups;
+        if (wgs < target)
+            S = (target + wgs - 1) / wgs;
+        const uint64_t s_rows = (R + kMinRowsPerSplit - 1) / kMinRowsPerSplit;
+        if (S > s_rows)
+            S = s_rows;
+        if (S > kMaxSplits)
+            S = kMaxSplits;
+        // The workspace bounds S * C partial values.
+        while (S > 1 && S * C * 4 > ws.partial_bytes)
+            S = (S + 1) / 2;
+        if (S < 1)
+            S = 1;
+        p.rows_per_split = (R + S - 1) / S;
+        S = (R + p.rows_per_split - 1) / p.rows_per_split; // no empty slice
+    }
     p.splits = (unsigned)S;
     p.partial_bytes = S > 1 ? S * C * 4 : 0;
+    if (S > 1) {
+        // Columns per second-pass workgroup: a power of two, no wider than
+        // needed to cover C, and narrow enough that each thread reads at
+        // most kFinishSlicesPerThread slices when it can.
+        uint32_t lg = 8; // 256 columns
+        while (lg > 0 && (((uint64_t)1 << lg) * S > kBlock * kFinishSlicesPerThread ||
+                          ((uint64_t)1 << lg) >= 2 * C))
+            --lg;
+        p.finish_cols_log2 = lg;
+        p.finish_blocks = (unsigned)((C + ((uint64_t)1 << lg) - 1) >> lg);
+    }
     return p;
 }
 

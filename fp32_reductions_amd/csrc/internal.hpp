@@ -71,13 +71,17 @@ enum class ColType { F32, F16, BF16, I32, U16 };
 size_t colprod_elem_size(ColType t);
 // Row splits the colprod kernel uses, and the workspace it needs.
 struct ColprodPlan {
-    unsigned col_blocks = 0;  // workgroups across the columns
+    unsigned col_blocks = 0;  // 256-byte column blocks
+    unsigned group_rows = 16; // row groups per column block (1, 4 or 16)
     unsigned splits = 1;      // workgroups along the rows (S)
     size_t rows_per_split = 0;
     size_t partial_bytes = 0; // S * C * 4 when S > 1
+    unsigned narrow_w = 0;    // 16-byte vectors per row when the narrow-row kernel runs, else 0
+    unsigned finish_blocks = 0;     // second-pass workgroups (S > 1)
+    unsigned finish_cols_log2 = 0;  // log2 of the columns per second-pass workgroup
 };
-ColprodPlan colprod_plan(ColType t, size_t R, size_t C, const DeviceInfo& dev,
-                         const Workspace& ws);
+ColprodPlan colprod_plan(ColType t, const void* src, size_t R, size_t C, size_t ld,
+                         const DeviceInfo& dev, const Workspace& ws);
 hipError_t launch_colprod(ColType t, const void* src, size_t R, size_t C,
                           size_t ld, void* dst, const ColprodPlan& plan,
                           const Workspace& ws, hipStream_t stream);

@@ -1,0 +1,199 @@
+"""GPU parity of the column reductions on narrow rows, on short and wide
+tiles, and of the second pass over many row slices.
+
+Rows narrower than 256 bytes whose start, stride and valid width are
+multiples of 16 bytes take the narrow-row kernel: a workgroup reads whole
+rows (W = ld * size / 16 vectors per row, 256 / W rows per step) and walks
+its sweeps grid-stride.  The cases cover every W from 1 to 15 for 4-byte
+and 2-byte elements, padding vectors past C (filled with NaN, never read),
+row counts that end inside a step and inside a sweep, and counts large
+enough for hundreds of workgroups and a second pass.  Products over long
+columns use factors +-1 with rare +-2 and +-0.5, so that the exact product
+stays in range and every order of multiplication gives it exactly.
+
+Short, wide tiles (thousands of 256-byte column blocks) give a workgroup
+several adjacent column blocks with 4 or 1 row groups each; the cases
+cover both, with a block count that leaves the last workgroup part empty,
+a ragged last block, and unaligned rows.
+
+The second pass spreads each column's S partial rows over the threads of
+a workgroup; the cases below put S from 2 to 256 against column counts from
+1 to a few thousand on both kernels."""
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from gpu_helpers import COLPROD_16_TOL, COLPROD_F32_TOL, check_rel, dev, host, say
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def red():
+    import fp32_reductions_amd as red
+    return red
+
+
+@pytest.fixture(scope="module")
+def orc():
+    return oracle.get()
+
+
+def pow2_factors(seed, shape, rare):
+    """+-1 with rare +-2 and +-0.5 (probability `rare` each)."""
+    rng = np.random.default_rng(seed)
+    u = rng.random(shape)
+    v = np.where(u < rare, 2.0, np.where(u < 2 * rare, 0.5, 1.0))
+    v = v * np.where(rng.random(shape) < 0.5, -1.0, 1.0)
+    return v.astype(np.float32)
+
+
+def tile_f32(seed, R, C, ld, kind, rare=2e-4):
+    x = np.full((R, ld), np.nan, np.float32)
+    if kind == "prod":
+        x[:, :C] = pow2_factors(seed, (R, C), rare)
+    else:
+        x[:, :C] = workloads.uniform_f32(seed, R * C).reshape(R, C)
+    return x
+
+
+def colprod_case(red, orc, kind, R, C, ld, seed):
+    what = "colprod %s R=%d C=%d ld=%d" % (kind, R, C, ld)
+    say(what)
+    if kind == "i32":
+        # odd factors: the product mod 2^32 stays odd, so every row counts
+        src = workloads.integers_i32(seed, R * ld, -(2 ** 31), 2 ** 31).reshape(R, ld) | 1
+        out = torch.zeros(C, dtype=torch.int32, device="cuda")
+        red.colprod_i32(dev(src), out, C=C)
+        got = host(out)
+        want = orc.colprod_i32(src, R, C, ld)
+        bad = np.nonzero(got != want)[0]
+        assert bad.size == 0, "%s: column %d" % (what, bad[0])
+        return
+    # binary16 keeps exponents -14..15: long columns get rarer powers of two
+    rare = 2e-5 if kind == "f16" and R > 4096 else 2e-4
+    x = tile_f32(seed, R, C, ld, "prod", rare)
+    if kind == "f32":
+        out = torch.zeros(C, dtype=torch.float32, device="cuda")
+        red.colprod_f32(dev(x), out, C=C)
+        check_rel(host(out), orc.colprod_f32(x, R, C, ld), COLPROD_F32_TOL, what)
+        return
+    bits = (workloads.to_f16_bits if kind == "f16" else workloads.to_bf16_bits)(x.reshape(-1))
+    bits = bits.reshape(R, ld)
+    tdt = torch.float16 if kind == "f16" else torch.bfloat16
+    out = torch.zeros(C, dtype=tdt, device="cuda")
+    getattr(red, "colprod_" + kind)(dev(bits.view(np.int16)).view(tdt), out, C=C)
+    want = (orc.colprod_f16 if kind == "f16" else orc.colprod_bf16)(bits, R, C, ld)
+    check_rel(host(out.float()), want, COLPROD_16_TOL, what)
+
+
+def cols_case(red, orc, op, R, C, ld, accum, seed):
+    what = "cols %s R=%d C=%d ld=%d accum=%d" % (op, R, C, ld, accum)
+    say(what)
+    x = tile_f32(seed, R, C, ld, op)
+    old = workloads.uniform_f32(seed + 1, C, -3.0, 3.0)
+    out = dev(old.copy())
+    getattr(red, op + "_cols_f32")(dev(x), out, C=C, accum=accum)
+    got = host(out)
+    if op == "sum":
+        s, a = orc.cols_sum_f32(x, R, C, ld, accum, old)
+        assert (np.abs(got.astype(np.float64) - s) <= 1e-6 * a).all(), what
+    else:
+        want = getattr(orc, "cols_%s_f32" % op)(x, R, C, ld, accum, old)
+        eq = (got.view(np.uint32) == want.view(np.uint32)) | ((got == 0) & (want == 0))
+        assert eq.all(), what
+
+
+# (W vectors per row, valid vectors, rows): rows end inside a step, inside
+# a sweep, and after many sweeps (S up to twice the compute units).
+NARROW = [
+    (1, 1, 1), (1, 1, 255), (1, 1, 2049), (1, 1, 600_000),
+    (2, 2, 130), (2, 1, 40_000),
+    (3, 3, 85), (3, 2, 3 * 2048 + 5),
+    (4, 4, 64 * 8 + 63), (4, 3, 200_000),
+    (5, 5, 51 * 8 * 3 + 50), (6, 6, 42 * 8 * 7), (6, 1, 70_000),
+    (7, 7, 36 * 8 * 5 + 1), (8, 8, 100_001), (8, 5, 9),
+    (9, 9, 28 * 8 * 3 + 27), (10, 10, 25 * 8 + 24), (11, 7, 23 * 8 * 2 + 1),
+    (12, 12, 21 * 8 * 9 + 20), (13, 13, 19 * 8 * 4 + 3), (14, 14, 40_000),
+    (15, 15, 17 * 8 * 11 + 16), (15, 2, 17),
+]
+
+
+@pytest.mark.parametrize("kind", ["f32", "i32"])
+@pytest.mark.parametrize("W,valid,R", NARROW)
+def test_narrow_4byte(red, orc, kind, W, valid, R):
+    colprod_case(red, orc, kind, R, 4 * valid, 4 * W, 500 + W)
+
+
+@pytest.mark.parametrize("kind", ["f16", "bf16"])
+@pytest.mark.parametrize("W,valid,R", NARROW)
+def test_narrow_2byte(red, orc, kind, W, valid, R):
+    colprod_case(red, orc, kind, min(R, 60_000), 8 * valid, 8 * W, 600 + W)
+
+
+@pytest.mark.parametrize("op", ["sum", "max", "min"])
+@pytest.mark.parametrize("W,valid,R", [(1, 1, 300_001), (4, 4, 5000), (5, 3, 70_000),
+                                       (8, 8, 63), (15, 15, 100_000)])
+@pytest.mark.parametrize("accum", [0, 1])
+def test_narrow_cols(red, orc, op, W, valid, R, accum):
+    cols_case(red, orc, op, R, 4 * valid, 4 * W, accum, 700 + W)
+
+
+# Second pass: (R, C, ld) with ld * 4 not a multiple of 16 (column-block
+# kernel) or C of a few 16-byte vectors (narrow kernel), spanning S from 2
+# to 256 and column counts on both sides of each power of two.
+FINISH = [
+    (4096, 1, 1), (100_000, 1, 3), (50_000, 3, 5), (70_000, 17, 17),
+    (40_000, 64, 65), (20_000, 255, 255), (8192, 257, 257), (5000, 1000, 1001),
+    (3000, 4099, 4099), (100_000, 16, 16), (60_000, 64, 64),
+]
+
+
+@pytest.mark.parametrize("R,C,ld", FINISH)
+@pytest.mark.parametrize("kind", ["f32", "i32"])
+def test_second_pass_products(red, orc, kind, R, C, ld):
+    colprod_case(red, orc, kind, R, C, ld, 800 + C)
+
+
+@pytest.mark.parametrize("R,C,ld", FINISH)
+@pytest.mark.parametrize("op", ["sum", "max", "min"])
+def test_second_pass_cols(red, orc, op, R, C, ld):
+    cols_case(red, orc, op, R, C, ld, 1, 900 + C)
+
+
+# Short, wide tiles: (R, C, ld).  For 4-byte elements, 1021 or more
+# column blocks give 4 row groups per block, 4081 or more give 1.
+WIDE = [
+    (37, 65536, 65536), (5, 131172, 131172), (7, 70001, 70002), (33, 80000, 80001),
+    (3, 300_000, 300_000), (16, 262_144, 262_144), (1, 1_000_003, 1_000_004),
+    (9, 300_001, 300_005), (2, 400_000, 400_001),
+]
+
+
+@pytest.mark.parametrize("R,C,ld", WIDE)
+@pytest.mark.parametrize("kind", ["f32", "i32"])
+def test_wide_4byte(red, orc, kind, R, C, ld):
+    colprod_case(red, orc, kind, R, C, ld, 1000 + R)
+
+
+# 2-byte elements: 2041 or more blocks of 128 columns give 4 row groups
+# per block, 8161 or more give 1.
+WIDE16 = [(20, 262_144, 262_144), (6, 270_000, 270_003), (4, 1_100_000, 1_100_008),
+          (11, 1_050_001, 1_050_001)]
+
+
+@pytest.mark.parametrize("R,C,ld", WIDE16)
+@pytest.mark.parametrize("kind", ["f16", "bf16"])
+def test_wide_2byte(red, orc, kind, R, C, ld):
+    colprod_case(red, orc, kind, R, C, ld, 1100 + R)
+
+
+@pytest.mark.parametrize("R,C,ld", [(37, 65536, 65536), (7, 70001, 70002),
+                                    (3, 300_000, 300_000), (9, 300_001, 300_005)])
+@pytest.mark.parametrize("op", ["sum", "max", "min"])
+@pytest.mark.parametrize("accum", [0, 1])
+def test_wide_cols(red, orc, op, R, C, ld, accum):
+    cols_case(red, orc, op, R, C, ld, accum, 1200 + R)
