@@ -21,10 +21,11 @@
 //    partial row in the workspace, and a second kernel combines the S
 //    partial rows of each column in a fixed order (strided runs per thread,
 //    then a pairwise tree in LDS), narrows once to T and writes dst;
-//  * rows narrower than 256 bytes (16-byte aligned, with C * sizeof(T) a
-//    multiple of 16) would leave most of those lanes idle: a narrow-row
-//    kernel reads whole rows instead, 256 / W rows of W vectors per step,
-//    each workgroup walking sweeps of eight steps grid-stride;
+//  * rows narrower than 256 bytes would leave most of those lanes idle: a
+//    narrow-row kernel reads whole rows instead, 256 / W rows of W units
+//    per step (16-byte vectors when the tile is aligned and C * sizeof(T) is
+//    a multiple of 16, else elements), each workgroup walking sweeps of
+//    eight steps grid-stride;
 //  * tile loads are non-temporal: each element is read once.
 //
 // Column sum / max / min of an fp32 tile reduce each column by the TVM
@@ -47,6 +48,16 @@ namespace {
 #endif
 constexpr int kRowsInFlight = RED_COLPROD_UNROLL; // 16-byte loads in flight per lane
 constexpr int kLanesPerRow = 16;                  // lanes sharing one row of a column block
+// Narrow rows read in elements: bytes each lane keeps in flight (16 loads
+// of 4-byte elements, 32 of 2-byte ones).  Measured on MI355X with
+// 256 MiB fp32 tiles of 1 to 63 columns: 16 loads per lane at 2 workgroups
+// per CU (32 KiB in flight per CU) streamed at 5.8-6.1 TB/s; 8 loads gave
+// 4.5-4.8 TB/s, and 64 KiB per CU (32 loads, or 8 workgroups per CU) less.
+#ifndef RED_COLPROD_ELEM_BYTES_IN_FLIGHT
+#define RED_COLPROD_ELEM_BYTES_IN_FLIGHT 64
+#endif
+template <class T>
+constexpr int kElemRowsInFlight = RED_COLPROD_ELEM_BYTES_IN_FLIGHT / (int)sizeof(T);
 
 struct TraitsF32 {
     using T = float;
@@ -322,18 +333,21 @@ __global__ __launch_bounds__(kBlock) void colred_kernel(
     }
 }
 
-// Narrow rows (a row of ld elements spans W < 16 aligned 16-byte vectors,
-// and C * sizeof(T) is a multiple of 16): the column-block layout above
-// would leave most lanes idle, so a workgroup reads whole rows instead.
-// Thread t owns vector cv = t % W of row offset ro = t / W; RB = 256 / W
-// rows form one step, read as RB * W consecutive vectors (threads past
-// RB * W and vectors of padding columns stay idle).  Steps are taken eight
-// at a time as sweeps of 8 * RB rows, and workgroup s walks sweeps s,
-// s + S, s + 2S, ... (grid-stride, as the 1-D stream).  Each thread folds
-// its rows in increasing order; the RB row offsets are then combined in LDS
-// by a fixed pairwise tree, and the RB threads of row offset 0 store the
-// workgroup's partial row (or dst when S == 1).
-template <class Tr, class Op>
+// Narrow rows (a row narrower than 256 bytes): the column-block layout
+// above would leave most lanes idle, so a workgroup reads whole rows
+// instead.  The unit a thread reads per row is one aligned 16-byte vector
+// of V elements when VEC (tile 16-byte aligned, ld * sizeof(T) and
+// C * sizeof(T) multiples of 16), else one element; a row is W units.
+// Thread t owns unit cu = t % W of row offset ro = t / W; RB = 256 / W rows
+// form one step, read as RB * W consecutive units (threads past RB * W and
+// units of padding columns stay idle).  Steps are taken NF at a time as
+// sweeps of NF * RB rows (NF = 8 vector rows, or 64 bytes of element rows
+// per lane), and workgroup s walks sweeps s, s + S, s + 2S, ... (grid-
+// stride, as the 1-D stream).  Each thread folds its rows in
+// increasing order; the RB row offsets are then combined in LDS by a fixed
+// pairwise tree, and the threads of row offset 0 store the workgroup's
+// partial row (or dst when S == 1).
+template <class Tr, class Op, bool VEC>
 __global__ __launch_bounds__(kBlock) void colred_narrow_kernel(
     const typename Tr::T* __restrict__ src, uint64_t R, uint64_t C,
     uint64_t ld, uint32_t W, typename Tr::T* __restrict__ dst,
@@ -341,55 +355,74 @@ __global__ __launch_bounds__(kBlock) void colred_narrow_kernel(
 {
     using T = typename Tr::T;
     using A = typename Tr::A;
-    constexpr int V = Tr::V;
+    constexpr int U = VEC ? Tr::V : 1; // elements per unit
+    constexpr int NF = VEC ? kRowsInFlight : kElemRowsInFlight<T>; // rows in flight
 
-    __shared__ A lds[kBlock][V];
+    __shared__ A lds[kBlock][U];
 
     const uint32_t RB = kBlock / W;
     const uint32_t t = threadIdx.x;
     const uint32_t ro = t / W;
-    const uint32_t cv = t - ro * W;
-    const bool live = ro < RB && (uint64_t)cv * V < C;
+    const uint32_t cu = t - ro * W;
+    const bool live = ro < RB && (uint64_t)cu * U < C;
     const uint32_t S = gridDim.x;
     const uint64_t s = blockIdx.x;
 
-    A acc[V];
+    A acc[U];
 #pragma unroll
-    for (int k = 0; k < V; ++k)
+    for (int k = 0; k < U; ++k)
         acc[k] = Op::identity();
 
+    auto fold_row = [&](const T* p) {
+        if constexpr (VEC) {
+            A a[U];
+            Tr::unpack(load_stream(reinterpret_cast<const uint4*>(p)), a);
+#pragma unroll
+            for (int k = 0; k < U; ++k)
+                acc[k] = Op::apply(acc[k], a[k]);
+        } else {
+            acc[0] = Op::apply(acc[0], Tr::widen(__builtin_nontemporal_load(p)));
+        }
+    };
+
     if (live) {
-        const T* __restrict__ col = src + (uint64_t)cv * V;
-        const uint64_t sweep = (uint64_t)kRowsInFlight * RB;
+        const T* __restrict__ col = src + (uint64_t)cu * U;
+        const uint64_t sweep = (uint64_t)NF * RB;
         uint64_t r = s * sweep + ro;
-        for (; r + (uint64_t)(kRowsInFlight - 1) * RB < R; r += (uint64_t)S * sweep) {
-            uint4 v[kRowsInFlight];
+        for (; r + (uint64_t)(NF - 1) * RB < R; r += (uint64_t)S * sweep) {
+            if constexpr (VEC) {
+                uint4 v[NF];
 #pragma unroll
-            for (int u = 0; u < kRowsInFlight; ++u)
-                v[u] = load_stream(reinterpret_cast<const uint4*>(
-                    col + (r + (uint64_t)u * RB) * ld));
-            __builtin_amdgcn_sched_barrier(0);
+                for (int u = 0; u < NF; ++u)
+                    v[u] = load_stream(reinterpret_cast<const uint4*>(
+                        col + (r + (uint64_t)u * RB) * ld));
+                __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int u = 0; u < kRowsInFlight; ++u) {
-                A a[V];
-                Tr::unpack(v[u], a);
+                for (int u = 0; u < NF; ++u) {
+                    A a[U];
+                    Tr::unpack(v[u], a);
 #pragma unroll
-                for (int k = 0; k < V; ++k)
-                    acc[k] = Op::apply(acc[k], a[k]);
+                    for (int k = 0; k < U; ++k)
+                        acc[k] = Op::apply(acc[k], a[k]);
+                }
+            } else {
+                T v[NF];
+#pragma unroll
+                for (int u = 0; u < NF; ++u)
+                    v[u] = __builtin_nontemporal_load(col + (r + (uint64_t)u * RB) * ld);
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int u = 0; u < NF; ++u)
+                    acc[0] = Op::apply(acc[0], Tr::widen(v[u]));
             }
         }
         // The sweep that reaches past R (if it is this workgroup's) is the
         // last one: its remaining rows are read one step at a time.
-        for (; r < R; r += RB) {
-            A a[V];
-            Tr::unpack(load_stream(reinterpret_cast<const uint4*>(col + r * ld)), a);
-#pragma unroll
-            for (int k = 0; k < V; ++k)
-                acc[k] = Op::apply(acc[k], a[k]);
-        }
+        for (; r < R; r += RB)
+            fold_row(col + r * ld);
     }
 #pragma unroll
-    for (int k = 0; k < V; ++k)
+    for (int k = 0; k < U; ++k)
         lds[t][k] = acc[k];
 
     uint32_t half = 1;
@@ -399,7 +432,7 @@ __global__ __launch_bounds__(kBlock) void colred_narrow_kernel(
         __syncthreads();
         if (ro < half && ro + half < RB) {
 #pragma unroll
-            for (int k = 0; k < V; ++k)
+            for (int k = 0; k < U; ++k)
                 lds[t][k] = Op::apply(lds[t][k], lds[t + half * W][k]);
         }
     }
@@ -407,8 +440,8 @@ __global__ __launch_bounds__(kBlock) void colred_narrow_kernel(
 
     if (ro == 0 && live) {
 #pragma unroll
-        for (int k = 0; k < V; ++k) {
-            const uint64_t j = (uint64_t)cv * V + k;
+        for (int k = 0; k < U; ++k) {
+            const uint64_t j = (uint64_t)cu * U + k;
             const A p = lds[t][k];
             if (S == 1)
                 dst[j] = Tr::narrow(accum ? Op::apply(Tr::widen(dst[j]), p) : p);
@@ -481,8 +514,12 @@ hipError_t launch_typed(const void* src, size_t R, size_t C, size_t ld,
     T* d = static_cast<T*>(dst);
     A* part = static_cast<A*>(ws.partials);
     if (plan.narrow_w) {
-        colred_narrow_kernel<Tr, Op><<<plan.splits, kBlock, 0, stream>>>(
-            s, R, C, ld, plan.narrow_w, d, part, accum);
+        if (plan.narrow_vec)
+            colred_narrow_kernel<Tr, Op, true><<<plan.splits, kBlock, 0, stream>>>(
+                s, R, C, ld, plan.narrow_w, d, part, accum);
+        else
+            colred_narrow_kernel<Tr, Op, false><<<plan.splits, kBlock, 0, stream>>>(
+                s, R, C, ld, plan.narrow_w, d, part, accum);
     } else {
         const unsigned per_wg = kBlock / kLanesPerRow / plan.group_rows;
         const dim3 grid((plan.col_blocks + per_wg - 1) / per_wg, plan.splits);
@@ -518,6 +555,10 @@ constexpr uint64_t kMaxSplits = 65535; // gridDim.y limit
 #define RED_COLPROD_NARROW_WG_PER_CU 2
 #endif
 constexpr uint64_t kNarrowWgPerCu = RED_COLPROD_NARROW_WG_PER_CU;
+#ifndef RED_COLPROD_NARROW_ELEM_WG_PER_CU
+#define RED_COLPROD_NARROW_ELEM_WG_PER_CU 2
+#endif
+constexpr uint64_t kNarrowElemWgPerCu = RED_COLPROD_NARROW_ELEM_WG_PER_CU;
 // Row groups per column block, from the fewest the planner may choose
 // (1, 4 or 16).
 #ifndef RED_COLPROD_MIN_GROUP_ROWS
@@ -535,15 +576,18 @@ ColprodPlan colprod_plan(ColType t, const void* src, size_t R, size_t C, size_t 
     const uint64_t es = colprod_elem_size(t);
     const bool vec = (((uintptr_t)src & 15u) == 0) && ((ld * es) % 16 == 0);
     uint64_t S = 1;
-    if (vec && (C * es) % 16 == 0 && ld * es < (uint64_t)kLanesPerRow * 16) {
-        // Narrow rows: one workgroup spans whole rows; the grid-stride walk
+    if (ld * es < (uint64_t)kLanesPerRow * 16) {
+        // Narrow rows: one workgroup spans whole rows, in 16-byte vectors
+        // when the tile allows, else in elements; the grid-stride walk
         // covers every sweep whatever S is.
-        p.narrow_w = (unsigned)(ld * es / 16);
+        p.narrow_vec = vec && (C * es) % 16 == 0;
+        p.narrow_w = (unsigned)(p.narrow_vec ? ld * es / 16 : ld);
         p.col_blocks = 1;
         const uint64_t rows_per_step = kBlock / p.narrow_w;
-        const uint64_t sweep = rows_per_step * kRowsInFlight;
+        const uint64_t sweep = rows_per_step *
+            (p.narrow_vec ? kRowsInFlight : RED_COLPROD_ELEM_BYTES_IN_FLIGHT / es);
         const uint64_t sweeps = (R + sweep - 1) / sweep;
-        S = (uint64_t)dev.cus * kNarrowWgPerCu;
+        S = (uint64_t)dev.cus * (p.narrow_vec ? kNarrowWgPerCu : kNarrowElemWgPerCu);
         if (S > sweeps)
             S = sweeps;
         while (S > 1 && S * C * 4 > ws.partial_bytes)

@@ -76,7 +76,8 @@ struct ColprodPlan {
     unsigned splits = 1;      // workgroups along the rows (S)
     size_t rows_per_split = 0;
     size_t partial_bytes = 0; // S * C * 4 when S > 1
-    unsigned narrow_w = 0;    // 16-byte vectors per row when the narrow-row kernel runs, else 0
+    unsigned narrow_w = 0;    // units per row when the narrow-row kernel runs, else 0
+    bool narrow_vec = false;  // its unit: a 16-byte vector (true) or one element
     unsigned finish_blocks = 0;     // second-pass workgroups (S > 1)
     unsigned finish_cols_log2 = 0;  // log2 of the columns per second-pass workgroup
 };

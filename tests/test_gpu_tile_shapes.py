@@ -1,13 +1,15 @@
 """GPU parity of the column reductions on narrow rows, on short and wide
 tiles, and of the second pass over many row slices.
 
-Rows narrower than 256 bytes whose start, stride and valid width are
-multiples of 16 bytes take the narrow-row kernel: a workgroup reads whole
-rows (W = ld * size / 16 vectors per row, 256 / W rows per step) and walks
-its sweeps grid-stride.  The cases cover every W from 1 to 15 for 4-byte
-and 2-byte elements, padding vectors past C (filled with NaN, never read),
-row counts that end inside a step and inside a sweep, and counts large
-enough for hundreds of workgroups and a second pass.  Products over long
+Rows narrower than 256 bytes take the narrow-row kernel: a workgroup
+reads whole rows (W units per row, 256 / W rows per step) and walks its
+sweeps grid-stride.  The unit is a 16-byte vector when the start, stride
+and valid width are multiples of 16 bytes, else one element.  The cases
+cover every vector width W from 1 to 15 for 4-byte and 2-byte elements,
+element rows of 1 to 127 elements with misaligned starts, padding past C
+(filled with NaN, never read), row counts that end inside a step and
+inside a sweep, and counts large enough for hundreds of workgroups and a
+second pass.  Products over long
 columns use factors +-1 with rare +-2 and +-0.5, so that the exact product
 stays in range and every order of multiplication gives it exactly.
 
@@ -60,14 +62,22 @@ def tile_f32(seed, R, C, ld, kind, rare=2e-4):
     return x
 
 
-def colprod_case(red, orc, kind, R, C, ld, seed):
-    what = "colprod %s R=%d C=%d ld=%d" % (kind, R, C, ld)
+def dev_at(a, off):
+    """Upload a host tile so that it starts `off` elements into a larger
+    device buffer (off = 0: the buffer's own 256-byte-aligned start)."""
+    flat = np.zeros(a.size + off, a.dtype)
+    flat[off:] = a.reshape(-1)
+    return dev(flat)[off:].view(*a.shape)
+
+
+def colprod_case(red, orc, kind, R, C, ld, seed, off=0):
+    what = "colprod %s R=%d C=%d ld=%d off=%d" % (kind, R, C, ld, off)
     say(what)
     if kind == "i32":
         # odd factors: the product mod 2^32 stays odd, so every row counts
         src = workloads.integers_i32(seed, R * ld, -(2 ** 31), 2 ** 31).reshape(R, ld) | 1
         out = torch.zeros(C, dtype=torch.int32, device="cuda")
-        red.colprod_i32(dev(src), out, C=C)
+        red.colprod_i32(dev_at(src, off), out, C=C)
         got = host(out)
         want = orc.colprod_i32(src, R, C, ld)
         bad = np.nonzero(got != want)[0]
@@ -78,25 +88,25 @@ def colprod_case(red, orc, kind, R, C, ld, seed):
     x = tile_f32(seed, R, C, ld, "prod", rare)
     if kind == "f32":
         out = torch.zeros(C, dtype=torch.float32, device="cuda")
-        red.colprod_f32(dev(x), out, C=C)
+        red.colprod_f32(dev_at(x, off), out, C=C)
         check_rel(host(out), orc.colprod_f32(x, R, C, ld), COLPROD_F32_TOL, what)
         return
     bits = (workloads.to_f16_bits if kind == "f16" else workloads.to_bf16_bits)(x.reshape(-1))
     bits = bits.reshape(R, ld)
     tdt = torch.float16 if kind == "f16" else torch.bfloat16
     out = torch.zeros(C, dtype=tdt, device="cuda")
-    getattr(red, "colprod_" + kind)(dev(bits.view(np.int16)).view(tdt), out, C=C)
+    getattr(red, "colprod_" + kind)(dev_at(bits.view(np.int16), off).view(tdt), out, C=C)
     want = (orc.colprod_f16 if kind == "f16" else orc.colprod_bf16)(bits, R, C, ld)
     check_rel(host(out.float()), want, COLPROD_16_TOL, what)
 
 
-def cols_case(red, orc, op, R, C, ld, accum, seed):
-    what = "cols %s R=%d C=%d ld=%d accum=%d" % (op, R, C, ld, accum)
+def cols_case(red, orc, op, R, C, ld, accum, seed, off=0):
+    what = "cols %s R=%d C=%d ld=%d accum=%d off=%d" % (op, R, C, ld, accum, off)
     say(what)
     x = tile_f32(seed, R, C, ld, op)
     old = workloads.uniform_f32(seed + 1, C, -3.0, 3.0)
     out = dev(old.copy())
-    getattr(red, op + "_cols_f32")(dev(x), out, C=C, accum=accum)
+    getattr(red, op + "_cols_f32")(dev_at(x, off), out, C=C, accum=accum)
     got = host(out)
     if op == "sum":
         s, a = orc.cols_sum_f32(x, R, C, ld, accum, old)
@@ -142,9 +152,42 @@ def test_narrow_cols(red, orc, op, W, valid, R, accum):
     cols_case(red, orc, op, R, 4 * valid, 4 * W, accum, 700 + W)
 
 
-# Second pass: (R, C, ld) with ld * 4 not a multiple of 16 (column-block
-# kernel) or C of a few 16-byte vectors (narrow kernel), spanning S from 2
-# to 256 and column counts on both sides of each power of two.
+# Narrow rows read in elements (rows narrower than 256 bytes whose start,
+# stride or valid width is not a multiple of 16 bytes): (R, C, ld, off).
+NARROW_ELEM = [
+    (1, 1, 1, 0), (100_000, 15, 15, 0), (70_000, 1, 3, 0), (5000, 63, 63, 1),
+    (3001, 33, 40, 3), (40_000, 16, 16, 2), (20_000, 30, 32, 0), (257, 7, 9, 1),
+    (300_000, 2, 2, 0), (12_345, 40, 60, 0),
+]
+
+
+@pytest.mark.parametrize("kind", ["f32", "i32", "f16", "bf16"])
+@pytest.mark.parametrize("R,C,ld,off", NARROW_ELEM)
+def test_narrow_elements(red, orc, kind, R, C, ld, off):
+    colprod_case(red, orc, kind, min(R, 60_000) if kind in ("f16", "bf16") else R,
+                 C, ld, 1300 + C, off)
+
+
+NARROW16_ELEM = [(9999, 127, 127, 0), (4000, 100, 120, 1), (50_000, 9, 9, 0)]
+
+
+@pytest.mark.parametrize("kind", ["f16", "bf16"])
+@pytest.mark.parametrize("R,C,ld,off", NARROW16_ELEM)
+def test_narrow_elements_2byte(red, orc, kind, R, C, ld, off):
+    colprod_case(red, orc, kind, R, C, ld, 1400 + C, off)
+
+
+@pytest.mark.parametrize("op", ["sum", "max", "min"])
+@pytest.mark.parametrize("R,C,ld,off", [(100_000, 15, 15, 0), (5000, 63, 63, 1),
+                                        (3001, 33, 40, 3), (300_000, 2, 2, 0)])
+@pytest.mark.parametrize("accum", [0, 1])
+def test_narrow_elements_cols(red, orc, op, R, C, ld, off, accum):
+    cols_case(red, orc, op, R, C, ld, accum, 1500 + C, off)
+
+
+# Second pass: (R, C, ld) on the column-block kernel (rows of 256 bytes or
+# more) and on both forms of the narrow-row kernel, spanning S from 2 to a
+# few hundred and column counts on both sides of each power of two.
 FINISH = [
     (4096, 1, 1), (100_000, 1, 3), (50_000, 3, 5), (70_000, 17, 17),
     (40_000, 64, 65), (20_000, 255, 255), (8192, 257, 257), (5000, 1000, 1001),
