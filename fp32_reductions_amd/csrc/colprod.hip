@@ -15,7 +15,9 @@
 //  * a workgroup (256 threads = 16 row groups of 16 lanes) covers one block
 //    of 16*V columns and a slice of rows; its row groups take interleaved
 //    rows of the slice and combine their partial products in LDS in
-//    row-group order;
+//    row-group order.  Short, wide tiles, whose blocks alone would give
+//    thousands of short-lived workgroups, put 4 or 16 adjacent blocks in a
+//    workgroup instead, with 4 or 1 row groups each;
 //  * when the grid needs more workgroups than there are column blocks, the
 //    rows are split into S slices (blockIdx.y); each workgroup stores its
 //    partial row in the workspace, and a second kernel combines the S
@@ -25,7 +27,7 @@
 //    narrow-row kernel reads whole rows instead, 256 / W rows of W units
 //    per step (16-byte vectors when the tile is aligned and C * sizeof(T) is
 //    a multiple of 16, else elements), each workgroup walking sweeps of
-//    eight steps grid-stride;
+//    several steps grid-stride;
 //  * tile loads are non-temporal: each element is read once.
 //
 // Column sum / max / min of an fp32 tile reduce each column by the TVM

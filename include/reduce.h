@@ -195,8 +195,9 @@ int red_min_cols_f32(const float* src, size_t R, size_t C, size_t ld,
  *          final product is rounded once to T (round to nearest even).
  * i32    : products wrap modulo 2^32 (two's complement); bit-exact.
  *
- * Deterministic: the row range is split over workgroups in a fixed way and
- * the partial products are multiplied in index order.
+ * Deterministic: for a given shape, alignment and device, the rows are
+ * split over workgroups in a fixed way and the partial products are
+ * combined in a fixed order, so repeated calls give identical bits.
  * ------------------------------------------------------------------- */
 int red_colprod_f32(const float* src, size_t R, size_t C, size_t ld,
                     float* dst, red_stream_t stream);
