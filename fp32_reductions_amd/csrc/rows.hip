@@ -1,10 +1,13 @@
 // rows.hip -- segmented reduction: out[r] = reduce(x[r*ld .. r*ld + n)).
 //
-// Four kernels, picked by the host from (rows, n) and the CU count alone, so
+// Kernels picked by the host from (rows, n) and the CU count alone, so
 // that a given problem on a given device always runs the same code and
 // gives the same bits:
 //
-//  * rows_thread (n <= 16) / rows_tile (16 < n <= 64): one thread per row
+//  * rows_short (n <= 4): eight rows per thread per step, all their loads
+//    issued together, over a grid of a few workgroups per CU; each row in
+//    the same order as rows_thread;
+//  * rows_thread (4 < n <= 16) / rows_tile (16 < n <= 64): one thread per row
 //    (rows of 17 to 64 elements first staged in LDS 128 at a time with
 //    coalesced loads), running the thread-scope
 //    algorithm of the TVM TIRx page "reduction -> sm100_packed" (section
@@ -63,6 +66,19 @@ __device__ __forceinline__ void load8(const float* __restrict__ p, float v[8])
     }
 }
 
+// The page's collapse of the eight sum slots: (0,1) += (2,3),
+// (4,5) += (6,7), (0,1) += (4,5), result = slot 0 + slot 1.
+__device__ __forceinline__ float slot_tree(float s[8])
+{
+    s[0] = s[0] + s[2];
+    s[1] = s[1] + s[3];
+    s[4] = s[4] + s[6];
+    s[5] = s[5] + s[7];
+    s[0] = s[0] + s[4];
+    s[1] = s[1] + s[5];
+    return s[0] + s[1];
+}
+
 template <bool VEC>
 __device__ __forceinline__ float page_sum(const float* __restrict__ p,
                                           uint32_t n, int accum, float old)
@@ -90,13 +106,7 @@ __device__ __forceinline__ float page_sum(const float* __restrict__ p,
     for (uint32_t k = 0; k < 8; ++k)
         if (c + k < n)
             s[k] = s[k] + p[c + k];
-    s[0] = s[0] + s[2];
-    s[1] = s[1] + s[3];
-    s[4] = s[4] + s[6];
-    s[5] = s[5] + s[7];
-    s[0] = s[0] + s[4];
-    s[1] = s[1] + s[5];
-    return s[0] + s[1];
+    return slot_tree(s);
 }
 
 template <class Op, bool VEC>
@@ -132,6 +142,84 @@ __global__ __launch_bounds__(kBlock) void rows_thread_kernel(
             out[r] = page_sum<VEC>(p, n, accum, old);
         else
             out[r] = page_minmax<Op, VEC>(p, n, accum, old);
+    }
+}
+
+// Rows of N < 8 elements, already in registers: the arithmetic page_sum
+// and page_minmax apply to such rows.  Each element sits alone in its
+// slot (slot 0 also takes the old value under accum) before the slot tree;
+// max / min fold the elements one by one.
+template <class Op, int N, bool ACC>
+__device__ __forceinline__ float short_row(const float v[N], float old)
+{
+    if constexpr (__is_same(Op, OpSum)) {
+        float s[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+            s[k] = (k < N) ? v[k < N ? k : 0] : -0.0f;
+        if (ACC)
+            s[0] = s[0] + old;
+        return slot_tree(s);
+    } else {
+        AccMinMax<Op> acc(ACC ? old : Op::identity());
+#pragma unroll
+        for (int k = 0; k < N; ++k)
+            acc.fold_scalar(v[k]);
+        return acc.collapse();
+    }
+}
+
+#ifndef RED_ROWS_SHORT_PER_THREAD
+#define RED_ROWS_SHORT_PER_THREAD 8
+#endif
+#ifndef RED_ROWS_SHORT_WG_PER_CU
+#define RED_ROWS_SHORT_WG_PER_CU 8
+#endif
+constexpr int kShortRowsPerThread = RED_ROWS_SHORT_PER_THREAD;
+constexpr uint64_t kShortWgPerCu = RED_ROWS_SHORT_WG_PER_CU;
+constexpr uint64_t kShortRowMax = 4; // rows this short take the short-row kernel
+
+// Rows of N = 1 to 4 elements.  One row per thread would give each
+// workgroup a few KiB to read and the grid hundreds of thousands of
+// workgroups; instead each thread takes kShortRowsPerThread rows per step
+// (rows base, base + 256, ..., so that every load instruction of a wave
+// reads 64 neighbouring rows), requests all their elements (and, under
+// accum, their old values) before reducing any, and a grid of a few
+// workgroups per CU walks the steps grid-stride.  N and accum are template
+// parameters, so that the loads of a step form one straight run.
+// (Measured on MI355X, row sums over 256 MiB from HBM: 1-element rows
+// 80 us instead of 175 us one row per thread, 2 to 4 elements 55-65 us
+// instead of 69-99 us; 5 to 7 elements were ~2 us slower this way than one
+// row per thread, so they stay with rows_thread.  4 and 16 rows per thread,
+// and 2 or 4 workgroups per CU, were no faster.)
+template <class Op, int N, bool ACC>
+__global__ __launch_bounds__(kBlock) void rows_short_kernel(
+    const float* __restrict__ x, uint64_t rows, uint64_t ld,
+    float* __restrict__ out)
+{
+    constexpr int RPT = kShortRowsPerThread;
+    const uint64_t span = (uint64_t)kBlock * RPT;
+    for (uint64_t base = (uint64_t)blockIdx.x * span + threadIdx.x; base < rows;
+         base += (uint64_t)gridDim.x * span) {
+        float v[RPT][N];
+        float old[RPT];
+#pragma unroll
+        for (int j = 0; j < RPT; ++j) {
+            const uint64_t r = base + (uint64_t)j * kBlock;
+            const uint64_t rr = r < rows ? r : base; // a row that exists
+            const float* __restrict__ p = x + rr * ld;
+#pragma unroll
+            for (int k = 0; k < N; ++k)
+                v[j][k] = __builtin_nontemporal_load(p + k);
+            old[j] = ACC ? out[rr] : 0.0f;
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int j = 0; j < RPT; ++j) {
+            const uint64_t r = base + (uint64_t)j * kBlock;
+            if (r < rows)
+                out[r] = short_row<Op, N, ACC>(v[j], old[j]);
+        }
     }
 }
 
@@ -458,7 +546,24 @@ hipError_t launch_rows_op(const float* x, size_t rows, size_t n, size_t ld,
                           float* out, int accum, const DeviceInfo& dev,
                           const Workspace& ws, hipStream_t stream)
 {
-    if (n <= kDirectRowMax) {
+    if (n <= kShortRowMax) {
+        const uint64_t span = (uint64_t)kBlock * kShortRowsPerThread;
+        const uint64_t steps = (rows + span - 1) / span;
+        const uint64_t cap = (uint64_t)dev.cus * kShortWgPerCu;
+        const unsigned grid = (unsigned)(steps < cap ? steps : cap);
+        auto go = [&](auto acc, auto plain) {
+            if (accum)
+                acc<<<grid, kBlock, 0, stream>>>(x, rows, ld, out);
+            else
+                plain<<<grid, kBlock, 0, stream>>>(x, rows, ld, out);
+        };
+        switch (n) {
+        case 1: go(rows_short_kernel<Op, 1, true>, rows_short_kernel<Op, 1, false>); break;
+        case 2: go(rows_short_kernel<Op, 2, true>, rows_short_kernel<Op, 2, false>); break;
+        case 3: go(rows_short_kernel<Op, 3, true>, rows_short_kernel<Op, 3, false>); break;
+        default: go(rows_short_kernel<Op, 4, true>, rows_short_kernel<Op, 4, false>); break;
+        }
+    } else if (n <= kDirectRowMax) {
         const unsigned grid = cap_grid((rows + kBlock - 1) / kBlock);
         const bool vec = (((uintptr_t)x & 15u) == 0) && (ld % 4 == 0);
         if (vec)

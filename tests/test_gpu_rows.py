@@ -132,6 +132,35 @@ def test_rows_shapes(red, orc, rows, n, ld, off):
                        "rows=%d n=%d ld=%d off=%d %s accum=%s" % (rows, n, ld, off, op, accum))
 
 
+# Rows of 1 to 7 elements.  Up to 4 elements: 8 rows per thread and step,
+# a grid of a few workgroups per CU walking 2048-row steps; row counts end
+# inside a step and inside a thread's 8 rows, and the largest need several
+# grid passes.  5 to 7 elements: one row per thread.
+SHORT = [  # (rows, n, ld, element offset of the base pointer)
+    (1, 1, 1, 0), (255, 1, 1, 0), (2049, 1, 1, 1), (3_000_001, 1, 1, 0), (100_000, 1, 4, 2),
+    (257, 2, 2, 0), (1_100_000, 2, 2, 0), (70_001, 2, 3, 1), (4097, 3, 3, 0),
+    (2_500_003, 3, 3, 0), (33_333, 3, 4, 3), (2047, 4, 4, 0), (600_001, 4, 4, 0),
+    (10_000, 4, 5, 1), (9999, 5, 5, 0), (700_007, 5, 8, 0), (6143, 6, 6, 2),
+    (800_000, 6, 6, 0), (2049, 7, 7, 3), (900_001, 7, 7, 0), (12_345, 7, 16, 0),
+]
+
+
+@pytest.mark.parametrize("rows,n,ld,off", SHORT)
+def test_rows_short(red, orc, rows, n, ld, off):
+    say("rows short rows=%d n=%d ld=%d off=%d" % (rows, n, ld, off))
+    flat = workloads.uniform_f32(34, rows * ld + off + 4, -4.0, 4.0)
+    flat[off:off + rows * ld].reshape(rows, ld)[:, n:] = np.nan  # padding
+    fd = dev(flat)
+    x = flat[off:off + rows * ld].reshape(rows, ld)
+    xd = fd[off:off + rows * ld].view(rows, ld)
+    old = workloads.uniform_f32(35, rows, -2.0, 2.0)
+    for op in ("sum", "max", "min"):
+        for accum in (False, True):
+            got = run_rows(red, op, xd, n, old if accum else None, accum)
+            check_rows(orc, op, x, n, got, accum, old if accum else None,
+                       "rows=%d n=%d ld=%d off=%d %s accum=%s" % (rows, n, ld, off, op, accum))
+
+
 def test_rows_empty_untouched(red):
     say("rows empty")
     x = torch.ones((4, 8), dtype=torch.float32, device="cuda")
