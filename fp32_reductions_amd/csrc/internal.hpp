@@ -78,6 +78,9 @@ struct ColprodPlan {
     size_t partial_bytes = 0; // S * C * 4 when S > 1
     unsigned narrow_w = 0;    // units per row when the narrow-row kernel runs, else 0
     bool narrow_vec = false;  // its unit: a 16-byte vector (true) or one element
+    unsigned wide_vpl = 0;    // vectors per lane of the wide-strip kernel, 0 when it does not run
+    unsigned full_strips = 0; // its workgroups that own whole strips
+    unsigned wide_grid = 0;   // its grid (full strips, then the remaining blocks)
     unsigned finish_blocks = 0;     // second-pass workgroups (S > 1)
     unsigned finish_cols_log2 = 0;  // log2 of the columns per second-pass workgroup
 };

@@ -70,13 +70,13 @@ def dev_at(a, off):
     return dev(flat)[off:].view(*a.shape)
 
 
-def colprod_case(red, orc, kind, R, C, ld, seed, off=0):
-    what = "colprod %s R=%d C=%d ld=%d off=%d" % (kind, R, C, ld, off)
+def colprod_case(red, orc, kind, R, C, ld, seed, off=0, dst_off=0):
+    what = "colprod %s R=%d C=%d ld=%d off=%d dst_off=%d" % (kind, R, C, ld, off, dst_off)
     say(what)
     if kind == "i32":
         # odd factors: the product mod 2^32 stays odd, so every row counts
         src = workloads.integers_i32(seed, R * ld, -(2 ** 31), 2 ** 31).reshape(R, ld) | 1
-        out = torch.zeros(C, dtype=torch.int32, device="cuda")
+        out = torch.zeros(C + dst_off, dtype=torch.int32, device="cuda")[dst_off:]
         red.colprod_i32(dev_at(src, off), out, C=C)
         got = host(out)
         want = orc.colprod_i32(src, R, C, ld)
@@ -87,25 +87,25 @@ def colprod_case(red, orc, kind, R, C, ld, seed, off=0):
     rare = 2e-5 if kind == "f16" and R > 4096 else 2e-4
     x = tile_f32(seed, R, C, ld, "prod", rare)
     if kind == "f32":
-        out = torch.zeros(C, dtype=torch.float32, device="cuda")
+        out = torch.zeros(C + dst_off, dtype=torch.float32, device="cuda")[dst_off:]
         red.colprod_f32(dev_at(x, off), out, C=C)
         check_rel(host(out), orc.colprod_f32(x, R, C, ld), COLPROD_F32_TOL, what)
         return
     bits = (workloads.to_f16_bits if kind == "f16" else workloads.to_bf16_bits)(x.reshape(-1))
     bits = bits.reshape(R, ld)
     tdt = torch.float16 if kind == "f16" else torch.bfloat16
-    out = torch.zeros(C, dtype=tdt, device="cuda")
+    out = torch.zeros(C + dst_off, dtype=tdt, device="cuda")[dst_off:]
     getattr(red, "colprod_" + kind)(dev_at(bits.view(np.int16), off).view(tdt), out, C=C)
     want = (orc.colprod_f16 if kind == "f16" else orc.colprod_bf16)(bits, R, C, ld)
     check_rel(host(out.float()), want, COLPROD_16_TOL, what)
 
 
-def cols_case(red, orc, op, R, C, ld, accum, seed, off=0):
-    what = "cols %s R=%d C=%d ld=%d accum=%d off=%d" % (op, R, C, ld, accum, off)
+def cols_case(red, orc, op, R, C, ld, accum, seed, off=0, dst_off=0):
+    what = "cols %s R=%d C=%d ld=%d accum=%d off=%d dst_off=%d" % (op, R, C, ld, accum, off, dst_off)
     say(what)
     x = tile_f32(seed, R, C, ld, op)
     old = workloads.uniform_f32(seed + 1, C, -3.0, 3.0)
-    out = dev(old.copy())
+    out = dev_at(old.copy(), dst_off)
     getattr(red, op + "_cols_f32")(dev_at(x, off), out, C=C, accum=accum)
     got = host(out)
     if op == "sum":
@@ -208,11 +208,16 @@ def test_second_pass_cols(red, orc, op, R, C, ld):
 
 
 # Short, wide tiles: (R, C, ld).  For 4-byte elements, 1021 or more
-# column blocks give 4 row groups per block, 4081 or more give 1.
+# column blocks give 4 row groups per block, 4081 or more give 1; with
+# 16-byte aligned rows, 256 strips of 32, 64 or 128 whole blocks (8 K, 16 K
+# or 32 K blocks) give the wide-strip kernel 2, 4 or 8 vectors per lane,
+# the remaining blocks going to one row group per block.
 WIDE = [
     (37, 65536, 65536), (5, 131172, 131172), (7, 70001, 70002), (33, 80000, 80001),
     (3, 300_000, 300_000), (16, 262_144, 262_144), (1, 1_000_003, 1_000_004),
     (9, 300_001, 300_005), (2, 400_000, 400_001),
+    (3, 2_100_001, 2_100_004), (5, 1_048_576, 1_048_576), (2, 1_600_000, 1_600_000),
+    (17, 600_000, 600_000),
 ]
 
 
@@ -223,9 +228,9 @@ def test_wide_4byte(red, orc, kind, R, C, ld):
 
 
 # 2-byte elements: 2041 or more blocks of 128 columns give 4 row groups
-# per block, 8161 or more give 1.
+# per block, 8161 or more give 1 (and the wide-strip kernel as above).
 WIDE16 = [(20, 262_144, 262_144), (6, 270_000, 270_003), (4, 1_100_000, 1_100_008),
-          (11, 1_050_001, 1_050_001)]
+          (11, 1_050_001, 1_050_001), (3, 4_200_005, 4_200_008), (2, 2_400_000, 2_400_000)]
 
 
 @pytest.mark.parametrize("R,C,ld", WIDE16)
@@ -235,8 +240,25 @@ def test_wide_2byte(red, orc, kind, R, C, ld):
 
 
 @pytest.mark.parametrize("R,C,ld", [(37, 65536, 65536), (7, 70001, 70002),
-                                    (3, 300_000, 300_000), (9, 300_001, 300_005)])
+                                    (3, 300_000, 300_000), (9, 300_001, 300_005),
+                                    (3, 2_100_001, 2_100_004), (2, 1_600_000, 1_600_000)])
 @pytest.mark.parametrize("op", ["sum", "max", "min"])
 @pytest.mark.parametrize("accum", [0, 1])
 def test_wide_cols(red, orc, op, R, C, ld, accum):
     cols_case(red, orc, op, R, C, ld, accum, 1200 + R)
+
+
+# The wide-strip kernel stores whole 16-byte vectors when dst is 16-byte
+# aligned and single elements otherwise: both, with and without accum.
+@pytest.mark.parametrize("dst_off", [0, 1, 3])
+@pytest.mark.parametrize("kind", ["f32", "i32", "bf16", "f16"])
+def test_wide_dst_alignment(red, orc, kind, dst_off):
+    R, C, ld = (3, 2_100_001, 2_100_004) if kind in ("f32", "i32") else (3, 4_200_005, 4_200_008)
+    colprod_case(red, orc, kind, R, C, ld, 1600, 0, dst_off)
+
+
+@pytest.mark.parametrize("dst_off", [0, 1])
+@pytest.mark.parametrize("op", ["sum", "max", "min"])
+@pytest.mark.parametrize("accum", [0, 1])
+def test_wide_cols_dst_alignment(red, orc, op, accum, dst_off):
+    cols_case(red, orc, op, 5, 1_048_576, 1_048_576, accum, 1700, 0, dst_off)
