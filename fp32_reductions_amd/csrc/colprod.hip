@@ -17,7 +17,9 @@
 //    rows of the slice and combine their partial products in LDS in
 //    row-group order.  Short, wide tiles, whose blocks alone would give
 //    thousands of short-lived workgroups, put 4 or 16 adjacent blocks in a
-//    workgroup instead, with 4 or 1 row groups each;
+//    workgroup instead, with 4 or 1 row groups each; with more blocks
+//    still, a wide-strip kernel gives each lane 2 to 8 vectors of a row and
+//    fewer rows in flight;
 //  * when the grid needs more workgroups than there are column blocks, the
 //    rows are split into S slices (blockIdx.y); each workgroup stores its
 //    partial row in the workspace, and a second kernel combines the S
