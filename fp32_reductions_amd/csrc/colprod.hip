@@ -20,11 +20,12 @@
 //    workgroup instead, with 4 or 1 row groups each; with more blocks
 //    still, a wide-strip kernel gives each lane 2 to 8 vectors of a row and
 //    fewer rows in flight;
-//  * when the grid needs more workgroups than there are column blocks, the
-//    rows are split into S slices (blockIdx.y); each workgroup stores its
-//    partial row in the workspace, and a second kernel combines the S
-//    partial rows of each column in a fixed order (strided runs per thread,
-//    then a pairwise tree in LDS), narrows once to T and writes dst;
+//  * when the grid needs more workgroups than there are column blocks, S
+//    workgroups (blockIdx.y) share each block's rows in interleaved chunks
+//    of 128 rows (grid-stride along the rows); each stores its partial row
+//    in the workspace, and a second kernel combines the S partial rows of
+//    each column in a fixed order (strided runs per thread, then a pairwise
+//    tree in LDS), narrows once to T and writes dst;
 //  * rows narrower than 256 bytes would leave most of those lanes idle: a
 //    narrow-row kernel reads whole rows instead, 256 / W rows of W units
 //    per step (16-byte vectors when the tile is aligned and C * sizeof(T) is
@@ -213,10 +214,10 @@ struct OpMul {
 //
 // A column block is kCols = 16 * V columns (256 bytes of each row).  A
 // workgroup's 256 threads form 16 row groups of 16 lanes, GPB row groups
-// per column block, so that it owns 16 / GPB adjacent column blocks and the
-// rows of its slice: row group gr of a block reads rows gr, gr + GPB,
-// gr + 2 GPB, ... of the slice, each lane one 16-byte vector per row, with
-// kRowsInFlight rows in flight.  The GPB partial products of a block are
+// per column block, so that it owns 16 / GPB adjacent column blocks: row
+// group gr of a block reads rows gr, gr + GPB, gr + 2 GPB, ... of each of
+// its chunks of GPB * kRowsInFlight rows, each lane one 16-byte vector per
+// row, with kRowsInFlight rows in flight.  The GPB partial products of a block are
 // combined in LDS in row-group order (GPB = 1 stores straight from the
 // lanes).  GPB = 16 (one block per workgroup, a wave reading 256 bytes of
 // four rows) serves tiles of many rows; GPB = 4 and 1 give short, wide
@@ -226,11 +227,14 @@ struct OpMul {
 // 44.1 us for workgroups of 256 columns whose waves each read 1 KiB of a
 // row, split four ways over the rows and finished by a second kernel.)
 // The work of workgroup `wg` along the columns and `s` of S along the rows.
+// The rows are walked in chunks of GPB * kRowsInFlight (each row group's
+// rows in flight at once); with S > 1 workgroup s takes chunks s, s + S,
+// s + 2S, ... (grid-stride along the rows).
 template <class Tr, class Op, bool VEC, int GPB>
 __device__ __forceinline__ void colred_blocks(
     const typename Tr::T* __restrict__ src, uint64_t R, uint64_t C,
     uint64_t ld, typename Tr::T* __restrict__ dst,
-    typename Tr::A* __restrict__ partials, uint64_t rows_per_split, int accum,
+    typename Tr::A* __restrict__ partials, int accum,
     uint64_t wg, uint64_t s, uint32_t S)
 {
     using T = typename Tr::T;
@@ -248,8 +252,8 @@ __device__ __forceinline__ void colred_blocks(
     const uint32_t gr = g % GPB;                      // row group within the block
     const uint64_t cb = wg * kBlocksPerWg + g / GPB;
     const uint64_t jb = cb * kCols; // first column of the block
-    const uint64_t r0 = s * rows_per_split;
-    const uint64_t r1 = (r0 + rows_per_split < R) ? r0 + rows_per_split : R;
+    constexpr uint64_t kChunk = (uint64_t)GPB * kRowsInFlight;
+    const uint64_t step = (uint64_t)S * kChunk;
     const bool full = VEC && jb + kCols <= C;
 
     A acc[V];
@@ -257,7 +261,9 @@ __device__ __forceinline__ void colred_blocks(
     for (int k = 0; k < V; ++k)
         acc[k] = Op::identity();
 
-    uint64_t r = r0 + gr;
+    // The chunk that reaches past R (if it is this workgroup's) is the last
+    // one: its remaining rows are read one at a time.
+    uint64_t r = s * kChunk + gr;
     if (jb >= C) {
         // A block past the last column (the workgroup's last blocks when
         // 16 / GPB does not divide the block count): nothing to read.
@@ -265,8 +271,7 @@ __device__ __forceinline__ void colred_blocks(
         // Lane q owns columns jb + qV .. jb + qV + V - 1: one 16-byte vector
         // per row.
         const T* __restrict__ col = src + jb + (uint64_t)q * V;
-        for (; r + (uint64_t)GPB * (kRowsInFlight - 1) < r1;
-             r += (uint64_t)GPB * kRowsInFlight) {
+        for (; r + (uint64_t)GPB * (kRowsInFlight - 1) < R; r += step) {
             uint4 v[kRowsInFlight];
 #pragma unroll
             for (int u = 0; u < kRowsInFlight; ++u)
@@ -281,7 +286,7 @@ __device__ __forceinline__ void colred_blocks(
                     acc[k] = Op::apply(acc[k], a[k]);
             }
         }
-        for (; r < r1; r += GPB) {
+        for (; r < R; r += GPB) {
             A a[V];
             Tr::unpack(load_stream(reinterpret_cast<const uint4*>(col + r * ld)), a);
 #pragma unroll
@@ -303,8 +308,7 @@ __device__ __forceinline__ void colred_blocks(
             ok[k] = jb + c < C;
             off[k] = ok[k] ? c : 0u;
         }
-        for (; r + (uint64_t)GPB * (kRowsInFlight - 1) < r1;
-             r += (uint64_t)GPB * kRowsInFlight) {
+        for (; r + (uint64_t)GPB * (kRowsInFlight - 1) < R; r += step) {
             T v[kRowsInFlight][V];
 #pragma unroll
             for (int u = 0; u < kRowsInFlight; ++u)
@@ -319,7 +323,7 @@ __device__ __forceinline__ void colred_blocks(
                     if (ok[k])
                         acc[k] = Op::apply(acc[k], Tr::widen(v[u][k]));
         }
-        for (; r < r1; r += GPB) {
+        for (; r < R; r += GPB) {
 #pragma unroll
             for (int k = 0; k < V; ++k)
                 if (ok[k])
@@ -374,10 +378,10 @@ template <class Tr, class Op, bool VEC, int GPB>
 __global__ __launch_bounds__(kBlock) void colred_kernel(
     const typename Tr::T* __restrict__ src, uint64_t R, uint64_t C,
     uint64_t ld, typename Tr::T* __restrict__ dst,
-    typename Tr::A* __restrict__ partials, uint64_t rows_per_split, int accum)
+    typename Tr::A* __restrict__ partials, int accum)
 {
-    colred_blocks<Tr, Op, VEC, GPB>(src, R, C, ld, dst, partials, rows_per_split,
-                                    accum, blockIdx.x, blockIdx.y, gridDim.y);
+    colred_blocks<Tr, Op, VEC, GPB>(src, R, C, ld, dst, partials, accum,
+                                    blockIdx.x, blockIdx.y, gridDim.y);
 }
 
 // Short, wide tiles with so many column blocks that a workgroup can own a
@@ -403,7 +407,7 @@ __global__ __launch_bounds__(kBlock) void colred_wide_kernel(
     static_assert(RU * VPL == kRowsInFlight, "VPL divides the loads in flight");
 
     if (blockIdx.x >= full_strips) {
-        colred_blocks<Tr, Op, true, 1>(src, R, C, ld, dst, nullptr, R, accum,
+        colred_blocks<Tr, Op, true, 1>(src, R, C, ld, dst, nullptr, accum,
                                        (uint64_t)full_strips * VPL + (blockIdx.x - full_strips),
                                        0, 1);
         return;
@@ -681,7 +685,7 @@ hipError_t launch_typed(const void* src, size_t R, size_t C, size_t ld,
         const unsigned per_wg = kBlock / kLanesPerRow / plan.group_rows;
         const dim3 grid((plan.col_blocks + per_wg - 1) / per_wg, plan.splits);
         auto go = [&](auto kern) {
-            kern<<<grid, kBlock, 0, stream>>>(s, R, C, ld, d, part, plan.rows_per_split, accum);
+            kern<<<grid, kBlock, 0, stream>>>(s, R, C, ld, d, part, accum);
         };
         if (plan.group_rows == 1)
             vec ? go(colred_kernel<Tr, Op, true, 1>) : go(colred_kernel<Tr, Op, false, 1>);
@@ -703,9 +707,6 @@ size_t colprod_elem_size(ColType t)
     return (t == ColType::F16 || t == ColType::BF16 || t == ColType::U16) ? 2 : 4;
 }
 
-// Fewest rows a workgroup should own when the rows are split: below this
-// the partial-row traffic grows relative to the tile.
-constexpr uint64_t kMinRowsPerSplit = 32;
 constexpr uint64_t kMaxSplits = 65535; // gridDim.y limit
 // Workgroups per compute unit for the narrow-row kernel (grid-stride).
 #ifndef RED_COLPROD_NARROW_WG_PER_CU
@@ -757,7 +758,6 @@ ColprodPlan colprod_plan(ColType t, const void* src, size_t R, size_t C, size_t 
             S = (S + 1) / 2;
         if (S < 1)
             S = 1;
-        p.rows_per_split = R;
     } else {
         const uint64_t cols = (uint64_t)kLanesPerRow * (16 / es);
         p.col_blocks = (unsigned)((C + cols - 1) / cols);
@@ -776,9 +776,11 @@ ColprodPlan colprod_plan(ColType t, const void* src, size_t R, size_t C, size_t 
         const uint64_t wgs = (p.col_blocks * p.group_rows + groups - 1) / groups;
         if (wgs < target)
             S = (target + wgs - 1) / wgs;
-        const uint64_t s_rows = (R + kMinRowsPerSplit - 1) / kMinRowsPerSplit;
-        if (S > s_rows)
-            S = s_rows;
+        // At least one chunk of rows per workgroup.
+        const uint64_t chunk = (uint64_t)p.group_rows * kRowsInFlight;
+        const uint64_t chunks = (R + chunk - 1) / chunk;
+        if (S > chunks)
+            S = chunks;
         if (S > kMaxSplits)
             S = kMaxSplits;
         // The workspace bounds S * C partial values.
@@ -786,8 +788,6 @@ ColprodPlan colprod_plan(ColType t, const void* src, size_t R, size_t C, size_t 
             S = (S + 1) / 2;
         if (S < 1)
             S = 1;
-        p.rows_per_split = (R + S - 1) / S;
-        S = (R + p.rows_per_split - 1) / p.rows_per_split; // no empty slice
         // Wide strips: the most vectors per lane that still give every CU a
         // workgroup of whole blocks.
         if (vec && p.group_rows == 1 && S == 1) {

@@ -74,7 +74,6 @@ struct ColprodPlan {
     unsigned col_blocks = 0;  // 256-byte column blocks
     unsigned group_rows = 16; // row groups per column block (1, 4 or 16)
     unsigned splits = 1;      // workgroups along the rows (S)
-    size_t rows_per_split = 0;
     size_t partial_bytes = 0; // S * C * 4 when S > 1
     unsigned narrow_w = 0;    // units per row when the narrow-row kernel runs, else 0
     bool narrow_vec = false;  // its unit: a 16-byte vector (true) or one element
