@@ -9,18 +9,21 @@ cover every vector width W from 1 to 15 for 4-byte and 2-byte elements,
 element rows of 1 to 127 elements with misaligned starts, padding past C
 (filled with NaN, never read), row counts that end inside a step and
 inside a sweep, and counts large enough for hundreds of workgroups and a
-second pass.  Products over long
-columns use factors +-1 with rare +-2 and +-0.5, so that the exact product
-stays in range and every order of multiplication gives it exactly.
+second pass.  Products over long columns use factors +-1 with rare +-2
+and +-0.5, so that the exact product stays in range and every order of
+multiplication gives it exactly.
 
 Short, wide tiles (thousands of 256-byte column blocks) give a workgroup
-several adjacent column blocks with 4 or 1 row groups each; the cases
-cover both, with a block count that leaves the last workgroup part empty,
-a ragged last block, and unaligned rows.
+several adjacent column blocks with 4 or 1 row groups each, and with
+more blocks still a wide strip in which each lane reads 2, 4 or 8
+vectors of a row; the cases cover each, with a block count that leaves
+the last workgroup part empty, a ragged last block, unaligned rows, and
+aligned and misaligned destinations.
 
 The second pass spreads each column's S partial rows over the threads of
-a workgroup; the cases below put S from 2 to 256 against column counts from
-1 to a few thousand on both kernels."""
+a workgroup; the cases below put S from 2 to a few hundred against column
+counts from 1 to a few thousand on the column-block and narrow-row
+kernels."""
 import numpy as np
 import pytest
 
