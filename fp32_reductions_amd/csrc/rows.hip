@@ -285,20 +285,77 @@ constexpr int kTileBatch = 8;          // loads in flight per thread while stagi
 constexpr uint64_t kDirectRowMax = 16; // rows this short are read by their thread directly
 
 // Rows of 17 to 64 elements: the workgroup copies TR rows at a time into
-// LDS with coalesced loads (16-byte non-temporal loads of the whole tile
-// when the rows are contiguous and 16-byte aligned, else 4-byte loads),
-// each row at an odd stride so that the threads' row reads hit distinct
-// banks; then thread t reduces rows t, t + 128, ... of the tile, each in
-// the page's order.  (Measured on MI355X, 256 MiB of contiguous rows from
+// LDS with coalesced loads, each row at an odd stride so that the threads'
+// row reads hit distinct banks; then thread t reduces rows t, t + 128, ...
+// of the tile, each in the page's order.  With a row stride of at most 64
+// elements (span) the tile is read as one contiguous run, from its first
+// row's first element to its last row's last valid element, in 16-byte
+// non-temporal loads at any 4-byte alignment (gfx950 reads unaligned
+// multi-dword vectors from global memory), and the ld - n padding elements
+// between rows are dropped on the way into LDS; longer strides read the
+// valid elements one by one.  (Measured on MI355X, 256 MiB of rows from
 // HBM: 31-element rows 260 us read directly by their thread, 52 us staged;
 // 33- to 64-element rows 84-204 us direct, 47-57 us staged.  Rows of up to
 // 16 elements are faster read directly: 51.5 us against 58.3 at n = 16.)
-// row_of(e) = floor(e / n) is computed as (e * inv_n) >> 32 with
-// inv_n = ceil(2^32 / n), exact for e < 2^13 and n <= 64.
+// floor(e / d) for d = n or ld is computed as (e * inv_d) >> 32 with
+// inv_d = ceil(2^32 / d), exact for e < 2^14 and d <= 128 (checked
+// exhaustively).
+// Copies T rows of n elements, row stride L <= 64, into the LDS tile (row
+// i at tile + i * stride), reading the span from the first element to the
+// last row's last valid element in 16-byte loads at any 4-byte alignment.
+// PAD (L > n): the padding elements between rows are dropped.
+template <bool PAD>
+__device__ __forceinline__ void stage_span(const float* __restrict__ x, uint32_t T,
+                                           uint32_t n, uint32_t L, uint64_t inv_ld,
+                                           float* __restrict__ tile, uint32_t stride)
+{
+    typedef float f4u __attribute__((ext_vector_type(4), aligned(4)));
+    const uint32_t t = threadIdx.x;
+    const f4u* __restrict__ src = reinterpret_cast<const f4u*>(x);
+    const uint32_t run = (T - 1) * L + n; // elements of the span
+    const uint32_t nv = run / 4;
+    for (uint32_t f0 = 0; f0 < nv; f0 += kTileBatch * kTileThreads) {
+        // Unconditional loads (past the end: vector 0 again, not stored) so
+        // that the whole batch is in flight at once.
+        f4u v[kTileBatch];
+#pragma unroll
+        for (int b = 0; b < kTileBatch; ++b) {
+            const uint32_t f = f0 + b * kTileThreads + t;
+            v[b] = __builtin_nontemporal_load(src + (f < nv ? f : 0));
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int b = 0; b < kTileBatch; ++b) {
+            const uint32_t f = f0 + b * kTileThreads + t;
+            if (f < nv) {
+                const uint32_t e = 4 * f;
+                uint32_t row = (uint32_t)(((uint64_t)e * inv_ld) >> 32);
+                uint32_t col = e - row * L;
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    if (!PAD || col < n)
+                        tile[row * stride + col] = v[b][c];
+                    if (++col == L) {
+                        col = 0;
+                        ++row;
+                    }
+                }
+            }
+        }
+    }
+    for (uint32_t e = 4 * nv + t; e < run; e += kTileThreads) {
+        const uint32_t row = (uint32_t)(((uint64_t)e * inv_ld) >> 32);
+        const uint32_t col = e - row * L;
+        if (!PAD || col < n)
+            tile[row * stride + col] = x[e];
+    }
+}
+
 template <class Op>
 __global__ __launch_bounds__(kTileThreads) void rows_tile_kernel(
     const float* __restrict__ x, uint64_t rows, uint32_t n, uint64_t ld,
-    float* __restrict__ out, int accum, int flat, uint64_t inv_n, uint32_t TR)
+    float* __restrict__ out, int accum, int span, uint64_t inv_n, uint64_t inv_ld,
+    uint32_t TR)
 {
     extern __shared__ float tile[];
     const uint32_t stride = n | 1u;
@@ -306,43 +363,11 @@ __global__ __launch_bounds__(kTileThreads) void rows_tile_kernel(
     for (uint64_t r0 = (uint64_t)blockIdx.x * TR; r0 < rows; r0 += (uint64_t)gridDim.x * TR) {
         const uint32_t T = (rows - r0 < TR) ? (uint32_t)(rows - r0) : TR;
         const uint32_t total = T * n;
-        if (flat) {
-            // Rows are contiguous (ld == n) and the tile starts 16-byte aligned.
-            const float4* __restrict__ src = reinterpret_cast<const float4*>(x + r0 * n);
-            const uint32_t nv = total / 4;
-            for (uint32_t f0 = 0; f0 < nv; f0 += kTileBatch * kTileThreads) {
-                // Unconditional loads (past the end: vector 0 again, not
-                // stored) so that the whole batch is in flight at once.
-                float4 v[kTileBatch];
-#pragma unroll
-                for (int b = 0; b < kTileBatch; ++b) {
-                    const uint32_t f = f0 + b * kTileThreads + t;
-                    v[b] = load_stream(src + (f < nv ? f : 0));
-                }
-                __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-                for (int b = 0; b < kTileBatch; ++b) {
-                    const uint32_t f = f0 + b * kTileThreads + t;
-                    if (f < nv) {
-                        const uint32_t e = 4 * f;
-                        uint32_t row = (uint32_t)(((uint64_t)e * inv_n) >> 32);
-                        uint32_t col = e - row * n;
-                        const float w[4] = {v[b].x, v[b].y, v[b].z, v[b].w};
-#pragma unroll
-                        for (int c = 0; c < 4; ++c) {
-                            tile[row * stride + col] = w[c];
-                            if (++col == n) {
-                                col = 0;
-                                ++row;
-                            }
-                        }
-                    }
-                }
-            }
-            for (uint32_t e = 4 * nv + t; e < total; e += kTileThreads) {
-                const uint32_t row = (uint32_t)(((uint64_t)e * inv_n) >> 32);
-                tile[row * stride + (e - row * n)] = x[r0 * n + e];
-            }
+        if (span) {
+            if (ld == n)
+                stage_span<false>(x + r0 * ld, T, n, n, inv_ld, tile, stride);
+            else
+                stage_span<true>(x + r0 * ld, T, n, (uint32_t)ld, inv_ld, tile, stride);
         } else {
             for (uint32_t e0 = 0; e0 < total; e0 += 2 * kTileBatch * kTileThreads) {
                 float v[2 * kTileBatch];
@@ -629,17 +654,19 @@ hipError_t launch_rows_op(const float* x, size_t rows, size_t n, size_t ld,
             rows_thread_kernel<Op, false><<<grid, kBlock, 0, stream>>>(
                 x, rows, (uint32_t)n, ld, out, accum);
     } else if (n <= kThreadRowMax) {
-        // A multiple of 4 rows per tile keeps every tile of contiguous rows
-        // 16-byte aligned; TR * n <= 8192 keeps the row index arithmetic exact.
+        // A multiple of 4 rows per tile keeps every tile of 16-byte aligned,
+        // contiguous rows aligned; TR * ld <= 8192 keeps the row index
+        // arithmetic exact on the span path.
         const uint32_t TR = kTileRows;
         const uint64_t tiles = (rows + TR - 1) / TR;
         const uint64_t cap = (uint64_t)dev.cus * kRowsWgPerCu;
         const unsigned grid = (unsigned)(tiles < cap ? tiles : cap);
-        const int flat = (ld == n) && (((uintptr_t)x & 15u) == 0);
+        const int span = ld <= kThreadRowMax;
         const uint64_t inv_n = ((1ull << 32) + n - 1) / n;
+        const uint64_t inv_ld = ((1ull << 32) + ld - 1) / ld;
         const size_t lds = (size_t)TR * (n | 1u) * sizeof(float);
         rows_tile_kernel<Op><<<grid, kTileThreads, lds, stream>>>(
-            x, rows, (uint32_t)n, ld, out, accum, flat, inv_n, TR);
+            x, rows, (uint32_t)n, ld, out, accum, span, inv_n, inv_ld, TR);
     } else if (n <= kPairRowMax) {
         // <G lanes per row, U vectors per lane and row, P rows per segment>:
         // 4 * G * U >= n covers the row; U * P = 8 loads per lane in flight.
