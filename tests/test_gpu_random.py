@@ -172,3 +172,75 @@ def test_random_columns(red, orc):
             got = host(out.float())
             want = getattr(orc, "colprod_" + kind)(bits, R, C, ld)
             check_rel(got, want, COLPROD_16_TOL, what)
+
+
+def test_random_column_paths(red, orc):
+    """Column cases drawn per layout class: narrow rows (16-byte vectors or
+    elements), short and wide tiles (several blocks per workgroup, wide
+    strips), rows shared by several workgroups, and general shapes; with a
+    random source and destination offset and, for the column sum / max /
+    min, random accum.  Products over long columns use factors +-1 with
+    rare +-2 and +-0.5 (exact in any order)."""
+    rng = np.random.default_rng(9004)
+    kinds = ["f32", "i32", "bf16", "f16", "sum", "max", "min"]
+    for case in range(84):
+        kind = kinds[case % 7]
+        layout = (case // 7) % 4
+        if layout == 0:
+            C, R = log_uniform(rng, 1, 127), log_uniform(rng, 1, 300000)
+        elif layout == 1:
+            C, R = log_uniform(rng, 60000, 2_500_000), log_uniform(rng, 1, 24)
+        elif layout == 2:
+            C, R = log_uniform(rng, 64, 5000), log_uniform(rng, 100, 40000)
+        else:
+            C, R = log_uniform(rng, 1, 40000), log_uniform(rng, 1, 5000)
+        ld = C + int(rng.integers(0, 2)) * int(rng.integers(0, 9))
+        R = max(1, min(R, 6_000_000 // ld))
+        off = int(rng.integers(0, 2)) * int(rng.integers(0, 4))
+        doff = int(rng.integers(0, 2)) * int(rng.integers(0, 3))
+        what = "col path case %d kind=%s R=%d C=%d ld=%d off=%d doff=%d" % (
+            case, kind, R, C, ld, off, doff)
+        say(what)
+
+        def at(a, o):
+            flat = np.zeros(a.size + o + 8, a.dtype)
+            flat[o:o + a.size] = a.reshape(-1)
+            return dev(flat)[o:o + a.size].view(*a.shape)
+
+        if kind == "i32":
+            src = rng.integers(-(2 ** 31), 2 ** 31, (R, ld), dtype=np.int64).astype(np.int32) | 1
+            out = torch.zeros(C + doff, dtype=torch.int32, device="cuda")[doff:]
+            red.colprod_i32(at(src, off), out, C=C)
+            assert (host(out) == orc.colprod_i32(src, R, C, ld)).all(), what
+        elif kind in ("sum", "max", "min"):
+            x = rng.uniform(-1, 1, (R, ld)).astype(np.float32)
+            x[:, C:] = np.nan
+            accum = bool(rng.integers(0, 2))
+            old = rng.uniform(-3, 3, C).astype(np.float32)
+            out = at(old.copy(), doff)
+            getattr(red, kind + "_cols_f32")(at(x, off), out, C=C, accum=accum)
+            got = host(out)
+            if kind == "sum":
+                s, a = orc.cols_sum_f32(x, R, C, ld, accum, old)
+                assert (np.abs(got.astype(np.float64) - s) <= 1e-6 * a).all(), what
+            else:
+                want = getattr(orc, "cols_%s_f32" % kind)(x, R, C, ld, accum, old)
+                eq = (got.view(np.uint32) == want.view(np.uint32)) | ((got == 0) & (want == 0))
+                assert eq.all(), what
+        else:
+            rare = 2e-5 if kind == "f16" else 2e-4
+            u = rng.random((R, ld))
+            x = np.where(u < rare, 2.0, np.where(u < 2 * rare, 0.5, 1.0))
+            x = (x * np.where(rng.random((R, ld)) < 0.5, -1.0, 1.0)).astype(np.float32)
+            x[:, C:] = np.nan
+            if kind == "f32":
+                out = torch.zeros(C + doff, dtype=torch.float32, device="cuda")[doff:]
+                red.colprod_f32(at(x, off), out, C=C)
+                check_rel(host(out), orc.colprod_f32(x, R, C, ld), COLPROD_F32_TOL, what)
+            else:
+                tdt = torch.bfloat16 if kind == "bf16" else torch.float16
+                bits = torch.from_numpy(x).to(tdt).view(torch.int16).numpy().view(np.uint16)
+                out = torch.zeros(C + doff, dtype=tdt, device="cuda")[doff:]
+                getattr(red, "colprod_" + kind)(at(bits.view(np.int16), off).view(tdt), out, C=C)
+                want = getattr(orc, "colprod_" + kind)(bits, R, C, ld)
+                check_rel(host(out.float()), want, COLPROD_16_TOL, what)
