@@ -13,8 +13,8 @@
 //    them; 16 lanes cover 256 contiguous bytes of a row and a wave reads
 //    four rows per load;
 //  * a workgroup (256 threads = 16 row groups of 16 lanes) covers one block
-//    of 16*V columns and a slice of rows; its row groups take interleaved
-//    rows of the slice and combine their partial products in LDS in
+//    of 16*V columns and its share of the rows; its row groups take
+//    interleaved rows and combine their partial products in LDS in
 //    row-group order.  Short, wide tiles, whose blocks alone would give
 //    thousands of short-lived workgroups, put 4 or 16 adjacent blocks in a
 //    workgroup instead, with 4 or 1 row groups each; with more blocks
