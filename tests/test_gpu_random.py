@@ -5,7 +5,7 @@ every kernel-selection boundary (1-D: one or many workgroups, partial last
 sweep; rows: n up to 16, 64, 128, 256, 512, 1024 and 4096 elements, few and
 many rows, split rows; columns: ragged last column block, row splits,
 16-byte-aligned and unaligned rows), with random base misalignment, row
-padding (filled with NaN, which must never be read) and accum.  Every
+padding (filled with NaN, which must never reach a result) and accum.  Every
 result is checked against the CPU oracle: bit-exact for max / min, the
 page-order sum of rows of at most 64 elements and the integer products;
 the stated tolerances otherwise.  The generator seed is fixed, so a
