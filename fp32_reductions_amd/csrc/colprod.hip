@@ -803,9 +803,30 @@ ColprodPlan colprod_plan(ColType t, const void* src, size_t R, size_t C, size_t 
                 break;
             }
         }
+        // Row shares per block.  Each workgroup streams until its share is
+        // done, so the time goes as the rounds of workgroups the CUs run
+        // divided by the workgroups: of floor(target / wgs) and the ceiling,
+        // take the one with less of it (a grid a little over the CU count
+        // leaves its extra workgroups a second round of their own).  On a
+        // tie, aligned rows take fewer workgroups and unaligned rows (element
+        // loads, which gain from more loads in flight) more.  (Measured on
+        // MI355X, 256 MiB fp32 tiles of 62 column blocks: 5 shares, 310
+        // workgroups, 52.8 us; 4 shares, 248 workgroups, 43.1 us.  4096 x
+        // 16000 of stride 16001: 2 shares 50.4 us, 1 share 53.5 us.)
         const uint64_t wgs = (p.col_blocks * p.group_rows + groups - 1) / groups;
-        if (wgs < target)
-            S = (target + wgs - 1) / wgs;
+        if (wgs < target) {
+            const uint64_t lo = target / wgs;
+            const uint64_t hi = (target + wgs - 1) / wgs;
+            S = lo;
+            if (hi != lo) {
+                const uint64_t rounds_lo = (wgs * lo + target - 1) / target;
+                const uint64_t rounds_hi = (wgs * hi + target - 1) / target;
+                // rounds_hi / (wgs hi) against rounds_lo / (wgs lo)
+                const uint64_t cost_hi = rounds_hi * lo, cost_lo = rounds_lo * hi;
+                if (cost_hi < cost_lo || (cost_hi == cost_lo && !vec))
+                    S = hi;
+            }
+        }
         // At least one chunk of rows per workgroup.
         const uint64_t chunk = (uint64_t)p.group_rows * kRowsInFlight;
         const uint64_t chunks = (R + chunk - 1) / chunk;
