@@ -94,3 +94,79 @@ def test_graph_replay_matches_eager(red):
             else:
                 assert got.tobytes() == want.tobytes(), ("replay", rep, k)
     say("graph replays match eager calls")
+
+
+def test_graph_replay_tile_layouts(red):
+    """The same check for the layouts chosen by tile and row shape: narrow
+    rows read as 16-byte vectors and as elements (each with a second pass
+    over several row shares), a short, wide tile on the wide-strip kernel,
+    a tile whose rows do not start on 128-byte lines (XCD-contiguous order,
+    rows shared with a second pass), rows of 3 elements (eight per thread)
+    and padded rows of 20 staged as one span."""
+    say("graph capture of tile-layout calls and 4 replays")
+    dev = "cuda"
+    narrow_v = torch.empty((100000, 16), dtype=torch.float32, device=dev)
+    narrow_e = torch.empty((50000, 15), dtype=torch.bfloat16, device=dev)
+    wide = torch.empty((3, 2_100_032), dtype=torch.float32, device=dev)
+    unal = torch.empty((20000, 1001), dtype=torch.float32, device=dev)
+    short = torch.empty((200000, 3), dtype=torch.float32, device=dev)
+    span = torch.empty((50000, 24), dtype=torch.float32, device=dev)
+
+    def fill(seed):
+        narrow_v.copy_(torch.from_numpy(workloads.uniform_f32(seed, narrow_v.shape, 0.9999, 1.0001)))
+        narrow_e.copy_(torch.from_numpy(workloads.uniform_f32(seed + 1, narrow_e.shape, 0.999, 1.001)))
+        wide.copy_(torch.from_numpy(workloads.uniform_f32(seed + 2, wide.shape, 0.5, 1.5)))
+        unal.copy_(torch.from_numpy(workloads.uniform_f32(seed + 3, unal.shape)))
+        short.copy_(torch.from_numpy(workloads.uniform_f32(seed + 4, short.shape)))
+        span.copy_(torch.from_numpy(workloads.uniform_f32(seed + 5, span.shape)))
+
+    def make_outs():
+        return {"narrow_v": torch.zeros(16, device=dev),
+                "narrow_e": torch.zeros(15, dtype=torch.bfloat16, device=dev),
+                "wide": torch.zeros(2_100_032, device=dev),
+                "unal": torch.zeros(1000, device=dev),
+                "short": torch.zeros(200000, device=dev),
+                "span": torch.zeros(50000, device=dev)}
+
+    def calls(o):
+        red.colprod_f32(narrow_v, o["narrow_v"])
+        red.colprod_bf16(narrow_e, o["narrow_e"])
+        red.colprod_f32(wide, o["wide"])
+        red.sum_cols_f32(unal, o["unal"], C=1000, accum=True)
+        red.sum_rows_f32(short, o["short"], accum=True)
+        red.max_rows_f32(span, o["span"], n=20)
+
+    cap = torch.cuda.Stream()
+    eager_stream = torch.cuda.Stream()
+    fill(700)
+    graph_out = make_outs()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(cap):      # first call on the stream: workspace created
+        calls(graph_out)
+    cap.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=cap):
+        calls(graph_out)
+    torch.cuda.synchronize()
+
+    accum_base = {"unal": 0.25, "short": -1.5}
+    for rep in range(4):
+        fill(800 + 10 * rep)
+        for k, t in graph_out.items():
+            t.fill_(accum_base.get(k, 0.0))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        eager = make_outs()
+        for k, v in accum_base.items():
+            eager[k].fill_(v)
+        torch.cuda.synchronize()
+        with torch.cuda.stream(eager_stream):
+            calls(eager)
+        eager_stream.synchronize()
+        for k in graph_out:
+            got, want = graph_out[k], eager[k]
+            if got.dtype == torch.bfloat16:
+                got, want = got.view(torch.int16), want.view(torch.int16)
+            assert host(got).tobytes() == host(want).tobytes(), ("replay", rep, k)
+    say("tile-layout graph replays match eager calls")
