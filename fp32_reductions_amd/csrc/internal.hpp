@@ -33,6 +33,8 @@ struct DeviceInfo {
 #define RED_COLPROD_WG_PER_CU 1
 #endif
 constexpr int kStreamWgPerCu = RED_STREAM_WG_PER_CU;
+// Workgroups per compute unit for the single-pass atomic variant.
+constexpr int kAtomicWgPerCu = 1;
 constexpr int kColprodWgPerCu = RED_COLPROD_WG_PER_CU;
 // Row count from which the row kernels use one wave per row whatever n is.
 constexpr int kRowsWavePerCu = 8;
