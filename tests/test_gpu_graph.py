@@ -101,8 +101,9 @@ def test_graph_replay_tile_layouts(red):
     rows read as 16-byte vectors and as elements (each with a second pass
     over several row shares), a short, wide tile on the wide-strip kernel,
     a tile whose rows do not start on 128-byte lines (XCD-contiguous order,
-    rows shared with a second pass), rows of 3 elements (eight per thread)
-    and padded rows of 20 staged as one span."""
+    rows shared with a second pass), a tile of 257 column blocks on the
+    balanced kernel (blocks shared by workgroups, second pass), rows of 3
+    elements (eight per thread) and padded rows of 20 staged as one span."""
     say("graph capture of tile-layout calls and 4 replays")
     dev = "cuda"
     narrow_v = torch.empty((100000, 16), dtype=torch.float32, device=dev)
@@ -111,6 +112,7 @@ def test_graph_replay_tile_layouts(red):
     unal = torch.empty((20000, 1001), dtype=torch.float32, device=dev)
     short = torch.empty((200000, 3), dtype=torch.float32, device=dev)
     span = torch.empty((50000, 24), dtype=torch.float32, device=dev)
+    bal = torch.empty((1000, 16448), dtype=torch.float32, device=dev)
 
     def fill(seed):
         narrow_v.copy_(torch.from_numpy(workloads.uniform_f32(seed, narrow_v.shape, 0.9999, 1.0001)))
@@ -119,6 +121,7 @@ def test_graph_replay_tile_layouts(red):
         unal.copy_(torch.from_numpy(workloads.uniform_f32(seed + 3, unal.shape)))
         short.copy_(torch.from_numpy(workloads.uniform_f32(seed + 4, short.shape)))
         span.copy_(torch.from_numpy(workloads.uniform_f32(seed + 5, span.shape)))
+        bal.copy_(torch.from_numpy(workloads.uniform_f32(seed + 6, bal.shape)))
 
     def make_outs():
         return {"narrow_v": torch.zeros(16, device=dev),
@@ -126,7 +129,8 @@ def test_graph_replay_tile_layouts(red):
                 "wide": torch.zeros(2_100_032, device=dev),
                 "unal": torch.zeros(1000, device=dev),
                 "short": torch.zeros(200000, device=dev),
-                "span": torch.zeros(50000, device=dev)}
+                "span": torch.zeros(50000, device=dev),
+                "bal": torch.zeros(16448, device=dev)}
 
     def calls(o):
         red.colprod_f32(narrow_v, o["narrow_v"])
@@ -135,6 +139,7 @@ def test_graph_replay_tile_layouts(red):
         red.sum_cols_f32(unal, o["unal"], C=1000, accum=True)
         red.sum_rows_f32(short, o["short"], accum=True)
         red.max_rows_f32(span, o["span"], n=20)
+        red.sum_cols_f32(bal, o["bal"], accum=True)
 
     cap = torch.cuda.Stream()
     eager_stream = torch.cuda.Stream()
@@ -149,7 +154,7 @@ def test_graph_replay_tile_layouts(red):
         calls(graph_out)
     torch.cuda.synchronize()
 
-    accum_base = {"unal": 0.25, "short": -1.5}
+    accum_base = {"unal": 0.25, "short": -1.5, "bal": 2.0}
     for rep in range(4):
         fill(800 + 10 * rep)
         for k, t in graph_out.items():
