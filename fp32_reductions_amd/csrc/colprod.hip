@@ -226,18 +226,16 @@ struct OpMul {
 // per call with 256 workgroups of GPB = 16 and no second pass, against
 // 44.1 us for workgroups of 256 columns whose waves each read 1 KiB of a
 // row, split four ways over the rows and finished by a second kernel.)
-// The work of workgroup `wg` along the columns, over rows below row_end.
+// The work of workgroup `wg` along the columns and `s` of S along the rows.
 // The rows are walked in chunks of GPB * kRowsInFlight (each row group's
-// rows in flight at once): chunks c0, c0 + step, c0 + 2 step, ... (step > 1
-// is a grid-stride walk shared with other workgroups).  The combined
-// column values go to dst (prow == nullptr: the old dst first under accum,
-// narrowed to T) or, as partials, to prow[j - pcol0] for column j.
+// rows in flight at once); with S > 1 workgroup s takes chunks s, s + S,
+// s + 2S, ... (grid-stride along the rows).
 template <class Tr, class Op, bool VEC, int GPB>
 __device__ __forceinline__ void colred_blocks(
-    const typename Tr::T* __restrict__ src, uint64_t C,
+    const typename Tr::T* __restrict__ src, uint64_t R, uint64_t C,
     uint64_t ld, typename Tr::T* __restrict__ dst,
-    typename Tr::A* __restrict__ prow, uint64_t pcol0, int accum,
-    uint64_t wg, uint64_t c0, uint64_t step_chunks, uint64_t row_end)
+    typename Tr::A* __restrict__ partials, int accum,
+    uint64_t wg, uint64_t s, uint32_t S)
 {
     using T = typename Tr::T;
     using A = typename Tr::A;
@@ -255,8 +253,7 @@ __device__ __forceinline__ void colred_blocks(
     const uint64_t cb = wg * kBlocksPerWg + g / GPB;
     const uint64_t jb = cb * kCols; // first column of the block
     constexpr uint64_t kChunk = (uint64_t)GPB * kRowsInFlight;
-    const uint64_t step = step_chunks * kChunk;
-    const uint64_t R = row_end;
+    const uint64_t step = (uint64_t)S * kChunk;
     const bool full = VEC && jb + kCols <= C;
 
     A acc[V];
@@ -266,7 +263,7 @@ __device__ __forceinline__ void colred_blocks(
 
     // The chunk that reaches past R (if it is this workgroup's) is the last
     // one: its remaining rows are read one at a time.
-    uint64_t r = c0 * kChunk + gr;
+    uint64_t r = s * kChunk + gr;
     if (jb >= C) {
         // A block past the last column (the workgroup's last blocks when
         // 16 / GPB does not divide the block count): nothing to read.
@@ -342,10 +339,10 @@ __device__ __forceinline__ void colred_blocks(
                 const uint64_t j = jb + (full ? (uint64_t)q * V + k
                                               : (uint64_t)q + (uint64_t)kLanesPerRow * k);
                 if (j < C) {
-                    if (prow == nullptr)
+                    if (S == 1)
                         dst[j] = Tr::narrow(accum ? Op::apply(Tr::widen(dst[j]), acc[k]) : acc[k]);
                     else
-                        prow[j - pcol0] = acc[k];
+                        partials[s * C + j] = acc[k];
                 }
             }
         }
@@ -368,10 +365,10 @@ __device__ __forceinline__ void colred_blocks(
                 p = Op::apply(p, lds[b * GPB + w][c]);
             const uint64_t j = (wg * kBlocksPerWg + b) * kCols + c;
             if (j < C) {
-                if (prow == nullptr)
+                if (S == 1)
                     dst[j] = Tr::narrow(accum ? Op::apply(Tr::widen(dst[j]), p) : p);
                 else
-                    prow[j - pcol0] = p;
+                    partials[s * C + j] = p;
             }
         }
     }
@@ -413,85 +410,7 @@ __global__ __launch_bounds__(kBlock) void colred_kernel(
 {
     uint64_t wg, s;
     column_workgroup(xcd_contiguous, wg, s);
-    const uint32_t S = gridDim.y;
-    colred_blocks<Tr, Op, VEC, GPB>(src, C, ld, dst, S == 1 ? nullptr : partials + s * C, 0,
-                                    accum, wg, s, S, R);
-}
-
-// More column blocks than CUs, one row group layout (16 per block): one
-// workgroup per block would leave the blocks past a multiple of the CU
-// count to a second round of their own (257 blocks took 55 us where 256
-// took 41 us per 256 MiB).  Instead a fixed grid of G workgroups shares the
-// units (block b, 128-row chunk c), numbered u = b * nc + c: workgroup w
-// takes units floor(w U / G) .. floor((w + 1) U / G) - 1, walking each
-// block's chunks in order.  A block that lies wholly in one workgroup's run
-// goes straight to dst; the pieces of a block shared by several
-// workgroups go to the workspace (row `seg` of workgroup w, seg counted
-// from the first block of its run), and colred_shared_finish combines them
-// in workgroup order.
-template <class Tr, class Op, bool VEC>
-__global__ __launch_bounds__(kBlock) void colred_balanced_kernel(
-    const typename Tr::T* __restrict__ src, uint64_t R, uint64_t C,
-    uint64_t ld, typename Tr::T* __restrict__ dst,
-    typename Tr::A* __restrict__ partials, int accum, int xcd_contiguous,
-    uint64_t nc, uint32_t segs)
-{
-    constexpr int kCols = kLanesPerRow * Tr::V;
-    constexpr uint64_t kChunk = (uint64_t)(kBlock / kLanesPerRow) * kRowsInFlight;
-    uint64_t w, unused;
-    column_workgroup(xcd_contiguous, w, unused);
-    const uint64_t G = gridDim.x;
-    const uint64_t nb = (C + kCols - 1) / kCols;
-    const uint64_t U = nb * nc;
-    const uint64_t lo = w * U / G;
-    const uint64_t hi = (w + 1) * U / G;
-    const uint64_t b_first = lo / nc;
-    for (uint64_t u = lo; u < hi;) {
-        const uint64_t b = u / nc;
-        const uint64_t end = (b + 1) * nc < hi ? (b + 1) * nc : hi;
-        const uint64_t c0 = u - b * nc;
-        const uint64_t c1 = end - b * nc;
-        const uint64_t row_end = c1 * kChunk < R ? c1 * kChunk : R;
-        typename Tr::A* prow = (c0 == 0 && c1 == nc)
-            ? nullptr
-            : partials + (w * segs + (b - b_first)) * (uint64_t)kCols;
-        colred_blocks<Tr, Op, VEC, kBlock / kLanesPerRow>(src, C, ld, dst, prow, b * kCols,
-                                                          accum, b, c0, 1, row_end);
-        __syncthreads(); // the LDS of the combine is reused by the next block
-        u = end;
-    }
-}
-
-// Second pass of colred_balanced_kernel: one thread per column of a block
-// shared by several workgroups combines their pieces in workgroup order
-// (after the old dst[j] under accum) and narrows once to T.  Columns of
-// blocks owned by one workgroup were written by it.
-template <class Tr, class Op>
-__global__ __launch_bounds__(kBlock) void colred_shared_finish(
-    const typename Tr::A* __restrict__ partials, uint64_t C, uint64_t nc,
-    uint32_t segs, uint32_t G, typename Tr::T* __restrict__ dst, int accum)
-{
-    constexpr int kCols = kLanesPerRow * Tr::V;
-    const uint64_t j = (uint64_t)blockIdx.x * kBlock + threadIdx.x;
-    if (j >= C)
-        return;
-    const uint64_t nb = (C + kCols - 1) / kCols;
-    const uint64_t U = nb * nc;
-    const uint64_t b = j / kCols;
-    const uint64_t c = j % kCols;
-    // The workgroup whose run holds unit u: the largest w with
-    // floor(w U / G) <= u.
-    const uint64_t w0 = ((b * nc + 1) * G - 1) / U;
-    const uint64_t w1 = (((b + 1) * nc) * G - 1) / U;
-    if (w0 == w1)
-        return;
-    typename Tr::A p = Op::identity();
-    for (uint64_t w = w0; w <= w1; ++w) {
-        const uint64_t b_first = (w * U / G) / nc;
-        const typename Tr::A v = partials[(w * segs + (b - b_first)) * (uint64_t)kCols + c];
-        p = (w == w0) ? v : Op::apply(p, v);
-    }
-    dst[j] = Tr::narrow(accum ? Op::apply(Tr::widen(dst[j]), p) : p);
+    colred_blocks<Tr, Op, VEC, GPB>(src, R, C, ld, dst, partials, accum, wg, s, gridDim.y);
 }
 
 // Short, wide tiles with so many column blocks that a workgroup can own a
@@ -517,9 +436,9 @@ __global__ __launch_bounds__(kBlock) void colred_wide_kernel(
     static_assert(RU * VPL == kRowsInFlight, "VPL divides the loads in flight");
 
     if (blockIdx.x >= full_strips) {
-        colred_blocks<Tr, Op, true, 1>(src, C, ld, dst, nullptr, 0, accum,
+        colred_blocks<Tr, Op, true, 1>(src, R, C, ld, dst, nullptr, accum,
                                        (uint64_t)full_strips * VPL + (blockIdx.x - full_strips),
-                                       0, 1, R);
+                                       0, 1);
         return;
     }
     const uint32_t w = threadIdx.x / kWave;
@@ -781,20 +700,6 @@ hipError_t launch_typed(const void* src, size_t R, size_t C, size_t ld,
         else
             colred_narrow_kernel<Tr, Op, false><<<plan.splits, kBlock, 0, stream>>>(
                 s, R, C, ld, plan.narrow_w, d, part, accum);
-    } else if (plan.balanced_segs) {
-        const uint64_t nc = (R + kBlock / kLanesPerRow * kRowsInFlight - 1) /
-                            (kBlock / kLanesPerRow * kRowsInFlight);
-        const int xcd = (((uintptr_t)src & 127u) != 0) || ((ld * sizeof(T)) % 128 != 0);
-        if (vec)
-            colred_balanced_kernel<Tr, Op, true><<<plan.balanced_grid, kBlock, 0, stream>>>(
-                s, R, C, ld, d, part, accum, xcd, nc, plan.balanced_segs);
-        else
-            colred_balanced_kernel<Tr, Op, false><<<plan.balanced_grid, kBlock, 0, stream>>>(
-                s, R, C, ld, d, part, accum, xcd, nc, plan.balanced_segs);
-        if (plan.balanced_shared)
-            colred_shared_finish<Tr, Op><<<(unsigned)((C + kBlock - 1) / kBlock), kBlock, 0, stream>>>(
-                part, C, nc, plan.balanced_segs, plan.balanced_grid, d, accum);
-        return hipGetLastError();
     } else if (plan.wide_vpl) {
         auto go = [&](auto kern) {
             kern<<<plan.wide_grid, kBlock, 0, stream>>>(s, R, C, ld, d, accum, plan.full_strips);
@@ -854,6 +759,12 @@ constexpr uint64_t kMinGroupRows = RED_COLPROD_MIN_GROUP_ROWS;
 #define RED_COLPROD_MAX_WIDE_VPL 8
 #endif
 constexpr uint64_t kMaxWideVpl = RED_COLPROD_MAX_WIDE_VPL;
+// Row shares for tiles whose workgroups overrun a multiple of the CU count
+// by at most a quarter of it.
+#ifndef RED_COLPROD_OVER_SPLITS
+#define RED_COLPROD_OVER_SPLITS 6
+#endif
+constexpr uint64_t kOverSplits = RED_COLPROD_OVER_SPLITS;
 // Second pass: at most this many slices per thread when the column count
 // allows it.
 constexpr uint64_t kFinishSlicesPerThread = 8;
@@ -909,7 +820,28 @@ ColprodPlan colprod_plan(ColType t, const void* src, size_t R, size_t C, size_t 
         // workgroups, 52.8 us; 4 shares, 248 workgroups, 43.1 us.  4096 x
         // 16000 of stride 16001: 2 shares 50.4 us, 1 share 53.5 us.)
         const uint64_t wgs = (p.col_blocks * p.group_rows + groups - 1) / groups;
-        if (wgs < target) {
+        const bool lines = (((uintptr_t)src & 127u) == 0) && ((ld * es) % 128 == 0);
+        const uint64_t chunk_rows = (uint64_t)p.group_rows * kRowsInFlight;
+        if (wgs > target && lines && p.group_rows > 1 && wgs % target != 0 &&
+            (wgs % target) * 4 <= target &&
+            (R + chunk_rows - 1) / chunk_rows >= kOverSplits) {
+            // A last round of workgroups at most a quarter full runs alone
+            // for as long as a full round: kOverSplits row shares, each of
+            // at least one chunk (32 KiB per workgroup), turn it into a
+            // short tail at the price of the second pass.  Rows off
+            // 128-byte lines keep one share (they read lines shared by
+            // neighbouring blocks, and their shorter workgroups were
+            // slower), and tiles of one row group per block have the
+            // wide-strip kernel.  (Measured on MI355X, fp32 tiles, one
+            // share -> six: 256 MiB of 257 blocks 55.1 -> 44.2 us, 520
+            // blocks 54.3 -> 46.6, 1100 blocks of 4 row groups 55.8 -> 47.7;
+            // 64 MiB of 257 blocks 16.0 -> 15.0, 272 blocks 17.4 -> 15.0.
+            // With fewer than six chunks per block the second pass and the
+            // shorter workgroups cost more than the tail: 64 MiB of 776
+            // blocks, 3 chunks, one share 14.3 us, three 15.7 us.  Fuller last rounds gained at 256 MiB
+            // and lost at 64 MiB: 384 blocks 49.3 -> 46.8 but 14.0 -> 15.0.)
+            S = kOverSplits;
+        } else if (wgs < target) {
             const uint64_t lo = target / wgs;
             const uint64_t hi = (target + wgs - 1) / wgs;
             S = lo;
@@ -934,44 +866,6 @@ ColprodPlan colprod_plan(ColType t, const void* src, size_t R, size_t C, size_t 
             S = (S + 1) / 2;
         if (S < 1)
             S = 1;
-        // More blocks than CUs with 16 row groups per block, the last round
-        // of workgroups at most a quarter full: the balanced kernel on
-        // `target` workgroups.  Only for rows on 128-byte lines: otherwise
-        // neighbouring blocks share a line in every row, which the one
-        // workgroup per block order reads once per XCD while the blocks
-        // run side by side, and the balanced order reads once per block.
-        // (Measured on MI355X, 256 MiB fp32 tiles: 257 blocks 55.5 -> 47.3
-        // us, 272 blocks 60.5 -> 47.2, 313 blocks 50.1 -> 46.4; 384 blocks
-        // 49.3 -> 50.2, 640 blocks 49.4 -> 50.9; 641 blocks of unaligned
-        // rows 61.3 -> 91.5.)
-        const bool lines = (((uintptr_t)src & 127u) == 0) && ((ld * es) % 128 == 0);
-        if (lines && p.group_rows == groups && p.col_blocks > target &&
-            p.col_blocks % target != 0 && (p.col_blocks % target) * 4 <= target) {
-            const uint64_t chunk = groups * kRowsInFlight;
-            const uint64_t nc = (R + chunk - 1) / chunk;
-            const uint64_t U = (uint64_t)p.col_blocks * nc;
-            const uint64_t G = target;
-            uint64_t segs = 1;
-            bool shared = false;
-            for (uint64_t w = 0; w < G; ++w) {
-                const uint64_t lo = w * U / G, hi = (w + 1) * U / G;
-                if (hi > lo) {
-                    const uint64_t n = (hi - 1) / nc - lo / nc + 1;
-                    if (n > segs)
-                        segs = n;
-                }
-                if (w > 0 && lo % nc != 0)
-                    shared = true;
-            }
-            if (G * segs * cols * 4 <= ws.partial_bytes) {
-                p.balanced_grid = (unsigned)G;
-                p.balanced_segs = (unsigned)segs;
-                p.balanced_shared = shared;
-                p.splits = 1;
-                p.partial_bytes = shared ? G * segs * cols * 4 : 0;
-                return p;
-            }
-        }
         // Wide strips: the most vectors per lane that still give every CU a
         // workgroup of whole blocks.
         if (vec && p.group_rows == 1 && S == 1) {

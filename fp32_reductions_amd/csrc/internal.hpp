@@ -76,15 +76,12 @@ struct ColprodPlan {
     unsigned col_blocks = 0;  // 256-byte column blocks
     unsigned group_rows = 16; // row groups per column block (1, 4 or 16)
     unsigned splits = 1;      // workgroups along the rows (S)
-    size_t partial_bytes = 0; // S * C * 4 when S > 1; the balanced kernel's rows when a block is shared
+    size_t partial_bytes = 0; // S * C * 4 when S > 1
     unsigned narrow_w = 0;    // units per row when the narrow-row kernel runs, else 0
     bool narrow_vec = false;  // its unit: a 16-byte vector (true) or one element
     unsigned wide_vpl = 0;    // vectors per lane of the wide-strip kernel, 0 when it does not run
     unsigned full_strips = 0; // its workgroups that own whole strips
     unsigned wide_grid = 0;   // its grid (full strips, then the remaining blocks)
-    unsigned balanced_grid = 0;   // workgroups of the balanced kernel (more blocks than CUs)
-    unsigned balanced_segs = 0;   // its workspace rows per workgroup; 0 when it does not run
-    bool balanced_shared = false; // some block is shared: its second pass runs
     unsigned finish_blocks = 0;     // second-pass workgroups (S > 1)
     unsigned finish_cols_log2 = 0;  // log2 of the columns per second-pass workgroup
 };

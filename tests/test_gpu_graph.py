@@ -101,9 +101,9 @@ def test_graph_replay_tile_layouts(red):
     rows read as 16-byte vectors and as elements (each with a second pass
     over several row shares), a short, wide tile on the wide-strip kernel,
     a tile whose rows do not start on 128-byte lines (XCD-contiguous order,
-    rows shared with a second pass), a tile of 257 column blocks on the
-    balanced kernel (blocks shared by workgroups, second pass), rows of 3
-    elements (eight per thread) and padded rows of 20 staged as one span."""
+    rows shared with a second pass), a tile of 257 column blocks whose rows
+    are split 6 ways (second pass), rows of 3 elements (eight per thread)
+    and padded rows of 20 staged as one span."""
     say("graph capture of tile-layout calls and 4 replays")
     dev = "cuda"
     narrow_v = torch.empty((100000, 16), dtype=torch.float32, device=dev)

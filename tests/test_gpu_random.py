@@ -174,6 +174,55 @@ def test_random_columns(red, orc):
             check_rel(got, want, COLPROD_16_TOL, what)
 
 
+def _at(a, o):
+    flat = np.zeros(a.size + o + 8, a.dtype)
+    flat[o:o + a.size] = a.reshape(-1)
+    return dev(flat)[o:o + a.size].view(*a.shape)
+
+
+def column_case(red, orc, rng, kind, R, C, ld, off, doff, what):
+    """One column call of `kind` on a seeded (R, ld) tile starting `off`
+    elements into its buffer, dst `doff` elements in; checked against the
+    oracle."""
+    if kind == "i32":
+        src = rng.integers(-(2 ** 31), 2 ** 31, (R, ld), dtype=np.int64).astype(np.int32) | 1
+        out = torch.zeros(C + doff, dtype=torch.int32, device="cuda")[doff:]
+        red.colprod_i32(_at(src, off), out, C=C)
+        assert (host(out) == orc.colprod_i32(src, R, C, ld)).all(), what
+    elif kind in ("sum", "max", "min"):
+        x = rng.uniform(-1, 1, (R, ld)).astype(np.float32)
+        x[:, C:] = np.nan
+        accum = bool(rng.integers(0, 2))
+        old = rng.uniform(-3, 3, C).astype(np.float32)
+        out = _at(old.copy(), doff)
+        getattr(red, kind + "_cols_f32")(_at(x, off), out, C=C, accum=accum)
+        got = host(out)
+        if kind == "sum":
+            s, a = orc.cols_sum_f32(x, R, C, ld, accum, old)
+            assert (np.abs(got.astype(np.float64) - s) <= 1e-6 * a).all(), what
+        else:
+            want = getattr(orc, "cols_%s_f32" % kind)(x, R, C, ld, accum, old)
+            eq = (got.view(np.uint32) == want.view(np.uint32)) | ((got == 0) & (want == 0))
+            assert eq.all(), what
+    else:
+        rare = 2e-5 if kind == "f16" else 2e-4
+        u = rng.random((R, ld))
+        x = np.where(u < rare, 2.0, np.where(u < 2 * rare, 0.5, 1.0))
+        x = (x * np.where(rng.random((R, ld)) < 0.5, -1.0, 1.0)).astype(np.float32)
+        x[:, C:] = np.nan
+        if kind == "f32":
+            out = torch.zeros(C + doff, dtype=torch.float32, device="cuda")[doff:]
+            red.colprod_f32(_at(x, off), out, C=C)
+            check_rel(host(out), orc.colprod_f32(x, R, C, ld), COLPROD_F32_TOL, what)
+        else:
+            tdt = torch.bfloat16 if kind == "bf16" else torch.float16
+            bits = torch.from_numpy(x).to(tdt).view(torch.int16).numpy().view(np.uint16)
+            out = torch.zeros(C + doff, dtype=tdt, device="cuda")[doff:]
+            getattr(red, "colprod_" + kind)(_at(bits.view(np.int16), off).view(tdt), out, C=C)
+            want = getattr(orc, "colprod_" + kind)(bits, R, C, ld)
+            check_rel(host(out.float()), want, COLPROD_16_TOL, what)
+
+
 def test_random_column_paths(red, orc):
     """Column cases drawn per layout class: narrow rows (16-byte vectors or
     elements), short and wide tiles (several blocks per workgroup, wide
@@ -201,46 +250,29 @@ def test_random_column_paths(red, orc):
         what = "col path case %d kind=%s R=%d C=%d ld=%d off=%d doff=%d" % (
             case, kind, R, C, ld, off, doff)
         say(what)
+        column_case(red, orc, rng, kind, R, C, ld, off, doff, what)
 
-        def at(a, o):
-            flat = np.zeros(a.size + o + 8, a.dtype)
-            flat[o:o + a.size] = a.reshape(-1)
-            return dev(flat)[o:o + a.size].view(*a.shape)
 
-        if kind == "i32":
-            src = rng.integers(-(2 ** 31), 2 ** 31, (R, ld), dtype=np.int64).astype(np.int32) | 1
-            out = torch.zeros(C + doff, dtype=torch.int32, device="cuda")[doff:]
-            red.colprod_i32(at(src, off), out, C=C)
-            assert (host(out) == orc.colprod_i32(src, R, C, ld)).all(), what
-        elif kind in ("sum", "max", "min"):
-            x = rng.uniform(-1, 1, (R, ld)).astype(np.float32)
-            x[:, C:] = np.nan
-            accum = bool(rng.integers(0, 2))
-            old = rng.uniform(-3, 3, C).astype(np.float32)
-            out = at(old.copy(), doff)
-            getattr(red, kind + "_cols_f32")(at(x, off), out, C=C, accum=accum)
-            got = host(out)
-            if kind == "sum":
-                s, a = orc.cols_sum_f32(x, R, C, ld, accum, old)
-                assert (np.abs(got.astype(np.float64) - s) <= 1e-6 * a).all(), what
-            else:
-                want = getattr(orc, "cols_%s_f32" % kind)(x, R, C, ld, accum, old)
-                eq = (got.view(np.uint32) == want.view(np.uint32)) | ((got == 0) & (want == 0))
-                assert eq.all(), what
-        else:
-            rare = 2e-5 if kind == "f16" else 2e-4
-            u = rng.random((R, ld))
-            x = np.where(u < rare, 2.0, np.where(u < 2 * rare, 0.5, 1.0))
-            x = (x * np.where(rng.random((R, ld)) < 0.5, -1.0, 1.0)).astype(np.float32)
-            x[:, C:] = np.nan
-            if kind == "f32":
-                out = torch.zeros(C + doff, dtype=torch.float32, device="cuda")[doff:]
-                red.colprod_f32(at(x, off), out, C=C)
-                check_rel(host(out), orc.colprod_f32(x, R, C, ld), COLPROD_F32_TOL, what)
-            else:
-                tdt = torch.bfloat16 if kind == "bf16" else torch.float16
-                bits = torch.from_numpy(x).to(tdt).view(torch.int16).numpy().view(np.uint16)
-                out = torch.zeros(C + doff, dtype=tdt, device="cuda")[doff:]
-                getattr(red, "colprod_" + kind)(at(bits.view(np.int16), off).view(tdt), out, C=C)
-                want = getattr(orc, "colprod_" + kind)(bits, R, C, ld)
-                check_rel(host(out.float()), want, COLPROD_16_TOL, what)
+def test_random_overrun_tiles(red, orc):
+    """Column cases whose workgroups overrun one, two or three multiples of
+    256 by at most 64 (blocks of 64 four-byte or 128 two-byte columns, 16
+    row groups each), rows on 128-byte lines (strides rounded up to 128
+    bytes, offsets of whole lines), row counts from one chunk of 128 to
+    many, and random dst offsets and accum."""
+    rng = np.random.default_rng(9005)
+    kinds = ["f32", "i32", "bf16", "f16", "sum", "max", "min"]
+    for case in range(28):
+        kind = kinds[case % 7]
+        es = 2 if kind in ("bf16", "f16") else 4
+        cols = 256 // es
+        blocks = 256 * int(rng.integers(1, 4)) + int(rng.integers(1, 65))
+        C = (blocks - 1) * cols + int(rng.integers(1, cols + 1))
+        line = 128 // es
+        ld = -(-C // line) * line + line * int(rng.integers(0, 2))
+        R = max(1, min(log_uniform(rng, 1, 3000), 16_000_000 // ld))
+        off = line * int(rng.integers(0, 3))
+        doff = int(rng.integers(0, 2)) * int(rng.integers(0, 3))
+        what = "overrun case %d kind=%s R=%d C=%d (%d blocks) ld=%d off=%d doff=%d" % (
+            case, kind, R, C, blocks, ld, off, doff)
+        say(what)
+        column_case(red, orc, rng, kind, R, C, ld, off, doff, what)

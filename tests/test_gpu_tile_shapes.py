@@ -13,15 +13,14 @@ second pass.  Products over long columns use factors +-1 with rare +-2
 and +-0.5, so that the exact product stays in range and every order of
 multiplication gives it exactly.
 
-Tiles of 257 to 1020 column blocks (more than the 256 CUs, too few for
-4 row groups per block) whose rows lie on 128-byte lines and whose last
-round of workgroups would be at most a quarter full take the balanced
-kernel: 256 workgroups each walk an equal run of (block, 128-row chunk)
-units, and blocks shared by several workgroups are finished by a second
-pass.  The cases cover block counts just over one, two and three
-multiples of 256, row counts of one chunk (no shared block) and of many,
-ragged last blocks, unaligned destinations and accum, and tiles that
-miss one of the conditions and keep one workgroup per block.
+Tiles whose workgroups (one per 16-row-group block, or per four blocks of
+4 row groups) overrun a multiple of the 256 CUs by at most a quarter of it
+and whose rows lie on 128-byte lines split their rows into 6 shares and
+take the second pass, so that the last round of workgroups is short; each
+share needs at least one 32 KiB chunk per workgroup.  The cases cover block counts just over one, two and three
+multiples of 256 and over 1024 (4 row groups per block), 6 to 24 chunks,
+ragged last blocks, unaligned destinations and accum, and tiles that miss
+one of the conditions and keep one share.
 
 Short, wide tiles (thousands of 256-byte column blocks) give a workgroup
 several adjacent column blocks with 4 or 1 row groups each, and with
@@ -277,54 +276,56 @@ def test_wide_cols_dst_alignment(red, orc, op, accum, dst_off):
     cols_case(red, orc, op, 5, 1_048_576, 1_048_576, accum, 1700, 0, dst_off)
 
 
-# (rows, columns, stride): 257 to 785 blocks of 64 (4-byte) columns on
-# 128-byte lines, with rows spanning 1 to 24 chunks of 128 and ragged last
-# blocks; then tiles that keep one workgroup per block: unaligned rows, and
-# a last round more than a quarter full.
-BALANCED = [
-    (1000, 16448, 16448), (517, 17405, 17408), (129, 20032, 20032), (64, 19008, 19008),
-    (1500, 33000, 33024), (3000, 36800, 36800), (2, 49216, 49216), (300, 49153, 49184),
-    (255, 50200, 50208),
+# (rows, columns, stride): 257 to 769 blocks of 64 (4-byte) columns on
+# 128-byte lines, with rows spanning 6 to 24 chunks and ragged last blocks;
+# 1100 and 2100 blocks of 4 row groups; then tiles that keep one share:
+# fewer than six chunks, unaligned rows, a last round more than a quarter
+# full.
+OVERRUN = [
+    (1000, 16448, 16448), (800, 17405, 17408), (1500, 33000, 33024), (3000, 36800, 36800),
+    (770, 49153, 49184), (200, 70400, 70400), (300, 134390, 134400),
+    (129, 20032, 20032), (64, 19008, 19008), (2, 49216, 49216),
     (1000, 16448, 16451), (127, 25000, 25001), (400, 24640, 24640), (2, 65000, 65024),
 ]
 
 
-@pytest.mark.parametrize("R,C,ld", BALANCED)
+@pytest.mark.parametrize("R,C,ld", OVERRUN)
 @pytest.mark.parametrize("kind", ["f32", "i32"])
-def test_balanced_4byte(red, orc, kind, R, C, ld):
+def test_overrun_4byte(red, orc, kind, R, C, ld):
     colprod_case(red, orc, kind, R, C, ld, 1800 + R)
 
 
-# 2-byte elements: 257 to 782 blocks of 128 columns on 128-byte lines, and
-# one unaligned tile.
-BALANCED16 = [(1000, 32896, 32896), (777, 40000, 40000), (3000, 70001, 70016),
-              (3, 100000, 100032), (500, 40000, 40001)]
+# 2-byte elements: 257 to 782 blocks of 128 columns on 128-byte lines, 1100
+# blocks of 4 row groups, and one unaligned tile.
+OVERRUN16 = [(1000, 32896, 32896), (777, 40000, 40000), (3000, 70001, 70016),
+             (3, 100000, 100032), (300, 140800, 140800), (500, 40000, 40001)]
 
 
-@pytest.mark.parametrize("R,C,ld", BALANCED16)
+@pytest.mark.parametrize("R,C,ld", OVERRUN16)
 @pytest.mark.parametrize("kind", ["f16", "bf16"])
-def test_balanced_2byte(red, orc, kind, R, C, ld):
+def test_overrun_2byte(red, orc, kind, R, C, ld):
     colprod_case(red, orc, kind, R, C, ld, 1900 + R)
 
 
 # off = 32 keeps 128-byte lines; off = 1 moves the rows off them.
-@pytest.mark.parametrize("R,C,ld,off", [(1000, 16448, 16448, 0), (517, 17405, 17408, 32),
+@pytest.mark.parametrize("R,C,ld,off", [(1000, 16448, 16448, 0), (800, 17405, 17408, 32),
                                         (1500, 33000, 33024, 0), (2, 49216, 49216, 0),
-                                        (3000, 36800, 36800, 0), (300, 49153, 49184, 1)])
+                                        (3000, 36800, 36800, 0), (770, 49153, 49184, 1),
+                                        (200, 70400, 70400, 0)])
 @pytest.mark.parametrize("op", ["sum", "max", "min"])
 @pytest.mark.parametrize("accum", [0, 1])
-def test_balanced_cols(red, orc, op, R, C, ld, off, accum):
+def test_overrun_cols(red, orc, op, R, C, ld, off, accum):
     cols_case(red, orc, op, R, C, ld, accum, 2000 + R, off)
 
 
 @pytest.mark.parametrize("dst_off", [1, 3])
 @pytest.mark.parametrize("kind", ["f32", "i32", "bf16", "f16"])
-def test_balanced_dst_alignment(red, orc, kind, dst_off):
+def test_overrun_dst_alignment(red, orc, kind, dst_off):
     R, C, ld = (700, 20000, 20000) if kind in ("f32", "i32") else (700, 40000, 40000)
     colprod_case(red, orc, kind, R, C, ld, 2100, 0, dst_off)
 
 
 @pytest.mark.parametrize("dst_off", [0, 1])
 @pytest.mark.parametrize("accum", [0, 1])
-def test_balanced_cols_dst_alignment(red, orc, accum, dst_off):
+def test_overrun_cols_dst_alignment(red, orc, accum, dst_off):
     cols_case(red, orc, "sum", 1000, 16448, 16448, accum, 2200, 0, dst_off)
