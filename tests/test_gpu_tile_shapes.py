@@ -22,6 +22,14 @@ multiples of 256 and over 1024 (4 row groups per block), 6 to 24 chunks,
 ragged last blocks, unaligned destinations and accum, and tiles that miss
 one of the conditions and keep one share.
 
+Rows that are not 16-byte aligned (an odd stride, a stride of 2 or 3
+elements past a multiple of four, a misaligned start) meet each column
+block at an offset within a 16-byte vector that depends on the row (on
+every fourth or eighth row the same).  The cases cover every such offset
+for 4-byte and 2-byte elements, ragged last blocks, a block count of one,
+leftover rows, row splits, NaN padding, accum and misaligned
+destinations.
+
 Short, wide tiles (thousands of 256-byte column blocks) give a workgroup
 several adjacent column blocks with 4 or 1 row groups each, and with
 more blocks still a wide strip in which each lane reads 2, 4 or 8
@@ -329,3 +337,49 @@ def test_overrun_dst_alignment(red, orc, kind, dst_off):
 @pytest.mark.parametrize("accum", [0, 1])
 def test_overrun_cols_dst_alignment(red, orc, accum, dst_off):
     cols_case(red, orc, "sum", 1000, 16448, 16448, accum, 2200, 0, dst_off)
+
+
+# (rows, columns, stride, offset in elements): strides of every residue mod
+# 4, starts of every residue, ragged last blocks, one to 256 blocks.
+ROWOFF4 = [
+    (1000, 16383, 16383, 0), (777, 16384, 16385, 0), (300, 16384, 16386, 0),
+    (129, 1000, 1001, 1), (128, 1001, 1003, 2), (17, 255, 255, 3), (5000, 130, 130, 1),
+    (16, 65, 67, 3), (1, 100, 101, 1), (3, 64, 64, 1), (250, 4097, 4097, 0),
+    (2049, 333, 335, 2), (40000, 70, 71, 0),
+]
+
+
+@pytest.mark.parametrize("R,C,ld,off", ROWOFF4)
+@pytest.mark.parametrize("kind", ["f32", "i32"])
+def test_row_offsets_4byte(red, orc, kind, R, C, ld, off):
+    colprod_case(red, orc, kind, R, C, ld, 2300 + R, off)
+
+
+# 2-byte elements: strides of every residue mod 8, starts of every residue.
+ROWOFF2 = [
+    (1000, 32767, 32767, 0), (500, 32768, 32769, 0), (500, 32768, 32771, 0),
+    (500, 32768, 32773, 0), (300, 1000, 1002, 1), (129, 1001, 1006, 3), (17, 255, 255, 5),
+    (5000, 200, 203, 7), (1, 129, 131, 1), (250, 4097, 4097, 2), (2049, 333, 340, 6),
+    (64, 4000, 4004, 4),
+]
+
+
+@pytest.mark.parametrize("R,C,ld,off", ROWOFF2)
+@pytest.mark.parametrize("kind", ["f16", "bf16"])
+def test_row_offsets_2byte(red, orc, kind, R, C, ld, off):
+    colprod_case(red, orc, kind, R, C, ld, 2400 + R, off)
+
+
+@pytest.mark.parametrize("R,C,ld,off", [(1000, 16383, 16383, 0), (129, 1000, 1001, 1),
+                                        (5000, 130, 130, 1), (16, 65, 67, 3),
+                                        (2049, 333, 335, 2), (40000, 70, 71, 0)])
+@pytest.mark.parametrize("op", ["sum", "max", "min"])
+@pytest.mark.parametrize("accum", [0, 1])
+def test_row_offsets_cols(red, orc, op, R, C, ld, off, accum):
+    cols_case(red, orc, op, R, C, ld, accum, 2500 + R, off)
+
+
+@pytest.mark.parametrize("dst_off", [1, 3])
+@pytest.mark.parametrize("kind", ["f32", "i32", "bf16", "f16"])
+def test_row_offsets_dst_alignment(red, orc, kind, dst_off):
+    colprod_case(red, orc, kind, 700, 5001, 5003, 2600, 1, dst_off)
