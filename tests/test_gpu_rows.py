@@ -110,10 +110,14 @@ SHAPES = [  # (rows, n, ld, element offset of the base pointer)
     (1000, 300, 300, 3), (31, 511, 511, 2), (4099, 512, 512, 0), (9, 513, 515, 1),
     (70, 700, 701, 0), (5, 1023, 1023, 3), (300, 1024, 1024, 0),
     (300000, 100, 100, 0), (70001, 384, 384, 1),
-    # 17 to 64 elements staged as one span (stride <= 64): unaligned starts,
-    # padding, and the last tile cut short
+    # 17 to 64 elements staged as one span (stride <= 64, or <= 128 with
+    # padding of at most an eighth of the row): unaligned starts, padding,
+    # and the last tile cut short; then strides just past that rule, read
+    # element by element
     (5000, 40, 40, 1), (777, 64, 64, 3), (3000, 17, 18, 1), (2049, 33, 36, 0),
     (129, 50, 64, 2), (100_001, 24, 28, 0),
+    (3000, 64, 65, 0), (777, 64, 72, 1), (2049, 60, 67, 3), (5000, 40, 45, 2),
+    (100_001, 33, 37, 0), (300, 64, 73, 0), (1000, 48, 60, 1),
     # long rows: split into chunks per row (with and without a second pass)
     (5, 300000, 300001, 1), (600, 20000, 20000, 0), (100, 5000, 5003, 2),
     (3000, 2000, 2000, 0), (1, (1 << 22) + 3, (1 << 22) + 3, 0), (37, 65536, 65540, 3),
