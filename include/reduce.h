@@ -138,8 +138,9 @@ int red_min_f32_atomic(const float* x, size_t n, float* out, int accum,
  * x      : row-major fp32 matrix, 4-byte aligned; row r starts at x + r*ld.
  *          Elements between n and ld in a row never affect the result.
  *          Nothing past the last row's n-th element is read; rows of 17
- *          to 64 elements with ld <= 64 are read as one span, padding
- *          included, and the padding is dropped.
+ *          to 64 elements with ld <= 64, or with ld <= 128 and
+ *          ld - n <= n / 8, are read as one span, padding included, and
+ *          the padding is dropped.
  * rows   : number of rows; n : elements reduced per row; ld : row stride
  *          in elements, ld >= n (RED_ERR_INVALID otherwise).
  * out    : rows fp32 values, 4-byte aligned.
