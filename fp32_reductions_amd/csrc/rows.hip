@@ -332,8 +332,11 @@ __host__ __device__ inline uint32_t tile_stride(uint64_t n, uint64_t ld, int spa
 // the last row's n-th) into the LDS tile, span row i at tile + i * stride,
 // in 16-byte loads at any 4-byte alignment.  PAD: the L - n padding
 // elements of each row are dropped (stride >= n); otherwise every element
-// is copied (stride > L).
-template <bool PAD>
+// is copied (stride > L).  WHOLE (L a multiple of 4): no 16-byte vector of
+// the span crosses a row, so each goes to one row at one offset.  (Measured
+// on MI355X, 256 MiB of rows, row test per element -> WHOLE: contiguous
+// 64-element rows 52.2 -> 44.3 us, 60 of stride 64 52.9 -> 45.2 us.)
+template <bool PAD, bool WHOLE>
 __device__ __forceinline__ void stage_span(const float* __restrict__ x, uint32_t T,
                                            uint32_t n, uint32_t L, uint64_t inv_ld,
                                            float* __restrict__ tile, uint32_t stride)
@@ -360,13 +363,21 @@ __device__ __forceinline__ void stage_span(const float* __restrict__ x, uint32_t
                 const uint32_t e = 4 * f;
                 uint32_t row = (uint32_t)(((uint64_t)e * inv_ld) >> 32);
                 uint32_t col = e - row * L;
+                if constexpr (WHOLE) {
+                    float* __restrict__ d = tile + row * stride + col;
 #pragma unroll
-                for (int c = 0; c < 4; ++c) {
-                    if (!PAD || col < n)
-                        tile[row * stride + col] = v[b][c];
-                    if (++col == L) {
-                        col = 0;
-                        ++row;
+                    for (int c = 0; c < 4; ++c)
+                        if (!PAD || col + c < n)
+                            d[c] = v[b][c];
+                } else {
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) {
+                        if (!PAD || col < n)
+                            tile[row * stride + col] = v[b][c];
+                        if (++col == L) {
+                            col = 0;
+                            ++row;
+                        }
                     }
                 }
             }
@@ -430,10 +441,14 @@ __global__ __launch_bounds__(kTileThreads) void rows_tile_kernel(
         if (span) {
             if (stride == ld)
                 stage_span_direct(x + r0 * ld, T, n, (uint32_t)ld, tile);
+            else if (stride == (ld | 1u) && ld % 4 == 0)
+                stage_span<false, true>(x + r0 * ld, T, n, (uint32_t)ld, inv_ld, tile, stride);
             else if (stride == (ld | 1u))
-                stage_span<false>(x + r0 * ld, T, n, (uint32_t)ld, inv_ld, tile, stride);
+                stage_span<false, false>(x + r0 * ld, T, n, (uint32_t)ld, inv_ld, tile, stride);
+            else if (ld % 4 == 0)
+                stage_span<true, true>(x + r0 * ld, T, n, (uint32_t)ld, inv_ld, tile, stride);
             else
-                stage_span<true>(x + r0 * ld, T, n, (uint32_t)ld, inv_ld, tile, stride);
+                stage_span<true, false>(x + r0 * ld, T, n, (uint32_t)ld, inv_ld, tile, stride);
         } else {
             for (uint32_t e0 = 0; e0 < total; e0 += 2 * kTileBatch * kTileThreads) {
                 float v[2 * kTileBatch];
