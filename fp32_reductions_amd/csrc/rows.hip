@@ -332,11 +332,14 @@ __host__ __device__ inline uint32_t tile_stride(uint64_t n, uint64_t ld, int spa
 // the last row's n-th) into the LDS tile, span row i at tile + i * stride,
 // in 16-byte loads at any 4-byte alignment.  PAD: the L - n padding
 // elements of each row are dropped (stride >= n); otherwise every element
-// is copied (stride > L).  WHOLE (L a multiple of 4): no 16-byte vector of
-// the span crosses a row, so each goes to one row at one offset.  (Measured
-// on MI355X, 256 MiB of rows, row test per element -> WHOLE: contiguous
-// 64-element rows 52.2 -> 44.3 us, 60 of stride 64 52.9 -> 45.2 us.)
-template <bool PAD, bool WHOLE>
+// is copied (stride > L).  PIECE = 4 (L a multiple of 4): no 16-byte
+// vector of the span crosses a row, so each goes to one row at one
+// offset; PIECE = 2 (L even): each half of a vector stays in one row;
+// PIECE = 1: elements one at a time, moving to the next row at its end.
+// (Measured on MI355X, 256 MiB of rows, elements one at a time -> PIECE 4:
+// contiguous 64-element rows 52.2 -> 44.3 us, 60 of stride 64 52.9 -> 45.2
+// us.)
+template <bool PAD, int PIECE>
 __device__ __forceinline__ void stage_span(const float* __restrict__ x, uint32_t T,
                                            uint32_t n, uint32_t L, uint64_t inv_ld,
                                            float* __restrict__ tile, uint32_t stride)
@@ -363,12 +366,28 @@ __device__ __forceinline__ void stage_span(const float* __restrict__ x, uint32_t
                 const uint32_t e = 4 * f;
                 uint32_t row = (uint32_t)(((uint64_t)e * inv_ld) >> 32);
                 uint32_t col = e - row * L;
-                if constexpr (WHOLE) {
+                if constexpr (PIECE == 4) {
                     float* __restrict__ d = tile + row * stride + col;
 #pragma unroll
                     for (int c = 0; c < 4; ++c)
                         if (!PAD || col + c < n)
                             d[c] = v[b][c];
+                } else if constexpr (PIECE == 2) {
+#pragma unroll
+                    for (int h = 0; h < 4; h += 2) {
+                        if (h == 2) {
+                            col += 2;
+                            if (col == L) {
+                                col = 0;
+                                ++row;
+                            }
+                        }
+                        float* __restrict__ d = tile + row * stride + col;
+                        if (!PAD || col < n)
+                            d[0] = v[b][h];
+                        if (!PAD || col + 1 < n)
+                            d[1] = v[b][h + 1];
+                    }
                 } else {
 #pragma unroll
                     for (int c = 0; c < 4; ++c) {
@@ -426,6 +445,21 @@ __device__ __forceinline__ void stage_span_direct(const float* __restrict__ x, u
         tile[e] = x[e];
 }
 
+// stage_span with the widest piece the row stride allows (ld is even here:
+// odd strides go to LDS unchanged).
+template <bool PAD>
+__device__ __forceinline__ void span_copy(const float* __restrict__ x, uint32_t T,
+                                          uint32_t n, uint32_t L, uint64_t inv_ld,
+                                          float* __restrict__ tile, uint32_t stride)
+{
+    if (L % 4 == 0)
+        stage_span<PAD, 4>(x, T, n, L, inv_ld, tile, stride);
+    else if (L % 2 == 0)
+        stage_span<PAD, 2>(x, T, n, L, inv_ld, tile, stride);
+    else
+        stage_span<PAD, 1>(x, T, n, L, inv_ld, tile, stride);
+}
+
 template <class Op>
 __global__ __launch_bounds__(kTileThreads) void rows_tile_kernel(
     const float* __restrict__ x, uint64_t rows, uint32_t n, uint64_t ld,
@@ -441,14 +475,10 @@ __global__ __launch_bounds__(kTileThreads) void rows_tile_kernel(
         if (span) {
             if (stride == ld)
                 stage_span_direct(x + r0 * ld, T, n, (uint32_t)ld, tile);
-            else if (stride == (ld | 1u) && ld % 4 == 0)
-                stage_span<false, true>(x + r0 * ld, T, n, (uint32_t)ld, inv_ld, tile, stride);
             else if (stride == (ld | 1u))
-                stage_span<false, false>(x + r0 * ld, T, n, (uint32_t)ld, inv_ld, tile, stride);
-            else if (ld % 4 == 0)
-                stage_span<true, true>(x + r0 * ld, T, n, (uint32_t)ld, inv_ld, tile, stride);
+                span_copy<false>(x + r0 * ld, T, n, (uint32_t)ld, inv_ld, tile, stride);
             else
-                stage_span<true, false>(x + r0 * ld, T, n, (uint32_t)ld, inv_ld, tile, stride);
+                span_copy<true>(x + r0 * ld, T, n, (uint32_t)ld, inv_ld, tile, stride);
         } else {
             for (uint32_t e0 = 0; e0 < total; e0 += 2 * kTileBatch * kTileThreads) {
                 float v[2 * kTileBatch];

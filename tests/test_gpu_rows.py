@@ -118,7 +118,7 @@ SHAPES = [  # (rows, n, ld, element offset of the base pointer)
     (129, 50, 64, 2), (100_001, 24, 28, 0),
     (3000, 64, 65, 0), (777, 64, 72, 1), (2049, 60, 67, 3), (5000, 40, 45, 2),
     (100_001, 33, 37, 0), (300, 64, 73, 0), (1000, 48, 60, 1), (2000, 17, 33, 1),
-    (999, 20, 24, 3),
+    (999, 20, 24, 3), (7001, 30, 30, 2), (2049, 62, 62, 0), (1000, 26, 30, 1),
     # long rows: split into chunks per row (with and without a second pass)
     (5, 300000, 300001, 1), (600, 20000, 20000, 0), (100, 5000, 5003, 2),
     (3000, 2000, 2000, 0), (1, (1 << 22) + 3, (1 << 22) + 3, 0), (37, 65536, 65540, 3),
