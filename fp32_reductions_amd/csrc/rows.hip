@@ -291,13 +291,12 @@ constexpr uint64_t kDirectRowMax = 16; // rows this short are read by their thre
 // below) the tile is read as one contiguous run, from its first
 // row's first element to its last row's last valid element, in 16-byte
 // non-temporal loads at any 4-byte alignment (gfx950 reads unaligned
-// multi-dword vectors from global memory), and the ld - n padding elements
-// between rows are dropped on the way into LDS; longer strides read the
-// valid elements one by one.  (Measured on MI355X, 256 MiB of rows from
+// multi-dword vectors from global memory); longer strides read each row's
+// whole vectors and then its last n % 4 elements.  (Measured on MI355X, 256 MiB of rows from
 // HBM: 31-element rows 260 us read directly by their thread, 52 us staged;
 // 33- to 64-element rows 84-204 us direct, 47-57 us staged.  Rows of up to
 // 16 elements are faster read directly: 51.5 us against 58.3 at n = 16.)
-// floor(e / d) for d = n or ld is computed as (e * inv_d) >> 32 with
+// floor(e / d) for d = ld or n / 4 is computed as (e * inv_d) >> 32 with
 // inv_d = ceil(2^32 / d), exact for e < 2^14 and d <= 128 (checked
 // exhaustively).
 // Staging reads the whole span, padding included, when the row stride is
@@ -460,10 +459,70 @@ __device__ __forceinline__ void span_copy(const float* __restrict__ x, uint32_t 
         stage_span<PAD, 1>(x, T, n, L, inv_ld, tile, stride);
 }
 
+// Rows too far apart for a span: each row's whole 16-byte vectors (n / 4
+// of them, at any 4-byte alignment) and then its n % 4 last elements one
+// at a time, so nothing past a row's n-th element is read.  (Measured on
+// MI355X, 256 MiB of rows, element loads -> vectors: 64 of stride 80 77.0
+// -> 45.0 us, 48 of stride 100 43.5 -> 35.1 us.)
+__device__ __forceinline__ void stage_rows(const float* __restrict__ x, uint32_t T,
+                                           uint32_t n, uint64_t ld,
+                                           float* __restrict__ tile, uint32_t stride)
+{
+    typedef float f4u __attribute__((ext_vector_type(4), aligned(4)));
+    const uint32_t t = threadIdx.x;
+    const uint32_t nw = n / 4; // at least 4: n > 16
+    const uint64_t inv_nw = ((1ull << 32) + nw - 1) / nw;
+    const uint32_t units = T * nw;
+    // The last n % 4 elements of each row (T * (n % 4) <= 3 * kTileThreads
+    // of them): requested first, stored after the vectors.
+    static_assert(kTileRows <= kTileThreads, "three leftover elements per thread at most");
+    const uint32_t rem = n - 4 * nw;
+    float rv[3];
+    uint32_t rdst[3];
+#pragma unroll
+    for (int k = 0; k < 3; ++k) {
+        const uint32_t e = t + (uint32_t)k * kTileThreads;
+        const bool ok = e < T * rem;
+        const uint32_t row = rem == 1 ? e : (rem == 2 ? e >> 1 : (e * 43691u) >> 17); // e / rem, e < 2^15
+        const uint32_t col = 4 * nw + (e - row * rem);
+        rv[k] = x[ok ? row * ld + col : 0];
+        rdst[k] = ok ? row * stride + col : ~0u;
+    }
+    for (uint32_t u0 = 0; u0 < units; u0 += kTileBatch * kTileThreads) {
+        f4u v[kTileBatch];
+#pragma unroll
+        for (int b = 0; b < kTileBatch; ++b) {
+            const uint32_t u = u0 + b * kTileThreads + t;
+            const uint32_t uc = u < units ? u : 0; // past the end: vector 0 again
+            const uint32_t row = (uint32_t)(((uint64_t)uc * inv_nw) >> 32);
+            const uint32_t j = uc - row * nw;
+            v[b] = __builtin_nontemporal_load(
+                reinterpret_cast<const f4u*>(x + row * ld + 4 * j));
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int b = 0; b < kTileBatch; ++b) {
+            const uint32_t u = u0 + b * kTileThreads + t;
+            if (u < units) {
+                const uint32_t row = (uint32_t)(((uint64_t)u * inv_nw) >> 32);
+                const uint32_t j = u - row * nw;
+                float* __restrict__ d = tile + row * stride + 4 * j;
+#pragma unroll
+                for (int c = 0; c < 4; ++c)
+                    d[c] = v[b][c];
+            }
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < 3; ++k)
+        if (rdst[k] != ~0u)
+            tile[rdst[k]] = rv[k];
+}
+
 template <class Op>
 __global__ __launch_bounds__(kTileThreads) void rows_tile_kernel(
     const float* __restrict__ x, uint64_t rows, uint32_t n, uint64_t ld,
-    float* __restrict__ out, int accum, int span, uint64_t inv_n, uint64_t inv_ld,
+    float* __restrict__ out, int accum, int span, uint64_t inv_ld,
     uint32_t TR)
 {
     extern __shared__ __align__(16) float tile[];
@@ -471,7 +530,6 @@ __global__ __launch_bounds__(kTileThreads) void rows_tile_kernel(
     const uint32_t t = threadIdx.x;
     for (uint64_t r0 = (uint64_t)blockIdx.x * TR; r0 < rows; r0 += (uint64_t)gridDim.x * TR) {
         const uint32_t T = (rows - r0 < TR) ? (uint32_t)(rows - r0) : TR;
-        const uint32_t total = T * n;
         if (span) {
             if (stride == ld)
                 stage_span_direct(x + r0 * ld, T, n, (uint32_t)ld, tile);
@@ -480,25 +538,7 @@ __global__ __launch_bounds__(kTileThreads) void rows_tile_kernel(
             else
                 span_copy<true>(x + r0 * ld, T, n, (uint32_t)ld, inv_ld, tile, stride);
         } else {
-            for (uint32_t e0 = 0; e0 < total; e0 += 2 * kTileBatch * kTileThreads) {
-                float v[2 * kTileBatch];
-#pragma unroll
-                for (int b = 0; b < 2 * kTileBatch; ++b) {
-                    const uint32_t e = e0 + b * kTileThreads + t;
-                    const uint32_t ec = e < total ? e : 0; // past the end: element 0 again
-                    const uint32_t row = (uint32_t)(((uint64_t)ec * inv_n) >> 32);
-                    v[b] = x[(r0 + row) * ld + (ec - row * n)];
-                }
-                __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-                for (int b = 0; b < 2 * kTileBatch; ++b) {
-                    const uint32_t e = e0 + b * kTileThreads + t;
-                    if (e < total) {
-                        const uint32_t row = (uint32_t)(((uint64_t)e * inv_n) >> 32);
-                        tile[row * stride + (e - row * n)] = v[b];
-                    }
-                }
-            }
+            stage_rows(x + r0 * ld, T, n, ld, tile, stride);
         }
         __syncthreads();
         for (uint32_t i = t; i < T; i += kTileThreads) {
@@ -773,11 +813,10 @@ hipError_t launch_rows_op(const float* x, size_t rows, size_t n, size_t ld,
         const uint64_t cap = (uint64_t)dev.cus * kRowsWgPerCu;
         const unsigned grid = (unsigned)(tiles < cap ? tiles : cap);
         const int span = rows_span(n, ld);
-        const uint64_t inv_n = ((1ull << 32) + n - 1) / n;
         const uint64_t inv_ld = ((1ull << 32) + ld - 1) / ld;
         const size_t lds = (size_t)TR * tile_stride(n, ld, span) * sizeof(float);
         rows_tile_kernel<Op><<<grid, kTileThreads, lds, stream>>>(
-            x, rows, (uint32_t)n, ld, out, accum, span, inv_n, inv_ld, TR);
+            x, rows, (uint32_t)n, ld, out, accum, span, inv_ld, TR);
     } else if (n <= kPairRowMax) {
         // <G lanes per row, U vectors per lane and row, P rows per segment>:
         // 4 * G * U >= n covers the row; U * P = 8 loads per lane in flight.
