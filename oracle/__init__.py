@@ -21,6 +21,7 @@ passage it follows, is stated in ``oracle.c``:
 from __future__ import annotations
 
 import ctypes
+import hashlib
 import os
 import subprocess
 
@@ -32,14 +33,44 @@ LIBRARY = os.path.join(_HERE, "liboracle.so")
 
 # Strict IEEE: no fast-math, no fused multiply-add contraction.
 CFLAGS = ["-O2", "-std=c11", "-fno-fast-math", "-ffp-contract=off",
-          "-fPIC", "-shared"]
+          "-fPIC", "-shared", "-pthread"]
+
+
+def source_digest(source: str = SOURCE) -> str:
+    """SHA-256 of the C source and the compiler flags it is built with."""
+    h = hashlib.sha256()
+    with open(source, "rb") as fh:
+        h.update(fh.read())
+    h.update(" ".join(CFLAGS).encode())
+    return h.hexdigest()
+
+
+def _stamp(library: str) -> str:
+    return library + ".sha256"
 
 
 def build(source: str = SOURCE, library: str = LIBRARY) -> str:
-    """Compile ``source`` with gcc into ``library``; returns the library path."""
+    """Compile ``source`` with gcc into ``library``; returns the library path.
+    The digest of the source is recorded beside the library."""
     tmp = library + ".tmp%d" % os.getpid()
     subprocess.run(["gcc", *CFLAGS, source, "-o", tmp, "-lm"], check=True)
     os.replace(tmp, library)
+    with open(_stamp(library) + ".tmp%d" % os.getpid(), "w") as fh:
+        fh.write(source_digest(source) + "\n")
+    os.replace(_stamp(library) + ".tmp%d" % os.getpid(), _stamp(library))
+    return library
+
+
+def ensure_built(source: str = SOURCE, library: str = LIBRARY) -> str:
+    """The library, rebuilt first when it is missing or was built from a
+    different source (its recorded digest differs from the source's)."""
+    try:
+        with open(_stamp(library)) as fh:
+            recorded = fh.read().strip()
+    except OSError:
+        recorded = None
+    if not os.path.exists(library) or recorded != source_digest(source):
+        build(source, library)
     return library
 
 
@@ -75,6 +106,15 @@ class Oracle:
             "oracle_cols_sum_f32": [_P, _SZ, _SZ, _SZ, _I, _P, _P, _P],
             "oracle_cols_max_f32": [_P, _SZ, _SZ, _SZ, _I, _P],
             "oracle_cols_min_f32": [_P, _SZ, _SZ, _SZ, _I, _P],
+            "oracle_sum_f32_mt": [_P, _SZ, _I, ctypes.c_float, _I, _P, _P],
+            "oracle_max_f32_mt": [_P, _SZ, _I, _I, _P],
+            "oracle_min_f32_mt": [_P, _SZ, _I, _I, _P],
+            "oracle_rows_sum_f32_mt": [_P, _SZ, _SZ, _SZ, _I, _P, _P],
+            "oracle_rows_max_f32_mt": [_P, _SZ, _SZ, _SZ, _I, _P],
+            "oracle_colprod_f32_mt": [_P, _SZ, _SZ, _SZ, _I, _P],
+            "oracle_colprod_f16_mt": [_P, _SZ, _SZ, _SZ, _I, _P],
+            "oracle_colprod_bf16_mt": [_P, _SZ, _SZ, _SZ, _I, _P],
+            "oracle_colprod_i32_mt": [_P, _SZ, _SZ, _SZ, _I, _P],
         }
         for name, args in sig.items():
             fn = getattr(lib, name)
@@ -221,6 +261,74 @@ class Oracle:
         fn(_ptr(src), R, C, ld, int(bool(accum)), _ptr(d))
         return d
 
+    # -- threaded forms (timing on several host cores) -------------------
+    @staticmethod
+    def _mt_status(rc):
+        if rc < 0:
+            raise RuntimeError("oracle: could not start its threads")
+        return rc
+
+    def sum_f32_mt(self, x, threads: int, accum: bool = False, old: float = 0.0):
+        """sum_f32 over `threads` contiguous pieces, combined in order."""
+        x = np.ascontiguousarray(x, dtype=np.float32)
+        s = np.zeros(1, np.float64)
+        a = np.zeros(1, np.float64)
+        ok = self._mt_status(self.lib.oracle_sum_f32_mt(
+            _ptr(x), x.size, int(bool(accum)), float(old), int(threads), _ptr(s), _ptr(a)))
+        return (float(s[0]), float(a[0])) if ok else None
+
+    def _extreme_mt(self, fn, x, threads, accum, old):
+        x = np.ascontiguousarray(x, dtype=np.float32)
+        d = np.array([old], dtype=np.float32)
+        self._mt_status(fn(_ptr(x), x.size, int(bool(accum)), int(threads), _ptr(d)))
+        return d[0]
+
+    def max_f32_mt(self, x, threads: int, accum: bool = False, old: float = 0.0):
+        return self._extreme_mt(self.lib.oracle_max_f32_mt, x, threads, accum, old)
+
+    def min_f32_mt(self, x, threads: int, accum: bool = False, old: float = 0.0):
+        return self._extreme_mt(self.lib.oracle_min_f32_mt, x, threads, accum, old)
+
+    def rows_sum_f32_mt(self, x, rows, n, ld, threads: int):
+        x = self._rows_view(x, rows, n, ld)
+        s = np.zeros(rows, np.float64)
+        a = np.zeros(rows, np.float64)
+        ok = self._mt_status(self.lib.oracle_rows_sum_f32_mt(
+            _ptr(x), rows, n, ld, int(threads), _ptr(s), _ptr(a)))
+        return (s, a) if ok else None
+
+    def rows_max_f32_mt(self, x, rows, n, ld, threads: int):
+        x = self._rows_view(x, rows, n, ld)
+        d = np.zeros(rows, np.float32)
+        self._mt_status(self.lib.oracle_rows_max_f32_mt(_ptr(x), rows, n, ld, int(threads),
+                                                        _ptr(d)))
+        return d
+
+    def _colprod_mt(self, fn, src, R, C, ld, dtype, out_dtype, threads):
+        src = np.ascontiguousarray(src).reshape(-1)
+        assert src.dtype == dtype, (src.dtype, dtype)
+        if R and C:
+            assert src.size >= (R - 1) * ld + C, "buffer too small"
+        d = np.zeros(C, out_dtype)
+        self._mt_status(fn(_ptr(src), R, C, ld, int(threads), _ptr(d)))
+        return d
+
+    def colprod_f32_mt(self, src, R, C, ld, threads: int):
+        return self._colprod_mt(self.lib.oracle_colprod_f32_mt, src, R, C, ld,
+                                np.float32, np.float64, threads)
+
+    def colprod_f16_mt(self, src_bits, R, C, ld, threads: int):
+        return self._colprod_mt(self.lib.oracle_colprod_f16_mt, src_bits, R, C, ld,
+                                np.uint16, np.float64, threads)
+
+    def colprod_bf16_mt(self, src_bits, R, C, ld, threads: int):
+        return self._colprod_mt(self.lib.oracle_colprod_bf16_mt, src_bits, R, C, ld,
+                                np.uint16, np.float64, threads)
+
+    def colprod_i32_mt(self, src, R, C, ld, threads: int):
+        return self._colprod_mt(self.lib.oracle_colprod_i32_mt, src, R, C, ld,
+                                np.int32, np.int32, threads)
+
     def f16_to_f64(self, h: int) -> float:
         return self.lib.oracle_f16_to_f64(h)
 
@@ -232,10 +340,9 @@ _default: Oracle | None = None
 
 
 def get() -> Oracle:
-    """The oracle built from ``oracle.c`` (compiled on first use if absent)."""
+    """The oracle built from the current ``oracle.c`` (compiled on first use
+    when the library is absent or was built from another source)."""
     global _default
     if _default is None:
-        if not os.path.exists(LIBRARY):
-            build()
-        _default = Oracle(LIBRARY)
+        _default = Oracle(ensure_built())
     return _default

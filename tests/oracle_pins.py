@@ -142,6 +142,46 @@ def pin_sum_subnormal(o):
     assert s == 2.0 ** -147
 
 
+def _ieee_seq_sum(terms) -> float:
+    """IEEE-754 double addition from the additive identity -0.0, term by
+    term (Python floats are IEEE doubles, round to nearest even)."""
+    acc = -0.0
+    for v in terms:
+        acc = acc + float(v)
+    return acc
+
+
+def pin_sum_signed_zero(o):
+    """A sum that is exactly zero is -0 when every term is -0 and +0
+    otherwise (IEEE-754 addition in round-to-nearest; the same in any
+    order).  Checked against sequential IEEE addition and by hand."""
+    nz, pz = np.float32(-0.0), np.float32(0.0)
+    cases = [
+        ([nz] * 1, False, 0.0, -1), ([nz] * 7, False, 0.0, -1),
+        ([nz] * 33, False, 0.0, -1), ([pz] * 8, False, 0.0, 1),
+        ([nz, pz], False, 0.0, 1), ([pz, nz, nz], False, 0.0, 1),
+        ([1.0, -1.0], False, 0.0, 1), ([-2.5, nz, 2.5], False, 0.0, 1),
+        ([nz] * 3, True, -0.0, -1), ([nz] * 3, True, 0.0, 1),
+        ([pz] * 3, True, -0.0, 1), ([nz] * 3, False, 0.0, -1),
+        ([0.75, -0.5], True, -0.25, 1),
+    ]
+    for terms, accum, old, sign in cases:
+        x = np.array(terms, np.float32)
+        s, a = o.sum_f32(x, accum, old)
+        ref = _ieee_seq_sum(([old] if accum else []) + list(x))
+        assert s == 0 and ref == 0, (terms, s, ref)
+        assert math.copysign(1.0, s) == sign == math.copysign(1.0, ref), (terms, accum, old, s)
+    # rows and columns follow the same rule, row by row / column by column
+    m = np.array([[nz, nz, nz], [nz, pz, nz], [1.0, nz, -1.0]], np.float32)
+    s, _ = o.rows_sum_f32(m, 3, 3, 3)
+    assert [math.copysign(1.0, v) for v in s] == [-1.0, 1.0, 1.0], s
+    s, _ = o.cols_sum_f32(m.T.copy(), 3, 3, 3)
+    assert [math.copysign(1.0, v) for v in s] == [-1.0, 1.0, 1.0], s
+    old = np.array([-0.0, 0.0, -0.0], np.float32)
+    s, _ = o.rows_sum_f32(np.full((3, 2), nz, np.float32), 3, 2, 2, True, old)
+    assert [math.copysign(1.0, v) for v in s] == [-1.0, 1.0, -1.0], s
+
+
 # ---------------------------------------------------------------------------
 # max / min
 # ---------------------------------------------------------------------------
@@ -500,10 +540,96 @@ def pin_cols_closed_forms(o):
     assert (o.cols_min_f32(t, 3, 0, 2, dst=np.full(2, 4.0)) == 4.0).all()
 
 
+# ---------------------------------------------------------------------------
+# threaded forms
+# ---------------------------------------------------------------------------
+
+THREADS = (1, 2, 3, 7, 16)
+
+
+def pin_mt_sum(o):
+    """Threaded sums against exact rational sums, for thread counts that do
+    and do not divide n and exceed it; the signed-zero rule; empty input."""
+    rng = np.random.default_rng(81)
+    for n in (1, 5, 33, 1000):
+        x = (rng.uniform(-1, 1, n) * 10.0 ** rng.uniform(-3, 3, n)).astype(np.float32)
+        for t in THREADS + (n + 3,):
+            for accum, old in ((False, 0.0), (True, -7.5)):
+                terms = list(x) + ([np.float32(old)] if accum else [])
+                ex = exact_sum(terms)
+                ab = sum((abs(Fraction(float(v))) for v in terms), Fraction(0))
+                s, a = o.sum_f32_mt(x, t, accum, old)
+                assert abs(Fraction(s) - ex) <= Fraction(1, 10**14) * ab, (n, t, s, ex)
+                assert abs(Fraction(a) - ab) <= Fraction(1, 10**14) * ab, (n, t, a, ab)
+    x = rng.integers(-1000, 1001, 100001).astype(np.float32)
+    assert o.sum_f32_mt(x, 16)[0] == float(np.sum(x.astype(np.int64)))
+    nz = np.full(9, -0.0, np.float32)
+    assert math.copysign(1.0, o.sum_f32_mt(nz, 4)[0]) == -1.0
+    nz[5] = 0.0
+    assert math.copysign(1.0, o.sum_f32_mt(nz, 4)[0]) == 1.0
+    assert o.sum_f32_mt(np.zeros(0, np.float32), 4) is None
+
+
+def pin_mt_extremes(o):
+    """Threaded max / min against Python's max / min, with accum and NaN."""
+    rng = np.random.default_rng(82)
+    for n in (1, 6, 100, 4099):
+        x = rng.standard_normal(n).astype(np.float32)
+        for t in THREADS + (n + 1,):
+            assert o.max_f32_mt(x, t) == max(x.tolist()), (n, t)
+            assert o.min_f32_mt(x, t) == min(x.tolist()), (n, t)
+            assert o.max_f32_mt(x, t, True, 50.0) == np.float32(50.0)
+            assert o.min_f32_mt(x, t, True, -50.0) == np.float32(-50.0)
+    x = np.array([np.nan, 2.0, np.nan, np.nan, -1.0, np.nan], np.float32)
+    assert o.max_f32_mt(x, 3) == 2.0 and o.min_f32_mt(x, 6) == -1.0
+    assert math.isnan(o.max_f32_mt(np.full(5, np.nan, np.float32), 2))
+
+
+def pin_mt_rows(o):
+    """Threaded row sums and maxima against exact sums and numpy maxima."""
+    rng = np.random.default_rng(83)
+    rows, n, ld = 13, 9, 11
+    x = rng.uniform(-2, 2, (rows, ld)).astype(np.float32)
+    for t in THREADS + (rows + 2,):
+        s, a = o.rows_sum_f32_mt(x, rows, n, ld, t)
+        m = o.rows_max_f32_mt(x, rows, n, ld, t)
+        for r in range(rows):
+            ex = exact_sum(x[r, :n])
+            assert abs(Fraction(s[r]) - ex) <= Fraction(1, 10**14) * exact_sum(np.abs(x[r, :n]))
+            assert a[r] == float(exact_sum(np.abs(x[r, :n].astype(np.float64))))
+            assert m[r] == x[r, :n].max(), (r, t)
+
+
+def pin_mt_colprod(o):
+    """Threaded column products against exact products of independently
+    decoded values (fp32, numpy float16, bfloat16 as the upper half of a
+    binary32) and big-integer products modulo 2^32."""
+    rng = np.random.default_rng(84)
+    R, C, ld = 7, 19, 21
+    v = rng.uniform(0.5, 1.5, (R, ld)).astype(np.float32)
+    h = v.astype(np.float16)
+    bbits = (v.view(np.uint32) >> 16).astype(np.uint16)
+    bvals = (bbits.astype(np.uint32) << 16).view(np.float32)
+    iv = rng.integers(-(2 ** 31), 2 ** 31, (R, ld), dtype=np.int64).astype(np.int32)
+    for t in THREADS + (C + 4,):
+        pf = o.colprod_f32_mt(v, R, C, ld, t)
+        ph = o.colprod_f16_mt(h.view(np.uint16), R, C, ld, t)
+        pb = o.colprod_bf16_mt(bbits, R, C, ld, t)
+        pi = o.colprod_i32_mt(iv, R, C, ld, t)
+        for j in range(C):
+            for got, col in ((pf[j], v[:, j]), (ph[j], h[:, j]), (pb[j], bvals[:, j])):
+                ex = exact_prod(col.astype(np.float64))
+                assert abs(Fraction(got) - ex) <= Fraction(1, 10**14) * abs(ex), (t, j)
+            p = 1
+            for val in iv[:, j].tolist():
+                p = (p * val) % U32
+            assert pi[j] == _i32(p), (t, j)
+
+
 PINS = [
     pin_sum_bruteforce, pin_sum_integer_exact, pin_sum_arithmetic_series,
     pin_sum_cancellation, pin_sum_accum, pin_sum_empty, pin_sum_nonfinite,
-    pin_sum_subnormal,
+    pin_sum_subnormal, pin_sum_signed_zero,
     pin_maxmin_bruteforce, pin_maxmin_nan_policy, pin_maxmin_accum,
     pin_maxmin_empty, pin_maxmin_special,
     pin_page_sum_golden, pin_page_sum_integer_exact, pin_page_sum_error_bound,
@@ -513,4 +639,5 @@ PINS = [
     pin_colprod_16bit_bruteforce, pin_colprod_i32_bruteforce,
     pin_colprod_i32_closed_forms, pin_colprod_u32_bruteforce,
     pin_colprod_u16_bruteforce, pin_cols_bruteforce, pin_cols_closed_forms,
+    pin_mt_sum, pin_mt_extremes, pin_mt_rows, pin_mt_colprod,
 ]

@@ -22,6 +22,10 @@ MUTANTS = [
     ("sum_ignores_accum",
      "if (accum)\n        neumaier_add(&st, (double)old);", ""),
     ("sum_abs_without_fabs", "st->a += fabs(v);", "st->a += v;"),
+    ("sum_starts_at_positive_zero",
+     "neumaier_t st = {-0.0, 0.0, 0.0, 0};", "neumaier_t st = {0.0, 0.0, 0.0, 0};"),
+    ("sum_adds_zero_correction",
+     "return st->c == 0.0 ? st->s : st->s + st->c;", "return st->s + st->c;"),
     ("sum_computes_empty",
      "    if (n == 0)\n        return 0;\n    neumaier_t st",
      "    neumaier_t st"),
@@ -74,6 +78,18 @@ MUTANTS = [
     ("cols_max_is_min",
      "            r = max_num(r, src[i * ld + j]);",
      "            r = min_num(r, src[i * ld + j]);"),
+    ("mt_pieces_drop_remainder",
+     "*len = base + ((size_t)i < extra ? 1 : 0);", "*len = base;"),
+    ("mt_sum_skips_first_piece",
+     "    for (int i = 0; i < k; i++) {\n        if (!p[i].ok)\n            continue;",
+     "    for (int i = 1; i < k; i++) {\n        if (!p[i].ok)\n            continue;"),
+    ("mt_extreme_ignores_accum",
+     "    float r = accum ? *dst : NAN;\n    for (int i = 0; i < k; i++)",
+     "    float r = NAN;\n    for (int i = 0; i < k; i++)"),
+    ("mt_colprod_offset_in_elements_not_bytes",
+     "(const char*)src + f * elem", "(const char*)src + f"),
+    ("mt_rows_offset_ignores_stride",
+     "p[i] = mt_piece(MT_ROWS_SUM, x + f * ld,", "p[i] = mt_piece(MT_ROWS_SUM, x + f * n,"),
     ("i32_signed_read",
      "uint32_t v;\n            memcpy(&v, &src[i * ld + j], sizeof v);",
      "uint32_t v = (uint32_t)(src[i * ld + j] & 0x7fffffff);"),
