@@ -10,7 +10,8 @@ import pytest
 
 import oracle
 import workloads
-from gpu_helpers import SUM_TOL, dev, host, say
+from gpu_helpers import (check_extremes, check_sums, dev, has_both_zeros, host, say,
+                         signed_zero_patterns, valid_region)
 
 pytestmark = pytest.mark.gpu
 
@@ -38,20 +39,16 @@ def run_cols(red, op, sd, C, accum=False, old=None):
 def check_cols(orc, op, src, R, C, ld, got, accum=False, old=None, what=""):
     if op == "sum":
         s, a = orc.cols_sum_f32(src, R, C, ld, accum, old)
+        check_sums(got, s, a, what)
         with np.errstate(invalid="ignore"):  # inf - inf in non-finite columns
             err = np.abs(got.astype(np.float64) - s)
         finite = np.isfinite(s)
-        worst = float(np.max(err[finite] / np.maximum(a[finite], 1e-300), initial=0.0))
-        assert (err[finite] <= SUM_TOL * a[finite]).all(), "%s: worst %g" % (what, worst)
-        assert (np.isnan(got[~finite]) == np.isnan(s[~finite])).all(), what
-        return worst
+        return float(np.max(err[finite] / np.maximum(a[finite], 1e-300), initial=0.0))
     else:
         fn = orc.cols_max_f32 if op == "max" else orc.cols_min_f32
         want = fn(src, R, C, ld, accum, old)
-        eq = (got.view(np.uint32) == want.view(np.uint32)) | ((got == 0) & (want == 0)) \
-            | (np.isnan(got) & np.isnan(want))
-        assert eq.all(), "%s: column %d got %r want %r" % (
-            what, int(np.nonzero(~eq)[0][0]), got[~eq][0], want[~eq][0])
+        both = has_both_zeros(valid_region(src, R, C, ld), old, accum, axis=0)
+        check_extremes(got, want, both, what)
 
 
 @pytest.fixture(scope="module")
@@ -114,6 +111,25 @@ def test_cols_special_values(red, orc):
     got = run_cols(red, "sum", td, C)
     assert got[4] == np.float32(R * 2.0 ** -149)
     assert got[2] == inf and got[3] == -inf and math.isnan(got[0])
+
+
+@pytest.mark.parametrize("R,C", [(3000, 12), (1000, 130), (200000, 16), (300, 4099),
+                                 (4096, 2048), (16, 262144)])
+def test_cols_signed_zeros(red, orc, R, C):
+    """Columns cycling through all -0, all +0, zeros of random signs, -0
+    with one +0, negatives with one -0 and positives with one +0: a zero
+    max / min carries the only sign of zero its column holds, and a zero
+    sum is -0 exactly when every term is -0 (old -0 in even columns, +0 in
+    odd ones under accum)."""
+    say("cols signed zeros R=%d C=%d" % (R, C))
+    t = np.ascontiguousarray(signed_zero_patterns(C, R, 70 + C).T)
+    td = dev(t)
+    old = np.where(np.arange(C) % 2 == 0, np.float32(-0.0), np.float32(0.0)).astype(np.float32)
+    for op in ("sum", "max", "min"):
+        for accum in (False, True):
+            got = run_cols(red, op, td, C, accum, old if accum else None)
+            check_cols(orc, op, t, R, C, C, got, accum, old if accum else None,
+                       "signed zeros R=%d C=%d %s accum=%s" % (R, C, op, accum))
 
 
 def test_cols_empty_untouched(red):

@@ -12,7 +12,7 @@ import numpy as np
 import pytest
 
 import oracle
-from gpu_helpers import dev, host, say
+from gpu_helpers import dev, extremes_match, has_both_zeros, host, say, zero_sum_sign_ok
 
 pytestmark = pytest.mark.gpu
 
@@ -106,7 +106,7 @@ def test_thread_extreme(lib, orc, n, op, accum):
     got = run_thread(lib, x, op, accum, old)
     fn = orc.rows_max_f32 if op == "max" else orc.rows_min_f32
     want = fn(x, rows, n, n, accum, old if accum else None)
-    eq = same_bits(got, want) | ((got == 0) & (want == 0))
+    eq = extremes_match(got, want, has_both_zeros(x, old, accum, axis=1))
     bad = np.nonzero(~eq)[0]
     assert bad.size == 0, "row %d: got %r want %r" % (bad[0], got[bad[0]], want[bad[0]])
 
@@ -136,10 +136,11 @@ def check_groups(orc, x, got, op, depth, what):
         assert np.isnan(res[nan]).all(), what
         inf = np.isinf(s)
         assert (res[inf] == s[inf]).all(), what
+        assert zero_sum_sign_ok(res, s).all(), "%s: zero sum with the wrong sign" % what
     else:
         fn = orc.rows_max_f32 if op == "max" else orc.rows_min_f32
         want = fn(x, groups, m, m)
-        eq = same_bits(res, want) | ((res == 0) & (want == 0))
+        eq = extremes_match(res, want, has_both_zeros(x, axis=1))
         assert eq.all(), "%s: group %d" % (what, int(np.nonzero(~eq)[0][0]))
 
 

@@ -16,8 +16,9 @@ import numpy as np
 import pytest
 
 import oracle
-from gpu_helpers import (COLPROD_16_TOL, COLPROD_F32_TOL, check_exact, check_rel,
-                         check_sum, dev, host, say)
+from gpu_helpers import (COLPROD_16_TOL, COLPROD_F32_TOL, check_exact, check_extremes,
+                         check_rel, check_sum, check_sums, dev, has_both_zeros, host, say,
+                         valid_region)
 
 pytestmark = pytest.mark.gpu
 
@@ -75,7 +76,8 @@ def test_random_1d(red, orc):
             s, a = orc.sum_f32(x, accum, old)
             check_sum(got, s, a, what)
         else:
-            check_exact(got, getattr(orc, op + "_f32")(x, accum, old), what)
+            check_exact(got, getattr(orc, op + "_f32")(x, accum, old), what,
+                        bool(has_both_zeros(x, np.float32(old), accum)))
 
 
 def test_random_rows(red, orc):
@@ -102,11 +104,10 @@ def test_random_rows(red, orc):
                 want = orc.rows_page_sum_f32(x, rows, n, ld, accum, old)
                 assert (got.view(np.uint32) == want.view(np.uint32)).all(), what
             s, a = orc.rows_sum_f32(x, rows, n, ld, accum, old)
-            assert (np.abs(got.astype(np.float64) - s) <= 1e-6 * a).all(), what
+            check_sums(got, s, a, what)
         else:
             want = getattr(orc, "rows_%s_f32" % op)(x, rows, n, ld, accum, old)
-            eq = (got.view(np.uint32) == want.view(np.uint32)) | ((got == 0) & (want == 0))
-            assert eq.all(), what
+            check_extremes(got, want, has_both_zeros(x[:, :n], old, accum, axis=1), what)
 
 
 COL_KINDS = ["f32", "bf16", "f16", "i32", "sum", "max", "min"]
@@ -141,6 +142,21 @@ def test_random_columns(red, orc):
             vals[:, :C] = rng.uniform(-1, 1, (R, C)).astype(np.float32)
         else:
             vals[:, :C] = rng.uniform(lo, hi, (R, C)).astype(np.float32)
+        if C >= 3 and case % 2 == 0:
+            # Signed zeros in three columns: for sum / max / min a column of
+            # zeros of random signs, one of -0 only and one of +0 only; for
+            # products one -0 factor, one +0 factor and a -0 factor in a
+            # column of negated values (the product's sign is the XOR).
+            j = rng.choice(C, 3, replace=False)
+            if kind in ("sum", "max", "min"):
+                vals[:, j[0]] = np.where(rng.random(R) < 0.5, 0.0, -0.0)
+                vals[:, j[1]] = -0.0
+                vals[:, j[2]] = 0.0
+            else:
+                vals[rng.integers(0, R), j[0]] = -0.0
+                vals[rng.integers(0, R), j[1]] = 0.0
+                vals[:, j[2]] = -vals[:, j[2]]
+                vals[rng.integers(0, R), j[2]] = -0.0
         if kind in ("f32", "sum", "max", "min"):
             sd = upload_padded(vals, off)
             out = torch.zeros(C, dtype=torch.float32, device="cuda")
@@ -155,11 +171,11 @@ def test_random_columns(red, orc):
                 got = host(out)
                 if kind == "sum":
                     s, a = orc.cols_sum_f32(vals, R, C, ld, accum, old)
-                    assert (np.abs(got.astype(np.float64) - s) <= 1e-6 * a).all(), what
+                    check_sums(got, s, a, what)
                 else:
                     want = getattr(orc, "cols_%s_f32" % kind)(vals, R, C, ld, accum, old)
-                    eq = (got.view(np.uint32) == want.view(np.uint32)) | ((got == 0) & (want == 0))
-                    assert eq.all(), what
+                    both = has_both_zeros(valid_region(vals, R, C, ld), old, accum, axis=0)
+                    check_extremes(got, want, both, what)
         else:
             tdt = torch.bfloat16 if kind == "bf16" else torch.float16
             h = torch.from_numpy(vals).to(tdt)           # exact RNE conversion; NaN padding stays NaN
@@ -199,11 +215,10 @@ def column_case(red, orc, rng, kind, R, C, ld, off, doff, what):
         got = host(out)
         if kind == "sum":
             s, a = orc.cols_sum_f32(x, R, C, ld, accum, old)
-            assert (np.abs(got.astype(np.float64) - s) <= 1e-6 * a).all(), what
+            check_sums(got, s, a, what)
         else:
             want = getattr(orc, "cols_%s_f32" % kind)(x, R, C, ld, accum, old)
-            eq = (got.view(np.uint32) == want.view(np.uint32)) | ((got == 0) & (want == 0))
-            assert eq.all(), what
+            check_extremes(got, want, has_both_zeros(x[:, :C], old, accum, axis=0), what)
     else:
         rare = 2e-5 if kind == "f16" else 2e-4
         u = rng.random((R, ld))

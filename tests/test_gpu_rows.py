@@ -8,7 +8,9 @@ import pytest
 
 import oracle
 import workloads
-from gpu_helpers import check_exact, check_sum, dev, host, say
+from gpu_helpers import (check_exact, check_extremes, check_sum, check_sums, dev,
+                         has_both_zeros, host, say, signed_zero_patterns,
+                         valid_region)
 
 pytestmark = pytest.mark.gpu
 
@@ -43,16 +45,15 @@ def check_rows(orc, op, x, n, got, accum=False, old=None, what=""):
             assert bad.size == 0, "%s: row %d got %r want %r" % (
                 what, bad[0], got[bad[0]], want[bad[0]])
         s, a = orc.rows_sum_f32(x, rows, n, ld, accum, old)
-        err = np.abs(got.astype(np.float64) - s)
-        worst = float((err / np.maximum(a, 1e-300)).max())
-        assert (err <= 1e-6 * a).all(), "%s: worst %g" % (what, worst)
-        return worst
+        check_sums(got, s, a, what)
+        with np.errstate(invalid="ignore"):
+            err = np.abs(got.astype(np.float64) - s)
+        return float(np.nanmax(err / np.maximum(a, 1e-300), initial=0.0))
     else:
         fn = orc.rows_max_f32 if op == "max" else orc.rows_min_f32
         want = fn(x, rows, n, ld, accum, old)
-        eq = (got.view(np.uint32) == want.view(np.uint32)) | ((got == 0) & (want == 0)) \
-            | (np.isnan(got) & np.isnan(want))
-        assert eq.all(), "%s: row %d" % (what, int(np.nonzero(~eq)[0][0]))
+        both = has_both_zeros(valid_region(x, x.shape[0], n, x.shape[1]), old, accum, axis=1)
+        check_extremes(got, want, both, what)
 
 
 @pytest.fixture(scope="module")
@@ -168,6 +169,23 @@ def test_rows_short(red, orc, rows, n, ld, off):
             got = run_rows(red, op, xd, n, old if accum else None, accum)
             check_rows(orc, op, x, n, got, accum, old if accum else None,
                        "rows=%d n=%d ld=%d off=%d %s accum=%s" % (rows, n, ld, off, op, accum))
+
+
+@pytest.mark.parametrize("rows,n", [(3000, 1), (3000, 3), (3000, 7), (3000, 32), (3000, 40),
+                                    (3000, 100), (300, 1000), (300, 2000), (5, 70000)])
+def test_rows_signed_zeros(red, orc, rows, n):
+    """A zero result carries the only sign of zero the row holds (max /
+    min), and a zero sum is -0 exactly when every term is -0; under accum
+    the old value (-0 in even rows, +0 in odd ones) takes part."""
+    say("rows signed zeros rows=%d n=%d" % (rows, n))
+    x = signed_zero_patterns(rows, n, 40 + n)
+    xd = dev(x)
+    old = np.where(np.arange(rows) % 2 == 0, np.float32(-0.0), np.float32(0.0)).astype(np.float32)
+    for op in ("sum", "max", "min"):
+        for accum in (False, True):
+            got = run_rows(red, op, xd, n, old if accum else None, accum)
+            check_rows(orc, op, x, n, got, accum, old if accum else None,
+                       "signed zeros rows=%d n=%d %s accum=%s" % (rows, n, op, accum))
 
 
 def test_rows_empty_untouched(red):

@@ -46,7 +46,8 @@ import pytest
 
 import oracle
 import workloads
-from gpu_helpers import COLPROD_16_TOL, COLPROD_F32_TOL, check_rel, dev, host, say
+from gpu_helpers import (COLPROD_16_TOL, COLPROD_F32_TOL, check_extremes, check_rel, check_sums,
+                         dev, has_both_zeros, host, say, valid_region)
 
 pytestmark = pytest.mark.gpu
 
@@ -130,11 +131,11 @@ def cols_case(red, orc, op, R, C, ld, accum, seed, off=0, dst_off=0):
     got = host(out)
     if op == "sum":
         s, a = orc.cols_sum_f32(x, R, C, ld, accum, old)
-        assert (np.abs(got.astype(np.float64) - s) <= 1e-6 * a).all(), what
+        check_sums(got, s, a, what)
     else:
         want = getattr(orc, "cols_%s_f32" % op)(x, R, C, ld, accum, old)
-        eq = (got.view(np.uint32) == want.view(np.uint32)) | ((got == 0) & (want == 0))
-        assert eq.all(), what
+        check_extremes(got, want, has_both_zeros(valid_region(x, R, C, ld), old, accum, axis=0),
+                       what)
 
 
 # (W vectors per row, valid vectors, rows): rows end inside a step, inside

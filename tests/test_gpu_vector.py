@@ -9,7 +9,7 @@ import pytest
 
 import oracle
 import workloads
-from gpu_helpers import check_exact, check_sum, dev, host, say
+from gpu_helpers import check_exact, check_sum, dev, has_both_zeros, host, say
 
 pytestmark = pytest.mark.gpu
 
@@ -44,10 +44,10 @@ def check(orc, op, x, got, accum=False, old=0.0, what=""):
         if a > 0 and x.size >= (1 << 20):
             say("%s: |gpu - exact| / sum|x| = %.3g (tolerance 1e-6)"
                 % (what, abs(float(got) - s) / a))
-    elif op == "max":
-        check_exact(got, orc.max_f32(x, accum, old), what)
     else:
-        check_exact(got, orc.min_f32(x, accum, old), what)
+        both = bool(has_both_zeros(x, np.float32(old), accum))
+        want = orc.max_f32(x, accum, old) if op == "max" else orc.min_f32(x, accum, old)
+        check_exact(got, want, what, both)
 
 
 # ---------------------------------------------------------------------------
@@ -149,33 +149,64 @@ def test_integer_sums_are_exact(red):
         assert run(red, "sum", dev(x), True, 7.0) == want + 7.0
 
 
-def test_special_values(red, orc):
-    say("special values")
-    nan, inf = float("nan"), float("inf")
-    cases = [
-        [nan, 1.0, nan, -3.0],
-        [nan] * 9,
-        [nan] * 3000 + [2.0] + [nan] * 3000,
-        [inf, 1.0, -2.0],
-        [-inf, 1.0, 5.0] * 100,
-        [2.0 ** -149, -(2.0 ** -149), 0.0, 2.0 ** -140] * 50,
-        [0.0, -0.0] * 1000,
-        [-0.0] * 17,
-    ]
-    for vals in cases:
+SPECIAL_CASES = [
+    [float("nan"), 1.0, float("nan"), -3.0],
+    [float("nan")] * 9,
+    [float("nan")] * 3000 + [2.0] + [float("nan")] * 3000,
+    [float("inf"), 1.0, -2.0],
+    [-float("inf"), 1.0, 5.0] * 100,
+    [float("inf"), -float("inf"), 1.0],
+    [2.0 ** -149, -(2.0 ** -149), 0.0, 2.0 ** -140] * 50,
+    [-(2.0 ** -149), -(2.0 ** -126) + 2.0 ** -149] * 3,
+    [0.0, -0.0] * 1000,
+    [-0.0] * 17,
+    [-0.0] * 20000,
+    [0.0] * 17,
+    [0.0] * 20000,
+    [-0.0] * 9000 + [0.0] + [-0.0] * 9000,
+    [-1.0, -0.0, -2.0] * 7,
+    [1.0, -0.0, 2.0] * 7,
+    [1.0, -1.0] * 5000,
+]
+
+
+@pytest.mark.parametrize("atomic", [False, True])
+def test_special_values(red, orc, atomic):
+    """NaN, infinities, subnormals and signed zeros through the
+    deterministic and the single-pass atomic entry points, with and
+    without accum (old -0.0, +0.0 and 1.5)."""
+    say("special values atomic=%s" % atomic)
+    for vals in SPECIAL_CASES:
         x = np.array(vals, np.float32)
         xd = dev(x)
         for op in OPS:
-            got = run(red, op, xd)
-            what = "special %s %s" % (op, vals[:4])
-            check(orc, op, x, got, what=what)
+            for accum, old in ((False, 0.0), (True, -0.0), (True, 0.0), (True, 1.5)):
+                got = run(red, op, xd, accum, old, atomic)
+                what = "special %s atomic=%s accum=%s old=%r n=%d %s" % (
+                    op, atomic, accum, old, len(vals), vals[:4])
+                check(orc, op, x, got, accum, old, what)
     # subnormals are summed, not flushed: exact small integer multiples
-    x = np.full(1000, 2.0 ** -149, np.float32)
-    assert run(red, "sum", dev(x)) == np.float32(1000 * 2.0 ** -149)
+    for n in (1000, 100000):
+        x = np.full(n, 2.0 ** -149, np.float32)
+        assert run(red, "sum", dev(x), atomic=atomic) == np.float32(n * 2.0 ** -149), n
+        assert run(red, "sum", dev(-x), atomic=atomic) == np.float32(-n * 2.0 ** -149), n
     # accum under NaN policy
-    x = dev(np.array([nan, nan], np.float32))
-    assert run(red, "max", x, True, 1.5) == np.float32(1.5)
-    assert math.isnan(run(red, "min", x))
+    x = dev(np.array([float("nan"), float("nan")], np.float32))
+    assert run(red, "max", x, True, 1.5, atomic) == np.float32(1.5)
+    assert math.isnan(run(red, "min", x, atomic=atomic))
+
+
+def test_special_values_fused(red, orc):
+    """The same special values through the fused sum / max / min call:
+    each result bit-identical to the single call's and checked against the
+    oracle."""
+    say("special values fused")
+    for vals in SPECIAL_CASES:
+        x = np.array(vals, np.float32)
+        xd = dev(x)
+        for accum, old in ((False, 0.0), (True, -0.0), (True, 0.0), (True, 1.5)):
+            check_fused(red, orc, x, xd, accum, (old, old, old),
+                        "special n=%d %s accum=%s old=%r" % (len(vals), vals[:4], accum, old))
 
 
 def test_empty_leaves_out_untouched(red):
@@ -260,15 +291,6 @@ def test_fused_lengths(red, orc, base, n):
         for accum, old in ((False, (0.0, 0.0, 0.0)), (True, (-2.5, 100.0, -100.0))):
             check_fused(red, orc, x[off:off + n], xd[off:off + n], accum, old,
                         "n=%d off=%d" % (n, off))
-
-
-def test_fused_special_values(red, orc):
-    say("fused special values")
-    nan, inf = float("nan"), float("inf")
-    for vals in ([nan, 1.0, nan, -3.0], [nan] * 9, [inf, 1.0, -2.0],
-                 [2.0 ** -149, -(2.0 ** -149), 0.0] * 5):
-        x = np.array(vals, np.float32)
-        check_fused(red, orc, x, dev(x), False, (0.0, 0.0, 0.0), "special %s" % vals[:3])
 
 
 def test_workspace_allocation_failure(red, vec16m):
