@@ -71,6 +71,7 @@ _SIGS = {
     "red_colprod_i16": [_P, _SZ, _SZ, _SZ, _P, _P],
     "red_colprod_u16": [_P, _SZ, _SZ, _SZ, _P, _P],
     "red_colprod_u32": [_P, _SZ, _SZ, _SZ, _P, _P],
+    "red_release_workspace": [_P],
 }
 for _name, _args in _SIGS.items():
     _fn = getattr(_lib, _name)
@@ -103,6 +104,12 @@ def _stream(stream) -> int:
     if isinstance(stream, torch.cuda.Stream):
         return stream.cuda_stream
     return int(stream)
+
+
+def release_workspace(stream=None) -> None:
+    """Free the library's workspace for `stream` (the current stream when
+    None) after the work enqueued on it has finished."""
+    _check(_lib.red_release_workspace(_stream(stream)), "red_release_workspace")
 
 
 def _check(status: int, where: str) -> None:

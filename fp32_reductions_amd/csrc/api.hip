@@ -6,11 +6,13 @@
 // calling stream's workspace, then enqueues the kernel and returns.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cstdint>
 #include <cstdlib>
 #include <map>
+#include <memory>
 #include <mutex>
-#include <utility>
+#include <tuple>
 
 #include "internal.hpp"
 #include "reduce.h"
@@ -26,9 +28,41 @@ using red::Workspace;
 // size their grids so that they never need more than this.
 constexpr size_t kPartialBytes = size_t(16) << 20;
 
+// One workspace and the lock a call holds while it enqueues the kernels
+// that use it: the first pass writes the partials and the second reads
+// them, so two calls on one stream from different host threads must not
+// interleave their launches.  `released` is set (under `mu`) when
+// red_release_workspace has taken the slot out of the map.
+struct Slot {
+    Workspace ws;
+    std::mutex mu;
+    bool released = false;
+};
+
+// A workspace belongs to a (device, stream).  hipStreamPerThread is one
+// handle for a different stream in every host thread, so for it the key is
+// the calling thread instead.
+enum KeyKind { kStreamKey = 0, kThreadKey = 1 };
+using SlotKey = std::tuple<int, int, uintptr_t>;
+
 std::mutex g_mu;
 std::map<int, DeviceInfo> g_dev;
-std::map<std::pair<int, uintptr_t>, Workspace> g_ws;
+std::map<SlotKey, std::shared_ptr<Slot>> g_ws;
+std::atomic<uint64_t> g_next_thread{1};
+
+// A number for the calling host thread, never reused within the process.
+uint64_t thread_token()
+{
+    thread_local uint64_t token = g_next_thread.fetch_add(1);
+    return token;
+}
+
+SlotKey slot_key(int dev, hipStream_t stream)
+{
+    if (stream == hipStreamPerThread)
+        return SlotKey(dev, kThreadKey, (uintptr_t)thread_token());
+    return SlotKey(dev, kStreamKey, (uintptr_t)stream);
+}
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
@@ -60,14 +94,14 @@ int current_device(int* dev, DeviceInfo* info)
     return RED_OK;
 }
 
-// The workspace of (dev, stream), created on first use.
-int stream_workspace(int dev, hipStream_t stream, Workspace* ws)
+// The slot of (dev, stream), created on first use.
+int find_slot(int dev, hipStream_t stream, std::shared_ptr<Slot>* out)
 {
     std::lock_guard<std::mutex> lock(g_mu);
-    const auto key = std::make_pair(dev, (uintptr_t)stream);
+    const SlotKey key = slot_key(dev, stream);
     auto it = g_ws.find(key);
     if (it != g_ws.end()) {
-        *ws = it->second;
+        *out = it->second;
         return RED_OK;
     }
     // Failure injection for tests of the RED_ERR_NOMEM path.
@@ -79,12 +113,37 @@ int stream_workspace(int dev, hipStream_t stream, Workspace* ws)
         (void)hipGetLastError(); // clear the sticky allocation error
         return RED_ERR_NOMEM;
     }
-    Workspace w;
-    w.partials = base;
-    w.partial_bytes = kPartialBytes;
-    g_ws.emplace(key, w);
-    *ws = w;
+    auto slot = std::make_shared<Slot>();
+    slot->ws.partials = base;
+    slot->ws.partial_bytes = kPartialBytes;
+    g_ws.emplace(key, slot);
+    *out = slot;
     return RED_OK;
+}
+
+// The workspace of (dev, stream), held for the caller until it goes out of
+// scope: `lock` keeps other host threads from enqueueing on the same
+// workspace in between this call's launches.
+struct HeldWorkspace {
+    std::shared_ptr<Slot> slot;
+    std::unique_lock<std::mutex> lock;
+};
+
+int stream_workspace(int dev, hipStream_t stream, Workspace* ws, HeldWorkspace* held)
+{
+    for (;;) {
+        std::shared_ptr<Slot> slot;
+        const int st = find_slot(dev, stream, &slot);
+        if (st != RED_OK)
+            return st;
+        std::unique_lock<std::mutex> lock(slot->mu);
+        if (slot->released)
+            continue; // released after the lookup: look again
+        *ws = slot->ws;
+        held->slot = std::move(slot);
+        held->lock = std::move(lock);
+        return RED_OK;
+    }
 }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? RED_OK : RED_ERR_HIP; }
@@ -120,8 +179,9 @@ int reduce1d(OpKind op, const float* x, size_t n, float* out, int accum,
     if ((st = current_device(&dev, &info)) != RED_OK)
         return st;
     Workspace ws;
+    HeldWorkspace held;
     const hipStream_t s = static_cast<hipStream_t>(stream);
-    if ((st = stream_workspace(dev, s, &ws)) != RED_OK)
+    if ((st = stream_workspace(dev, s, &ws, &held)) != RED_OK)
         return st;
     clear_stale_error();
     return hip_status(red::launch_reduce1d(op, x, n, out, accum, info, ws, s));
@@ -140,8 +200,9 @@ int reduce1d_summaxmin(const float* x, size_t n, float* out, int accum,
     if ((st = current_device(&dev, &info)) != RED_OK)
         return st;
     Workspace ws;
+    HeldWorkspace held;
     const hipStream_t s = static_cast<hipStream_t>(stream);
-    if ((st = stream_workspace(dev, s, &ws)) != RED_OK)
+    if ((st = stream_workspace(dev, s, &ws, &held)) != RED_OK)
         return st;
     clear_stale_error();
     return hip_status(red::launch_reduce1d_summaxmin(x, n, out, accum, info, ws, s));
@@ -181,8 +242,9 @@ int reduce_rows(OpKind op, const float* x, size_t rows, size_t n, size_t ld,
         return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
     Workspace ws;
+    HeldWorkspace held;
     if (red::rows_chunks(x, rows, n, info) > 1 &&
-        (st = stream_workspace(dev, s, &ws)) != RED_OK)
+        (st = stream_workspace(dev, s, &ws, &held)) != RED_OK)
         return st;
     clear_stale_error();
     return hip_status(red::launch_rows(op, x, rows, n, ld, out, accum, info, ws, s));
@@ -221,8 +283,9 @@ int cols(OpKind op, const float* src, size_t R, size_t C, size_t ld, float* dst,
     if ((st = current_device(&dev, &info)) != RED_OK)
         return st;
     Workspace ws;
+    HeldWorkspace held;
     const hipStream_t s = static_cast<hipStream_t>(stream);
-    if ((st = stream_workspace(dev, s, &ws)) != RED_OK)
+    if ((st = stream_workspace(dev, s, &ws, &held)) != RED_OK)
         return st;
     const red::ColprodPlan plan = red::colprod_plan(ColType::F32, src, R, C, ld, info, ws);
     clear_stale_error();
@@ -242,8 +305,9 @@ int colprod(ColType t, const void* src, size_t R, size_t C, size_t ld,
     if ((st = current_device(&dev, &info)) != RED_OK)
         return st;
     Workspace ws;
+    HeldWorkspace held;
     const hipStream_t s = static_cast<hipStream_t>(stream);
-    if ((st = stream_workspace(dev, s, &ws)) != RED_OK)
+    if ((st = stream_workspace(dev, s, &ws, &held)) != RED_OK)
         return st;
     const red::ColprodPlan plan = red::colprod_plan(t, src, R, C, ld, info, ws);
     clear_stale_error();
@@ -352,6 +416,34 @@ int red_colprod_u32(const uint32_t* src, size_t R, size_t C, size_t ld, uint32_t
                     red_stream_t stream)
 {
     return colprod(ColType::I32, src, R, C, ld, dst, stream);
+}
+
+int red_release_workspace(red_stream_t stream)
+{
+    int dev;
+    if (hipGetDevice(&dev) != hipSuccess)
+        return RED_ERR_HIP;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    std::shared_ptr<Slot> slot;
+    {
+        std::lock_guard<std::mutex> lock(g_mu);
+        auto it = g_ws.find(slot_key(dev, s));
+        if (it == g_ws.end())
+            return RED_OK;
+        slot = it->second;
+        g_ws.erase(it);
+    }
+    {
+        // Waits for a call that is enqueueing on this workspace; a call
+        // that looked the slot up before the erase finds it released and
+        // takes a new one.
+        std::lock_guard<std::mutex> lock(slot->mu);
+        slot->released = true;
+    }
+    // Work already enqueued on the stream may still read the partials.
+    const hipError_t e = hipStreamSynchronize(s);
+    const hipError_t f = hipFree(slot->ws.partials);
+    return (e == hipSuccess && f == hipSuccess) ? RED_OK : RED_ERR_HIP;
 }
 
 const char* red_status_str(int status)

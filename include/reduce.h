@@ -49,11 +49,23 @@
  *     returned.
  *   - The default (non-atomic) entry points are deterministic: for a given
  *     input, device model and library build the result bits never change
- *     between runs.  Internally they use a per-(device, stream) workspace of
- *     a fixed size, created on the first call on that stream (that first
- *     call allocates device memory and must not be made under HIP graph
- *     capture).  Calls on different streams never share a workspace;
- *     concurrent calls on the same stream are ordered by the stream.
+ *     between runs.
+ *   - Workspace.  The calls that combine per-workgroup partials in a second
+ *     kernel (1-D, fused, column and column-product calls, and row calls
+ *     with very long rows or very few rows) keep those partials in a
+ *     16 MiB workspace the library allocates on the first such call for a
+ *     (device, stream) pair and keeps until red_release_workspace.  For
+ *     hipStreamPerThread, which names a different stream in every host
+ *     thread, the workspace belongs to (device, calling thread).  A call
+ *     holds its workspace while it enqueues its kernels, so calls from
+ *     several host threads on one stream are ordered by that stream and
+ *     never interleave their kernels.  The first call on a stream allocates
+ *     device memory and must not be made under HIP graph capture.
+ *   - HIP graphs.  A call captured into a graph uses the workspace of its
+ *     capture stream at every replay.  Replays must therefore be ordered
+ *     with each other and with the calls made on that stream (replaying
+ *     on the capture stream does this), and must end before that stream's
+ *     workspace is released.
  *   - Thread safety: any host thread may call any entry point.
  */
 #ifndef LIBREDUCE_REDUCE_H
@@ -228,6 +240,15 @@ int red_colprod_u32(const uint32_t* src, size_t R, size_t C, size_t ld,
 /* ---------------------------------------------------------------------
  * Utilities
  * ------------------------------------------------------------------- */
+
+/* Waits for the work enqueued on `stream` to finish, then frees the
+ * workspace the library holds for (current device, stream) -- for
+ * hipStreamPerThread, the calling thread's.  Call it before destroying a
+ * stream that library calls used, or before a thread that used
+ * hipStreamPerThread exits; a later call on the stream allocates a new
+ * workspace.  RED_OK when there is nothing to free; RED_ERR_HIP when the
+ * synchronisation or the free fails.  The stream must still exist. */
+int red_release_workspace(red_stream_t stream);
 
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* red_status_str(int status);
