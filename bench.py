@@ -1,19 +1,33 @@
 """Benchmark of libreduce on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                    [--cpu-seconds S] [--no-configs]
 
 Prints ONE JSON line on stdout.  A step is one pass of the workload's calls
-over its input (default workload ``vec16m``: a 2^24-element fp32 vector
-reduced by sum, max and min, then again with accum into a destination
-preset to 3.25).  ``value`` is whole-step effective bandwidth: algorithmic
-bytes of all calls in a step divided by the wall time per step, with every
-input already resident in HBM.
+over its input.  The default workload is ``vec1g``: one fp32 vector of
+2^30 + 7 elements (normal(0,1), 1 % of the entries scaled by 1e6, seed 3)
+reduced by sum, max and min.  ``value`` is whole-step effective bandwidth:
+algorithmic bytes of all calls in a step divided by the wall time per step,
+with every input already resident in HBM.
+
+``per_config`` (default run only; --no-configs skips it) times the other
+workloads in the same process, after the headline's timed region, with an
+event pair around every call: the 4096 x 32 rows and 16 x 16 tile
+(``rows32``, latency only), the 2^24 vector with and without accum
+(``vec16m``), the 4096 x 16384 fp32 / int32 column products
+(``colprod4k``), and the 65536 x 1000 row sum / max with the
+2048 x 32768 bf16 / fp16 column products (``rows1000``).  Each call reports
+microseconds per call, GB/s, the fraction of the 8 TB/s peak and, when a
+counter summary for that call and source is committed, its HBM traffic.
+``read_ceiling`` gives the same figures for a read-only streaming kernel
+(the 1-D stream kernel with its reduction replaced by a trivial sink) over
+the 2^30 + 7 and the 2^24 vectors.
 
 Cold cache: MI355X's 256 MB Infinity Cache would hold a 64 MiB vector
-between calls, so the input exists as several identical copies in HBM and
-consecutive calls read different copies, which puts at least 1 GiB of other
-traffic between two reads of the same copy.  No flush runs in the timed
-region.
+between calls, so a small input exists as several identical copies in HBM
+and consecutive calls read different copies, which puts at least 1 GiB of
+other traffic between two reads of the same copy.  No flush runs in the
+timed region.
 
 ``roofline`` covers the dominant kernel: its algorithmic bytes per launch
 over its mean launch duration, measured with HIP events recorded on the
@@ -21,19 +35,19 @@ launch stream around every launch inside the timed region.  ``traffic`` is
 the HBM bytes per launch measured with rocprofv3 counters (FETCH_SIZE,
 WRITE_SIZE, scaled against a plain copy kernel), read from the committed
 counter summary under profiles/, or null when that summary was taken on a
-different kernel source.
+different kernel or host-planning source.
 
-``cpu_baseline`` times the CPU oracle (single-threaded, as written) on whole
-steps of the same workload for about ten seconds, as a reference point only.
+``cpu_baseline`` times the CPU oracle on whole steps of the headline
+workload: on T host threads (T = the CPU share of this process: its
+affinity, capped by OMP_NUM_THREADS) with the oracle's threaded forms, and
+single-threaded as written, about ``--cpu-seconds`` each, as a reference
+point only.
 
-Other workloads (--workload): vec16m_fused (the same vector, sum / max / min
-from one read per call), vec16m_atomic (the vec16m step through the
-single-pass atomic variant), vec1g (2^30+7 vector), colprod4k (4096 x 16384
-f32 and i32 column products), rows1000 (65536 x 1000 row sum / max, then
-2048 x 32768 bf16 / f16 column products), rows32 (4096 x 32 rows, 16 x 16
-tile), colprod_int (int16 and uint32 column products), cols4k (column
-sum / max / min of a 4096 x 16384 tile), copycal (a plain
-device copy, for counter calibration).
+Other workloads (--workload): vec16m, vec16m_fused (sum / max / min from
+one read per call), vec16m_atomic (the vec16m step through the single-pass
+atomic variant), colprod4k, rows1000, rows32, colprod_int (int16 and
+uint32 column products), cols4k (column sum / max / min of a
+4096 x 16384 tile), copycal (a plain device copy, for counter calibration).
 """
 from __future__ import annotations
 
@@ -60,6 +74,12 @@ COLD_BYTES = 1 << 30   # other traffic between two reads of the same copy
 PROFILES = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "fp32_reductions_amd", "csrc")
 DEVICE_HEADERS = ["device.hpp", "../../include/reduce_device.hpp"]
+# Host-side planning (grids, row splits, workgroups per CU): a change here
+# changes what the kernels read, so it also invalidates counter summaries.
+HOST_PLANNING = ["api.hip", "internal.hpp"]
+SOURCES_1D = ["reduce1d.hip"] + DEVICE_HEADERS + HOST_PLANNING
+SOURCES_ROWS = ["rows.hip"] + DEVICE_HEADERS + HOST_PLANNING
+SOURCES_COLS = ["colprod.hip"] + DEVICE_HEADERS + HOST_PLANNING
 
 
 def log(msg: str) -> None:
@@ -119,14 +139,18 @@ class Call:
 
 
 class Workload:
-    def __init__(self, name, desc, config, calls, dominant, sources, cpu):
+    def __init__(self, name, desc, config, calls, dominant, sources, cpu,
+                 device_inputs=()):
         self.name = name
+        self.device_inputs = list(device_inputs)  # the workload's input tensors
         self.desc = desc
         self.config = config      # extra config keys
         self.calls = calls
         self.dominant = dominant  # call names timed for the roofline
-        self.sources = sources    # csrc files that define the dominant kernel
-        self.cpu = cpu            # list of (bytes, host callable) for one step
+        self.sources = sources    # csrc files that define the kernels and their grids
+        # CPU oracle calls of one step: (bytes, single-threaded callable,
+        # callable taking a thread count, or None when no threaded form exists)
+        self.cpu = cpu
 
 
 class Rotor:
@@ -170,6 +194,22 @@ def up(torch, a):
 # workloads
 # ---------------------------------------------------------------------------
 
+def vector_cpu(orc, x, accums):
+    """Oracle calls of a 1-D step: sum, max, min for each accum setting
+    (destination preset 3.25 under accum), single-threaded and threaded."""
+    n = x.size
+    cpu = []
+    for accum in accums:
+        nbytes = 4 * n + (8 if accum else 4)
+        cpu += [(nbytes, lambda a=accum: orc.sum_f32(x, a, 3.25),
+                 lambda t, a=accum: orc.sum_f32_mt(x, t, a, 3.25)),
+                (nbytes, lambda a=accum: orc.max_f32(x, a, 3.25),
+                 lambda t, a=accum: orc.max_f32_mt(x, t, a, 3.25)),
+                (nbytes, lambda a=accum: orc.min_f32(x, a, 3.25),
+                 lambda t, a=accum: orc.min_f32_mt(x, t, a, 3.25))]
+    return cpu
+
+
 def wl_vec16m(torch, red, orc, steps):
     x = workloads.vec16m()
     n = x.size
@@ -189,17 +229,13 @@ def wl_vec16m(torch, red, orc, steps):
         calls.append(Call(op, kern, 4 * n + 4, plain))
         calls.append(Call(op + "_accum", kern, 4 * n + 8, accum))
     calls = [calls[0], calls[2], calls[4], calls[1], calls[3], calls[5]]
-    cpu = [(4 * n + 4, lambda: orc.sum_f32(x)), (4 * n + 4, lambda: orc.max_f32(x)),
-           (4 * n + 4, lambda: orc.min_f32(x)),
-           (4 * n + 8, lambda: orc.sum_f32(x, True, 3.25)),
-           (4 * n + 8, lambda: orc.max_f32(x, True, 3.25)),
-           (4 * n + 8, lambda: orc.min_f32(x, True, 3.25))]
+    cpu = vector_cpu(orc, x, (False, True))
     return Workload(
         "vec16m",
         "one fp32 vector of 2^24 elements, uniform[-1,1), seed 1; sum, max, min, "
         "then sum, max, min with accum into a destination preset to 3.25",
         {"n": n, "calls_per_step": 6, "cold_copies": len(xs)},
-        calls, ["sum"], ["reduce1d.hip"] + DEVICE_HEADERS, cpu)
+        calls, ["sum"], SOURCES_1D, cpu)
 
 
 def wl_vec16m_atomic(torch, red, orc, steps):
@@ -222,18 +258,14 @@ def wl_vec16m_atomic(torch, red, orc, steps):
         calls.append(Call(op, "fill_u32_kernel + " + kern, 4 * n + 4, plain))
         calls.append(Call(op + "_accum", kern, 4 * n + 8, accum))
     calls = [calls[0], calls[2], calls[4], calls[1], calls[3], calls[5]]
-    cpu = [(4 * n + 4, lambda: orc.sum_f32(x)), (4 * n + 4, lambda: orc.max_f32(x)),
-           (4 * n + 4, lambda: orc.min_f32(x)),
-           (4 * n + 8, lambda: orc.sum_f32(x, True, 3.25)),
-           (4 * n + 8, lambda: orc.max_f32(x, True, 3.25)),
-           (4 * n + 8, lambda: orc.min_f32(x, True, 3.25))]
+    cpu = vector_cpu(orc, x, (False, True))
     return Workload(
         "vec16m_atomic",
         "one fp32 vector of 2^24 elements, uniform[-1,1), seed 1; sum, max, min, "
         "then with accum into a destination preset to 3.25, each as one pass "
         "with one device-scope atomic per workgroup",
         {"n": n, "calls_per_step": 6, "cold_copies": len(xs)},
-        calls, ["sum_accum"], ["reduce1d.hip"] + DEVICE_HEADERS, cpu)
+        calls, ["sum_accum"], SOURCES_1D, cpu)
 
 
 def wl_vec16m_fused(torch, red, orc, steps):
@@ -249,17 +281,21 @@ def wl_vec16m_fused(torch, red, orc, steps):
              Call("sum_max_min_accum", kern, 4 * n + 24,
                   lambda k: red.plan("sum_max_min_f32", xs.next(), accs[k], accum=True))]
 
-    def oracle_all(accum):
-        return (orc.sum_f32(x, accum, 3.25), orc.max_f32(x, accum, 3.25),
-                orc.min_f32(x, accum, 3.25))
-    cpu = [(4 * n + 12, lambda: oracle_all(False)), (4 * n + 24, lambda: oracle_all(True))]
+    def oracle_all(accum, t=None):
+        if t is None:
+            return (orc.sum_f32(x, accum, 3.25), orc.max_f32(x, accum, 3.25),
+                    orc.min_f32(x, accum, 3.25))
+        return (orc.sum_f32_mt(x, t, accum, 3.25), orc.max_f32_mt(x, t, accum, 3.25),
+                orc.min_f32_mt(x, t, accum, 3.25))
+    cpu = [(4 * n + 12, lambda: oracle_all(False), lambda t: oracle_all(False, t)),
+           (4 * n + 24, lambda: oracle_all(True), lambda t: oracle_all(True, t))]
     return Workload(
         "vec16m_fused",
         "one fp32 vector of 2^24 elements, uniform[-1,1), seed 1; sum, max and min "
         "from one read (fused call), then again with accum into destinations preset "
         "to 3.25",
         {"n": n, "calls_per_step": 2, "cold_copies": len(xs)},
-        calls, ["sum_max_min"], ["reduce1d.hip"] + DEVICE_HEADERS, cpu)
+        calls, ["sum_max_min"], SOURCES_1D, cpu)
 
 
 def wl_vec1g(torch, red, orc, steps):
@@ -270,17 +306,17 @@ def wl_vec1g(torch, red, orc, steps):
     outs = torch.zeros((steps, 3), dtype=torch.float32, device="cuda")
     calls = []
     for j, op in enumerate(("sum", "max", "min")):
-        kern = "reduce1d_stream_kernel<Op{0}> + reduce1d_finish_kernel<Op{0}>".format(op.capitalize())
+        kern = ("reduce1d_stream_kernel<Op{0}> (+ reduce1d_finish_kernel<Op{0}>, one "
+                "workgroup)".format(op.capitalize()))
         calls.append(Call(op, kern, 4 * n + 4,
                           lambda k, op=op, j=j: red.plan(op + "_f32", xd, outs[k, j:j + 1])))
-    cpu = [(4 * n + 4, lambda: orc.sum_f32(x)), (4 * n + 4, lambda: orc.max_f32(x)),
-           (4 * n + 4, lambda: orc.min_f32(x))]
+    cpu = vector_cpu(orc, x, (False,))
     return Workload(
         "vec1g",
         "one fp32 vector of 2^30+7 elements, normal(0,1) with 1% of entries "
         "scaled by 1e6, seed 3; sum, max, min",
         {"n": n, "calls_per_step": 3, "cold_copies": 1},
-        calls, ["sum"], ["reduce1d.hip"] + DEVICE_HEADERS, cpu)
+        calls, ["sum"], SOURCES_1D, cpu, device_inputs=[xd])
 
 
 def wl_colprod4k(torch, red, orc, steps):
@@ -296,14 +332,16 @@ def wl_colprod4k(torch, red, orc, steps):
                   lambda k: red.plan("colprod_f32", fs.next(), of)),
              Call("colprod_i32", COLRED.format("TraitsI32, OpMul<unsigned int>"), nbytes,
                   lambda k: red.plan("colprod_i32", is_.next(), oi))]
-    cpu = [(nbytes, lambda: orc.colprod_f32(f, R, C, C)),
-           (nbytes, lambda: orc.colprod_i32(i, R, C, C))]
+    cpu = [(nbytes, lambda: orc.colprod_f32(f, R, C, C),
+            lambda t: orc.colprod_f32_mt(f, R, C, C, t)),
+           (nbytes, lambda: orc.colprod_i32(i, R, C, C),
+            lambda t: orc.colprod_i32_mt(i, R, C, C, t))]
     return Workload(
         "colprod4k",
         "column products of a 4096 x 16384 fp32 tile, uniform[0.999,1.001), and "
         "an int32 tile of the same shape, values in {-3..3}\\{0}, seed 2",
         {"R": R, "C": C, "calls_per_step": 2, "cold_copies": len(fs)},
-        calls, ["colprod_f32"], ["colprod.hip"] + DEVICE_HEADERS, cpu)
+        calls, ["colprod_f32"], SOURCES_COLS, cpu)
 
 
 def wl_colprod_int(torch, red, orc, steps):
@@ -322,14 +360,14 @@ def wl_colprod_int(torch, red, orc, steps):
                   lambda k: red.plan("colprod_i16", hs.next(), oh)),
              Call("colprod_u32", COLRED.format("TraitsI32, OpMul<unsigned int>"), ub,
                   lambda k: red.plan("colprod_u32", us.next(), ou))]
-    cpu = [(hb, lambda: orc.colprod_u16(h.view(np.uint16), 2048, 32768, 32768)),
-           (ub, lambda: orc.colprod_u32(u.view(np.uint32), 4096, 16384, 16384))]
+    cpu = [(hb, lambda: orc.colprod_u16(h.view(np.uint16), 2048, 32768, 32768), None),
+           (ub, lambda: orc.colprod_u32(u.view(np.uint32), 4096, 16384, 16384), None)]
     return Workload(
         "colprod_int",
         "column products of a 2048 x 32768 int16 tile and a 4096 x 16384 uint32 tile, "
         "values uniform over {-3, -1, 1, 3} (seeds 51, 52)",
         {"calls_per_step": 2, "cold_copies": [len(hs), len(us)]},
-        calls, ["colprod_i16"], ["colprod.hip"] + DEVICE_HEADERS, cpu)
+        calls, ["colprod_i16"], SOURCES_COLS, cpu)
 
 
 def wl_rows1000(torch, red, orc, steps):
@@ -355,17 +393,21 @@ def wl_rows1000(torch, red, orc, steps):
                   lambda k: red.plan("colprod_bf16", bs.next(), ob)),
              Call("colprod_f16", COLRED.format("TraitsF16, OpMul<float>"), tbytes,
                   lambda k: red.plan("colprod_f16", hs.next(), oh))]
-    cpu = [(rbytes, lambda: orc.rows_sum_f32(x, rows, n, n)),
-           (rbytes, lambda: orc.rows_max_f32(x, rows, n, n)),
-           (tbytes, lambda: orc.colprod_bf16(b, R, C, C)),
-           (tbytes, lambda: orc.colprod_f16(h, R, C, C))]
+    cpu = [(rbytes, lambda: orc.rows_sum_f32(x, rows, n, n),
+            lambda t: orc.rows_sum_f32_mt(x, rows, n, n, t)),
+           (rbytes, lambda: orc.rows_max_f32(x, rows, n, n),
+            lambda t: orc.rows_max_f32_mt(x, rows, n, n, t)),
+           (tbytes, lambda: orc.colprod_bf16(b, R, C, C),
+            lambda t: orc.colprod_bf16_mt(b, R, C, C, t)),
+           (tbytes, lambda: orc.colprod_f16(h, R, C, C),
+            lambda t: orc.colprod_f16_mt(h, R, C, C, t))]
     return Workload(
         "rows1000",
         "65536 rows x 1000 fp32, uniform[-1,1), row sum and row max; then column "
         "products of 2048 x 32768 bf16 and f16 tiles, uniform[0.99,1.01), seed 4",
         {"rows": rows, "n": n, "R": R, "C": C, "calls_per_step": 4,
          "cold_copies": [len(xs), len(bs), len(hs)]},
-        calls, ["rows_sum"], ["rows.hip"] + DEVICE_HEADERS, cpu)
+        calls, ["rows_sum"], SOURCES_ROWS, cpu)
 
 
 def wl_cols4k(torch, red, orc, steps):
@@ -378,14 +420,14 @@ def wl_cols4k(torch, red, orc, steps):
     calls = [Call(op + "_cols", COLRED.format("TraitsF32, Op%s" % op.capitalize()),
                   nbytes, lambda k, op=op, j=j: red.plan(op + "_cols_f32", ts.next(), outs[j]))
              for j, op in enumerate(("sum", "max", "min"))]
-    cpu = [(nbytes, lambda: orc.cols_sum_f32(t, R, C, C)),
-           (nbytes, lambda: orc.cols_max_f32(t, R, C, C)),
-           (nbytes, lambda: orc.cols_min_f32(t, R, C, C))]
+    cpu = [(nbytes, lambda: orc.cols_sum_f32(t, R, C, C), None),
+           (nbytes, lambda: orc.cols_max_f32(t, R, C, C), None),
+           (nbytes, lambda: orc.cols_min_f32(t, R, C, C), None)]
     return Workload(
         "cols4k",
         "column sum, max and min of a 4096 x 16384 fp32 tile, uniform[-1,1), seed 60",
         {"R": R, "C": C, "calls_per_step": 3, "cold_copies": len(ts)},
-        calls, ["sum_cols"], ["colprod.hip"] + DEVICE_HEADERS, cpu)
+        calls, ["sum_cols"], SOURCES_COLS, cpu)
 
 
 def wl_rows32(torch, red, orc, steps):
@@ -403,16 +445,16 @@ def wl_rows32(torch, red, orc, steps):
                   lambda k: red.plan("min_rows_f32", ad, o[2])),
              Call("colprod_tile16", "colred_narrow_kernel<TraitsF32, OpMul<float>>", 16 * 16 * 4 + 64,
                   lambda k: red.plan("colprod_f32", td, ot))]
-    cpu = [(rbytes, lambda: orc.rows_page_sum_f32(a, rows, n, n)),
-           (rbytes, lambda: orc.rows_max_f32(a, rows, n, n)),
-           (rbytes, lambda: orc.rows_min_f32(a, rows, n, n)),
-           (16 * 16 * 4 + 64, lambda: orc.colprod_f32(t, 16, 16, 16))]
+    cpu = [(rbytes, lambda: orc.rows_page_sum_f32(a, rows, n, n), None),
+           (rbytes, lambda: orc.rows_max_f32(a, rows, n, n), None),
+           (rbytes, lambda: orc.rows_min_f32(a, rows, n, n), None),
+           (16 * 16 * 4 + 64, lambda: orc.colprod_f32(t, 16, 16, 16), None)]
     return Workload(
         "rows32",
         "4096 rows x 32 fp32, uniform[-1,1), seed 0: row sum, max, min (one "
         "thread per row, rows staged in LDS); one 16 x 16 fp32 tile column product",
         {"rows": rows, "n": n, "calls_per_step": 4, "cold_copies": 1},
-        calls, ["rows_sum"], ["rows.hip"] + DEVICE_HEADERS, cpu)
+        calls, ["rows_sum"], SOURCES_ROWS, cpu)
 
 
 def wl_copycal(torch, red, orc, steps):
@@ -444,18 +486,20 @@ def _code_only(text: str) -> str:
     return " ".join(text.split())
 
 
-def source_hash(files) -> str:
+def source_hash(files, csrc: str = CSRC) -> str:
     h = hashlib.sha256()
     for f in files:
-        with open(os.path.join(CSRC, f), encoding="utf-8") as fh:
+        with open(os.path.join(csrc, f), encoding="utf-8") as fh:
             h.update(_code_only(fh.read()).encode())
     return h.hexdigest()[:16]
 
 
-def committed_traffic(wl: Workload):
-    """HBM bytes per launch of the dominant kernel from the committed counter
-    summary, or None if absent or taken on different kernel source."""
-    path = os.path.join(PROFILES, "%s_%s_counters.txt" % (wl.dominant[0], wl.name))
+def committed_traffic(wl: Workload, call: str, profiles: str = PROFILES,
+                      csrc: str = CSRC):
+    """HBM bytes per launch of `call` from the committed counter summary
+    profiles/<call>_<workload>_counters.txt, or None if it is absent or was
+    taken on different kernel or planning source."""
+    path = os.path.join(profiles, "%s_%s_counters.txt" % (call, wl.name))
     if not wl.sources or not os.path.exists(path):
         return None
     vals = {}
@@ -464,7 +508,7 @@ def committed_traffic(wl: Workload):
             if "=" in line and not line.startswith("#"):
                 k, v = line.split("=", 1)
                 vals[k.strip()] = v.strip()
-    if vals.get("kernel_source_sha256_16") != source_hash(wl.sources):
+    if vals.get("kernel_source_sha256_16") != source_hash(wl.sources, csrc):
         return None
     try:
         return float(vals["traffic_bytes_per_launch"])
@@ -473,36 +517,169 @@ def committed_traffic(wl: Workload):
 
 
 # ---------------------------------------------------------------------------
-# main
+# timing
 # ---------------------------------------------------------------------------
 
-def cpu_baseline(wl: Workload, budget_s: float = 10.0):
-    if not wl.cpu:
-        return None
-    total_bytes, t0, steps = 0, time.perf_counter(), 0
+def time_calls(hev, stream_handle, plans, calls, first, count):
+    """An event pair around every call of steps first .. first + count - 1;
+    returns {call name: [durations in ms]}."""
+    import torch
+    record = hev.record_fn
+    evs = [[(hev.create(), hev.create()) for _ in calls] for _ in range(count)]
+    torch.cuda.synchronize()
+    for k in range(count):
+        for j, p in enumerate(plans[first + k]):
+            record(evs[k][j][0], stream_handle)
+            p()
+            record(evs[k][j][1], stream_handle)
+    torch.cuda.synchronize()
+    durs = {c.name: [hev.elapsed_ms(*evs[k][j]) for k in range(count)]
+            for j, c in enumerate(calls)}
+    for row in evs:
+        for a, b in row:
+            hev.destroy(a)
+            hev.destroy(b)
+    return durs
+
+
+def call_entry(call, durs, traffic=None):
+    mean_ms = float(np.mean(durs))
+    gbs = call.nbytes / (mean_ms * 1e-3) / 1e9
+    entry = {"kernel": call.kernel, "bytes": call.nbytes,
+             "mean_us": round(1e3 * mean_ms, 3),
+             "median_us": round(1e3 * float(np.median(durs)), 3),
+             "gbs_mean": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4)}
+    if traffic is not None:
+        entry["traffic"] = traffic
+        entry["traffic_over_algorithmic"] = round(traffic / call.nbytes, 4)
+    return entry
+
+
+def measure_workload(torch, red, orc, name, steps, warmup, hev, stream_handle):
+    """Per-call event timings of one workload (for per_config)."""
+    wl = WORKLOADS[name](torch, red, orc, steps + warmup)
+    plans = [[c.make(k) for c in wl.calls] for k in range(steps + warmup)]
+    for k in range(warmup):
+        for p in plans[k]:
+            p()
+    torch.cuda.synchronize()
+    durs = time_calls(hev, stream_handle, plans, wl.calls, warmup, steps)
+    out = {"workload": "%s: %s" % (wl.name, wl.desc),
+           "calls": {c.name: call_entry(c, durs[c.name], committed_traffic(wl, c.name))
+                     for c in wl.calls}}
+    del plans, wl
+    return out
+
+
+def read_ceiling(torch, hev, stream_handle, x_dev, copies, steps, warmup, cus):
+    """Event-timed read-only streaming kernel (libreduce_calib.so) over the
+    device vector x_dev (and its extra cold copies)."""
+    lib = ctypes.CDLL(os.path.join(ROOT, "fp32_reductions_amd", "libreduce_calib.so"))
+    lib.calib_read_grid.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int]
+    lib.calib_read_grid.restype = ctypes.c_int
+    lib.calib_read_f32.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+                                   ctypes.c_uint, ctypes.c_int, ctypes.c_void_p]
+    lib.calib_read_f32.restype = ctypes.c_int
+    vecs = [x_dev] + list(copies)
+    n = x_dev.numel()
+    grid = max(lib.calib_read_grid(v.data_ptr(), n, cus) for v in vecs)
+    sink = torch.zeros(grid * 256, dtype=torch.int32, device="cuda")
+    match = 0x5EED1E55  # a thread stores its XOR only if it equals this
+
+    def launch(k):
+        v = vecs[k % len(vecs)]
+        rc = lib.calib_read_f32(v.data_ptr(), n, sink.data_ptr(), match, cus, stream_handle)
+        if rc != 0:
+            raise RuntimeError("calib_read_f32: hipError %d" % rc)
+
+    for k in range(warmup):
+        launch(k)
+    torch.cuda.synchronize()
+    record = hev.record_fn
+    evs = [(hev.create(), hev.create()) for _ in range(steps)]
+    for k in range(steps):
+        record(evs[k][0], stream_handle)
+        launch(warmup + k)
+        record(evs[k][1], stream_handle)
+    torch.cuda.synchronize()
+    durs = [hev.elapsed_ms(a, b) for a, b in evs]
+    for a, b in evs:
+        hev.destroy(a)
+        hev.destroy(b)
+    mean_ms = float(np.mean(durs))
+    gbs = 4 * n / (mean_ms * 1e-3) / 1e9
+    return {"kernel": "read_sink_kernel (1-D stream kernel, XOR sink)", "bytes": 4 * n,
+            "mean_us": round(1e3 * mean_ms, 3), "gbs_mean": round(gbs, 1),
+            "frac": round(gbs / HBM_PEAK_GBS, 4), "cold_copies": len(vecs)}
+
+
+# ---------------------------------------------------------------------------
+# CPU baseline
+# ---------------------------------------------------------------------------
+
+def cpu_threads() -> int:
+    """Host threads this process may use: its CPU affinity, capped by
+    OMP_NUM_THREADS when that is set (the per-job CPU share on a shared
+    host)."""
+    n = len(os.sched_getaffinity(0))
+    cap = os.environ.get("OMP_NUM_THREADS", "")
+    if cap.isdigit() and int(cap) > 0:
+        n = min(n, int(cap))
+    return max(1, n)
+
+
+def _time_cpu(calls, budget_s):
+    total_bytes, steps, t0 = 0, 0, time.perf_counter()
     while True:
-        for nbytes, fn in wl.cpu:
+        for nbytes, fn in calls:
             fn()
             total_bytes += nbytes
         steps += 1
         if time.perf_counter() - t0 >= budget_s:
             break
     dt = time.perf_counter() - t0
-    return {"value": round(total_bytes / dt / 1e9, 3), "unit": "GB/s", "cores": 1,
-            "kind": "oracle",
-            "sample": "%d whole step(s) of the same workload (all %d calls, same "
-                      "host arrays), single-threaded C oracle, %.1f s"
-                      % (steps, len(wl.cpu), dt)}
+    return total_bytes / dt / 1e9, steps, dt
+
+
+def cpu_baseline(wl: Workload, budget_s: float = 10.0):
+    """The oracle on whole steps of the workload, threaded on cpu_threads()
+    cores (reported as the baseline) and single-threaded (single_core)."""
+    if not wl.cpu:
+        return None
+    v1, s1, d1 = _time_cpu([(b, f1) for b, f1, _ in wl.cpu], budget_s)
+    single = {"value": round(v1, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+              "sample": "%d whole step(s) of the workload (all %d calls, same host "
+                        "arrays), single-threaded C oracle, %.1f s" % (s1, len(wl.cpu), d1)}
+    threads = cpu_threads()
+    if threads == 1 or any(ft is None for _, _, ft in wl.cpu):
+        return dict(single, single_core=None)
+    vt, st, dt = _time_cpu([(b, (lambda f=ft: f(threads))) for b, _, ft in wl.cpu], budget_s)
+    return {"value": round(vt, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": "%d whole step(s) of the workload (all %d calls, same host arrays), "
+                      "the C oracle's threaded form: %d contiguous pieces on %d threads, "
+                      "combined in order, %.1f s" % (st, len(wl.cpu), threads, threads, dt),
+            "single_core": single}
+
+
+# ---------------------------------------------------------------------------
+# main
+# ---------------------------------------------------------------------------
+
+# The other workloads timed after the headline (one per remaining input
+# configuration, the smallest first).
+PER_CONFIG = ["rows32", "vec16m", "colprod4k", "rows1000"]
 
 
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=500)
-    ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="vec16m", choices=sorted(WORKLOADS))
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="vec1g", choices=sorted(WORKLOADS))
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
-                    help="time budget of the CPU-oracle baseline (0: skip)")
+                    help="time budget of each CPU-oracle baseline (0: skip)")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the per_config and read_ceiling blocks")
     args = ap.parse_args(argv)
 
     if args.gpus != 1:
@@ -555,33 +732,21 @@ def main(argv=None) -> int:
     step_bytes = sum(call.nbytes for call in wl.calls)
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
     dom_durs = {j: [hev.elapsed_ms(a, b) for a, b in ev[j]] for j in dom_idx}
+    for evs in ev.values():
+        for a, b in evs:
+            hev.destroy(a)
+            hev.destroy(b)
 
     # Per-call breakdown (not part of the timed region): a short pass with an
     # event pair around every call.
     kb = min(K, 50)
-    evb = [[(hev.create(), hev.create()) for _ in wl.calls] for _ in range(kb)]
-    torch.cuda.synchronize()
-    for k in range(kb):
-        for j, p in enumerate(plans[W + k]):
-            record(evb[k][j][0], sh)
-            p()
-            record(evb[k][j][1], sh)
-    torch.cuda.synchronize()
-    per_call = {}
-    for j, call in enumerate(wl.calls):
-        durs = [hev.elapsed_ms(evb[k][j][0], evb[k][j][1]) for k in range(kb)]
-        per_call[call.name] = {"kernel": call.kernel, "bytes": call.nbytes,
-                               "mean_us": round(1e3 * float(np.mean(durs)), 3),
-                               "median_us": round(1e3 * float(np.median(durs)), 3),
-                               "gbs_mean": round(call.nbytes / (float(np.mean(durs)) * 1e-3) / 1e9, 1)}
-    for evs in list(ev.values()) + evb:
-        for a, b in evs:
-            hev.destroy(a)
-            hev.destroy(b)
+    durs = time_calls(hev, sh, plans, wl.calls, W, kb)
+    per_call = {c.name: call_entry(c, durs[c.name], committed_traffic(wl, c.name))
+                for c in wl.calls}
     dom_bytes = float(np.mean([wl.calls[j].nbytes for j in dom_idx]))
     dom_us = 1e3 * float(np.mean([np.mean(dom_durs[j]) for j in dom_idx]))
     achieved = dom_bytes / (dom_us * 1e-6) / 1e9
-    traffic = committed_traffic(wl)
+    traffic = committed_traffic(wl, wl.dominant[0])
 
     line = {
         "metric": METRIC,
@@ -606,8 +771,32 @@ def main(argv=None) -> int:
         "per_call": per_call,
         "device": {"name": props.name, "cus": props.multi_processor_count},
     }
+    del plans
+
+    if args.workload == "vec1g" and not args.no_configs:
+        ks, ws = min(K, 30), min(W, 5)
+        x_dev = wl.device_inputs[0]
+        log("read-only ceiling over the 2^30 + 7 vector")
+        ceiling = {"vec1g": read_ceiling(torch, hev, sh, x_dev, [], ks, ws,
+                                         props.multi_processor_count)}
+        n16 = workloads.N_VEC16M
+        small = x_dev[:n16]
+        copies = [small.clone() for _ in range(16)]
+        log("read-only ceiling over 2^24 elements (17 cold copies)")
+        ceiling["vec16m"] = read_ceiling(torch, hev, sh, small, copies, ks, ws,
+                                         props.multi_processor_count)
+        del copies
+        line["read_ceiling"] = ceiling
+        per_config = {}
+        for name in PER_CONFIG:
+            log("per_config: %s" % name)
+            per_config[name] = measure_workload(torch, red, orc, name, ks, ws, hev, sh)
+            torch.cuda.empty_cache()
+        line["per_config"] = per_config
+
     if args.cpu_seconds > 0:
-        log("timing the CPU oracle (~%.0f s)" % args.cpu_seconds)
+        log("timing the CPU oracle (~%.0f s per mode, %d threads)"
+            % (args.cpu_seconds, cpu_threads()))
         line["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
     else:
         line["cpu_baseline"] = None

@@ -39,3 +39,66 @@ def test_every_workload_names_its_counter_summary_format():
         for key in ("kernel_source_sha256_16", "traffic_bytes_per_launch",
                     "algorithmic_bytes_per_launch", "fetch_factor", "write_factor"):
             assert key + " = " in text, (path, key)
+
+
+def _source_tree(tmp_path):
+    """A copy of the kernel and planning sources, laid out as in the repo
+    (csrc/ two levels below the include/ directory)."""
+    import shutil
+    csrc = tmp_path / "pkg" / "csrc"
+    csrc.mkdir(parents=True)
+    (tmp_path / "include").mkdir()
+    for f in bench.SOURCES_1D:
+        dst = csrc / f
+        dst.parent.mkdir(parents=True, exist_ok=True)
+        shutil.copy(os.path.join(bench.CSRC, f), dst)
+    return str(csrc)
+
+
+def test_planning_change_invalidates_traffic(tmp_path):
+    """A counter summary stops counting once the kernel source OR the host
+    planning (grid sizes, workgroups per CU) differs from the one it was
+    taken on."""
+    csrc = _source_tree(tmp_path)
+    prof = tmp_path / "profiles"
+    prof.mkdir()
+    wl = bench.Workload("vec1g", "", {}, [], ["sum"], bench.SOURCES_1D, [])
+    (prof / "sum_vec1g_counters.txt").write_text(
+        "# test\nkernel_source_sha256_16 = %s\ntraffic_bytes_per_launch = 123\n"
+        % bench.source_hash(bench.SOURCES_1D, csrc))
+    assert bench.committed_traffic(wl, "sum", str(prof), csrc) == 123.0
+    assert "api.hip" in bench.SOURCES_1D and "internal.hpp" in bench.SOURCES_1D
+    for f, old, new in (("internal.hpp", "#define RED_STREAM_WG_PER_CU 2",
+                         "#define RED_STREAM_WG_PER_CU 3"),
+                        ("api.hip", "kPartialBytes = size_t(16) << 20",
+                         "kPartialBytes = size_t(8) << 20"),
+                        ("reduce1d.hip", "if (grid > 1)", "if (grid > 2)")):
+        path = os.path.join(csrc, f)
+        text = open(path).read()
+        assert old in text, (f, old)
+        open(path, "w").write(text.replace(old, new, 1))
+        assert bench.committed_traffic(wl, "sum", str(prof), csrc) is None, f
+        open(path, "w").write(text)
+        assert bench.committed_traffic(wl, "sum", str(prof), csrc) == 123.0
+    # a comment-only change keeps the summary
+    path = os.path.join(csrc, "internal.hpp")
+    open(path, "a").write("\n// a comment\n")
+    assert bench.committed_traffic(wl, "sum", str(prof), csrc) == 123.0
+
+
+def test_cpu_threads_respects_the_job_share(monkeypatch):
+    monkeypatch.setenv("OMP_NUM_THREADS", "3")
+    assert 1 <= bench.cpu_threads() <= 3
+    monkeypatch.setenv("OMP_NUM_THREADS", "")
+    assert bench.cpu_threads() == len(os.sched_getaffinity(0))
+
+
+def test_cpu_baseline_reports_threads_and_single_core():
+    """Both oracle modes are timed; the threaded one is the baseline."""
+    import numpy as np
+    import oracle
+    x = np.linspace(-1, 1, 1 << 16, dtype=np.float32)
+    wl = bench.Workload("t", "", {}, [], [], [], bench.vector_cpu(oracle.get(), x, (False,)))
+    b = bench.cpu_baseline(wl, 0.05)
+    assert b["kind"] == "oracle" and b["value"] > 0
+    assert b["single_core"] is None or (b["single_core"]["cores"] == 1 and b["cores"] >= 2)
