@@ -33,7 +33,7 @@ import torch
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIBRARY = os.path.join(_PKG, "libreduce.so")
 
-RED_OK, RED_ERR_INVALID, RED_ERR_ALIGN, RED_ERR_NOMEM, RED_ERR_HIP = range(5)
+RED_OK, RED_ERR_INVALID, RED_ERR_ALIGN, RED_ERR_NOMEM, RED_ERR_HIP, RED_ERR_SCRATCH = range(6)
 
 
 class ReduceError(RuntimeError):
@@ -55,6 +55,7 @@ _SIGS = {
     "red_max_f32": [_P, _SZ, _P, _I, _P],
     "red_min_f32": [_P, _SZ, _P, _I, _P],
     "red_sum_max_min_f32": [_P, _SZ, _P, _I, _P],
+    "red_sum_max_min_f32_noalloc": [_P, _SZ, _P, _I, _P],
     "red_sum_f32_atomic": [_P, _SZ, _P, _I, _P],
     "red_max_f32_atomic": [_P, _SZ, _P, _I, _P],
     "red_min_f32_atomic": [_P, _SZ, _P, _I, _P],
@@ -154,7 +155,7 @@ def _need(t: torch.Tensor, dtype, what: str) -> None:
 def _args_reduce1d(name: str, x, out, accum=False, stream=None):
     _need(x, torch.float32, "x")
     _need(out, torch.float32, "out")
-    need = 3 if name == "red_sum_max_min_f32" else 1
+    need = 3 if name.startswith("red_sum_max_min_f32") else 1
     if out.numel() < need:
         raise ValueError("out needs %d element(s)" % need)
     return (x.data_ptr(), x.numel(), out.data_ptr(), int(bool(accum)),
@@ -183,6 +184,12 @@ def min_f32(x, out, accum=False, stream=None):
 def sum_max_min_f32(x, out, accum=False, stream=None):
     """out[0:3] = [out[0:3] (+, max, min)] (sum, max, min) of x, one read."""
     return _reduce1d("red_sum_max_min_f32", x, out, accum, stream)
+
+
+def sum_max_min_f32_noalloc(x, out, accum=False, stream=None):
+    """sum_max_min_f32 with its partials in the library's static scratch
+    (no allocation); calls overlapping on one GPU race."""
+    return _reduce1d("red_sum_max_min_f32_noalloc", x, out, accum, stream)
 
 
 def sum_f32_atomic(x, out, accum=False, stream=None):
@@ -354,6 +361,7 @@ for _op in ("sum", "max", "min"):
     _MARSHAL["%s_rows_f32" % _op] = ("red_%s_rows_f32" % _op, _args_rows)
     _MARSHAL["%s_cols_f32" % _op] = ("red_%s_cols_f32" % _op, _args_cols)
 _MARSHAL["sum_max_min_f32"] = ("red_sum_max_min_f32", _args_reduce1d)
+_MARSHAL["sum_max_min_f32_noalloc"] = ("red_sum_max_min_f32_noalloc", _args_reduce1d)
 for _t in ("f32", "f16", "bf16", "i32", "i16", "u16", "u32"):
     _MARSHAL["colprod_" + _t] = ("red_colprod_" + _t, _args_colprod)
 

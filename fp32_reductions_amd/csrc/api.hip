@@ -45,8 +45,13 @@ struct Slot {
 enum KeyKind { kStreamKey = 0, kThreadKey = 1 };
 using SlotKey = std::tuple<int, int, uintptr_t>;
 
+// Devices whose compute-unit count is cached (a fixed table, so that a
+// lookup never allocates host memory); devices past it are queried on
+// every call.
+constexpr int kMaxDevices = 64;
+
 std::mutex g_mu;
-std::map<int, DeviceInfo> g_dev;
+DeviceInfo g_dev[kMaxDevices]; // cus == 0: not looked up yet
 std::map<SlotKey, std::shared_ptr<Slot>> g_ws;
 std::atomic<uint64_t> g_next_thread{1};
 
@@ -79,18 +84,25 @@ bool extent_ok(size_t count, size_t stride, size_t width, size_t elem)
 
 int current_device(int* dev, DeviceInfo* info)
 {
-    if (hipGetDevice(dev) != hipSuccess)
+    if (hipGetDevice(dev) != hipSuccess || *dev < 0)
         return RED_ERR_HIP;
-    std::lock_guard<std::mutex> lock(g_mu);
-    auto it = g_dev.find(*dev);
-    if (it == g_dev.end()) {
-        int cus = 0;
-        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount,
-                                  *dev) != hipSuccess || cus <= 0)
-            return RED_ERR_HIP;
-        it = g_dev.emplace(*dev, DeviceInfo{cus}).first;
+    const bool cached = *dev < kMaxDevices;
+    if (cached) {
+        std::lock_guard<std::mutex> lock(g_mu);
+        if (g_dev[*dev].cus > 0) {
+            *info = g_dev[*dev];
+            return RED_OK;
+        }
     }
-    *info = it->second;
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, *dev) !=
+            hipSuccess || cus <= 0)
+        return RED_ERR_HIP;
+    info->cus = cus;
+    if (cached) {
+        std::lock_guard<std::mutex> lock(g_mu);
+        g_dev[*dev] = *info;
+    }
     return RED_OK;
 }
 
@@ -147,6 +159,53 @@ int stream_workspace(int dev, hipStream_t stream, Workspace* ws, HeldWorkspace* 
 }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? RED_OK : RED_ERR_HIP; }
+
+// ---- static scratch of the allocation-free fused call ---------------------
+//
+// red_sum_max_min_f32_noalloc keeps its per-workgroup partials (3 floats
+// per workgroup of the first pass) in this file-scope device array instead
+// of a hipMalloc'd workspace.  Each GPU the library runs on holds its own
+// copy until the process ends, and every call on that GPU shares it.  In
+// host code `scratch` only names the symbol: its device address on a
+// device comes from hipGetSymbolAddress, taken once per device (with that
+// device current) on the first call there and kept in g_scratch.
+constexpr size_t kScratchBytes = 16384;
+static __device__ __align__(256) float scratch[kScratchBytes / sizeof(float)];
+
+std::mutex g_scratch_mu;
+float* g_scratch[kMaxDevices]; // device address of each device's `scratch`
+
+// The device address of `scratch` on the current device `dev`.
+int scratch_address(int dev, float** out)
+{
+    if (dev >= kMaxDevices)
+        return RED_ERR_HIP;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+            (void)hipGetLastError();
+            return RED_ERR_HIP;
+        }
+        g_scratch[dev] = static_cast<float*>(p);
+    }
+    *out = g_scratch[dev];
+    return RED_OK;
+}
+
+// Bytes of scratch a call may use: kScratchBytes, or less when the test
+// hook RED_TEST_SCRATCH_LIMIT (bytes) asks for less, so that tests can
+// reach the rejection path on a device whose grids always fit.
+size_t scratch_limit()
+{
+    const char* s = std::getenv("RED_TEST_SCRATCH_LIMIT");
+    if (s && *s) {
+        const unsigned long long v = std::strtoull(s, nullptr, 10);
+        if (v < kScratchBytes)
+            return (size_t)v;
+    }
+    return kScratchBytes;
+}
 
 // Called right before a call's launches: drops an error an earlier,
 // unrelated HIP call left on this thread, so that the status returned after
@@ -206,6 +265,31 @@ int reduce1d_summaxmin(const float* x, size_t n, float* out, int accum,
         return st;
     clear_stale_error();
     return hip_status(red::launch_reduce1d_summaxmin(x, n, out, accum, info, ws, s));
+}
+
+int reduce1d_summaxmin_noalloc(const float* x, size_t n, float* out, int accum,
+                               red_stream_t stream)
+{
+    if (n == 0)
+        return RED_OK;
+    int st = check_1d(x, n, out);
+    if (st != RED_OK)
+        return st;
+    int dev;
+    DeviceInfo info;
+    if ((st = current_device(&dev, &info)) != RED_OK)
+        return st;
+    Workspace ws;
+    ws.partial_bytes = scratch_limit();
+    if ((size_t)red::reduce1d_grid(x, n, info) * 3 * sizeof(float) > ws.partial_bytes)
+        return RED_ERR_SCRATCH;
+    float* p;
+    if ((st = scratch_address(dev, &p)) != RED_OK)
+        return st;
+    ws.partials = p;
+    clear_stale_error();
+    return hip_status(red::launch_reduce1d_summaxmin(x, n, out, accum, info, ws,
+                                                     static_cast<hipStream_t>(stream)));
 }
 
 int reduce1d_atomic(OpKind op, const float* x, size_t n, float* out, int accum,
@@ -336,6 +420,12 @@ int red_sum_max_min_f32(const float* x, size_t n, float* out, int accum, red_str
     return reduce1d_summaxmin(x, n, out, accum, stream);
 }
 
+int red_sum_max_min_f32_noalloc(const float* x, size_t n, float* out, int accum,
+                                red_stream_t stream)
+{
+    return reduce1d_summaxmin_noalloc(x, n, out, accum, stream);
+}
+
 int red_sum_f32_atomic(const float* x, size_t n, float* out, int accum, red_stream_t stream)
 {
     return reduce1d_atomic(OpKind::Sum, x, n, out, accum, stream);
@@ -454,6 +544,7 @@ const char* red_status_str(int status)
     case RED_ERR_ALIGN: return "pointer not aligned to its element size";
     case RED_ERR_NOMEM: return "workspace allocation failed";
     case RED_ERR_HIP: return "HIP runtime error";
+    case RED_ERR_SCRATCH: return "the call needs more scratch than the static buffer holds";
     default: return "unknown status";
     }
 }

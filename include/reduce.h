@@ -78,7 +78,7 @@
 extern "C" {
 #endif
 
-#define RED_ABI_VERSION 1
+#define RED_ABI_VERSION 2
 
 /* A hipStream_t, passed as an opaque pointer (NULL: the null stream). */
 typedef void* red_stream_t;
@@ -89,7 +89,9 @@ enum red_status {
                             or a size whose byte extent overflows size_t */
     RED_ERR_ALIGN = 2,   /* a pointer not aligned to its element size */
     RED_ERR_NOMEM = 3,   /* the per-stream workspace could not be allocated */
-    RED_ERR_HIP = 4      /* the HIP runtime reported an error */
+    RED_ERR_HIP = 4,     /* the HIP runtime reported an error */
+    RED_ERR_SCRATCH = 5  /* red_sum_max_min_f32_noalloc: the grid would need
+                            more than the static scratch buffer holds */
 };
 
 /* ---------------------------------------------------------------------
@@ -124,6 +126,24 @@ int red_min_f32(const float* x, size_t n, float* out, int accum,
  * aligned and must not overlap x. */
 int red_sum_max_min_f32(const float* x, size_t n, float* out, int accum,
                         red_stream_t stream);
+
+/* For callers that cannot allocate (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): red_sum_max_min_f32
+ * without any device or host allocation.  Same arguments, results (bit for
+ * bit) and errors, and the same two kernels, but the per-workgroup partials
+ * (12 bytes per workgroup of the first pass, at most 2 workgroups per
+ * compute unit) live in a 16 KiB static device buffer that the library
+ * declares and that each GPU it runs on holds until the process ends.
+ * Calls whose grid would need more than 16 KiB of partials (devices of
+ * more than 682 compute units) return RED_ERR_SCRATCH and enqueue nothing.
+ * Nothing in the buffer has to start at zero: the first kernel writes
+ * every partial the second reads.  Every call on one GPU shares that GPU's
+ * buffer, whatever its stream or host thread: calls that overlap in time
+ * on one GPU race and give wrong results, so the caller must order them
+ * (for example, issue them all on one stream).  The first call on a device
+ * looks up the buffer's device address once (hipGetSymbolAddress). */
+int red_sum_max_min_f32_noalloc(const float* x, size_t n, float* out, int accum,
+                                red_stream_t stream);
 
 /* Single-pass variants: each workgroup folds its partial into *out with
  * one device-scope atomic, as the one-atomic-per-program block reduce in

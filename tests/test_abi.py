@@ -17,7 +17,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "reduce.h")
 LIBRARY = os.path.join(ROOT, "fp32_reductions_amd", "libreduce.so")
 
-RED_OK, RED_ERR_INVALID, RED_ERR_ALIGN, RED_ERR_NOMEM, RED_ERR_HIP = range(5)
+RED_OK, RED_ERR_INVALID, RED_ERR_ALIGN, RED_ERR_NOMEM, RED_ERR_HIP, RED_ERR_SCRATCH = range(6)
 
 # Fake device addresses: aligned and misaligned; never dereferenced.
 A16 = 0x7F0000000000
@@ -75,8 +75,8 @@ def test_version_and_status_strings(lib):
     assert lib.red_abi_version() == ver
     lib.red_status_str.restype = ctypes.c_char_p
     lib.red_status_str.argtypes = [I]
-    texts = [lib.red_status_str(s).decode() for s in range(5)]
-    assert texts[0] == "ok" and len(set(texts)) == 5
+    texts = [lib.red_status_str(s).decode() for s in range(6)]
+    assert texts[0] == "ok" and len(set(texts)) == 6
     assert lib.red_status_str(99).decode() == "unknown status"
 
 
@@ -88,7 +88,7 @@ def _fn(lib, name, argtypes):
 
 
 @pytest.mark.parametrize("name", ["red_sum_f32", "red_max_f32", "red_min_f32",
-                                  "red_sum_max_min_f32",
+                                  "red_sum_max_min_f32", "red_sum_max_min_f32_noalloc",
                                   "red_sum_f32_atomic", "red_max_f32_atomic",
                                   "red_min_f32_atomic"])
 def test_1d_validation(lib, name):
