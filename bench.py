@@ -80,6 +80,7 @@ HOST_PLANNING = ["api.hip", "internal.hpp"]
 SOURCES_1D = ["reduce1d.hip"] + DEVICE_HEADERS + HOST_PLANNING
 SOURCES_ROWS = ["rows.hip"] + DEVICE_HEADERS + HOST_PLANNING
 SOURCES_COLS = ["colprod.hip"] + DEVICE_HEADERS + HOST_PLANNING
+SOURCES_ROWS_COLS = SOURCES_ROWS + ["colprod.hip"]  # row calls and column products
 
 
 def log(msg: str) -> None:
@@ -407,7 +408,7 @@ def wl_rows1000(torch, red, orc, steps):
         "products of 2048 x 32768 bf16 and f16 tiles, uniform[0.99,1.01), seed 4",
         {"rows": rows, "n": n, "R": R, "C": C, "calls_per_step": 4,
          "cold_copies": [len(xs), len(bs), len(hs)]},
-        calls, ["rows_sum"], SOURCES_ROWS, cpu)
+        calls, ["rows_sum"], SOURCES_ROWS_COLS, cpu)
 
 
 def wl_cols4k(torch, red, orc, steps):
@@ -454,7 +455,7 @@ def wl_rows32(torch, red, orc, steps):
         "4096 rows x 32 fp32, uniform[-1,1), seed 0: row sum, max, min (one "
         "thread per row, rows staged in LDS); one 16 x 16 fp32 tile column product",
         {"rows": rows, "n": n, "calls_per_step": 4, "cold_copies": 1},
-        calls, ["rows_sum"], SOURCES_ROWS, cpu)
+        calls, ["rows_sum"], SOURCES_ROWS_COLS, cpu)
 
 
 def wl_copycal(torch, red, orc, steps):
