@@ -4,13 +4,14 @@
 // library (libreduce_calib.so).
 //
 // The kernel is the 1-D stream kernel with the reduction replaced by a
-// trivial sink: the same grid (two workgroups per CU, at most one per
-// 32 KiB sweep), the same grid-stride sweeps of eight non-temporal 16-byte
-// loads per thread (stream_chunk), but each element's bits are XORed into
-// one word per thread instead of being added, and a thread stores its word
-// only when it equals a value the caller passes (so the loads cannot be
-// removed, and in practice nothing is stored).  Its time for a vector is
-// therefore what reading the vector costs on this device, launch included.
+// trivial sink: the same launch shape (stream_shape) and the same sweeps of
+// eight non-temporal 16-byte loads per thread (stream_chunk or
+// stream_regions), but each element's bits are XORed into one word per
+// thread instead of being added, and a thread stores its word only when it
+// equals a value the caller passes (so the loads cannot be removed, and in
+// practice nothing is stored).  Its time for a vector is therefore what
+// reading the vector costs on this device with that launch, launch
+// included.
 #include <hip/hip_runtime.h>
 
 #include "device.hpp"
@@ -34,13 +35,17 @@ struct AccXor {
     __device__ __forceinline__ void fold_scalar(float v) { w ^= __float_as_uint(v); }
 };
 
+template <bool REGIONAL>
 __global__ __launch_bounds__(kBlock) void read_sink_kernel(const float* __restrict__ x,
                                                            uint64_t n,
                                                            uint32_t* __restrict__ sink,
                                                            uint32_t match)
 {
     AccXor acc;
-    stream_chunk(x, n, blockIdx.x, gridDim.x, acc);
+    if constexpr (REGIONAL)
+        stream_regions(x, n, acc);
+    else
+        stream_chunk(x, n, blockIdx.x, gridDim.x, acc);
     if (acc.w == match)
         sink[(uint64_t)blockIdx.x * kBlock + threadIdx.x] = acc.w;
 }
@@ -48,15 +53,10 @@ __global__ __launch_bounds__(kBlock) void read_sink_kernel(const float* __restri
 } // namespace
 } // namespace red
 
-// The stream kernel's grid for x[0, n): one workgroup per 32 KiB sweep, at
-// most kStreamWgPerCu per CU.
+// The stream kernel's grid for x[0, n).
 extern "C" int calib_read_grid(const float* x, size_t n, int cus)
 {
-    uint64_t g = red::sweep_count(x, n);
-    const uint64_t cap = (uint64_t)cus * red::kStreamWgPerCu;
-    if (g > cap)
-        g = cap;
-    return (int)(g < 1 ? 1 : g);
+    return (int)red::stream_shape(x, n, cus, red::kStreamWgPerCu).grid;
 }
 
 // Streams x[0, n) once on `stream`.  sink must hold grid * 256 words, grid
@@ -67,8 +67,11 @@ extern "C" int calib_read_f32(const float* x, size_t n, unsigned* sink,
 {
     if (n == 0)
         return 0;
-    const unsigned grid = (unsigned)calib_read_grid(x, n, cus);
-    red::read_sink_kernel<<<grid, red::kBlock, 0, static_cast<hipStream_t>(stream)>>>(
-        x, n, sink, match);
+    const red::StreamShape sh = red::stream_shape(x, n, cus, red::kStreamWgPerCu);
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    if (sh.regional)
+        red::read_sink_kernel<true><<<sh.grid, red::kBlock, 0, s>>>(x, n, sink, match);
+    else
+        red::read_sink_kernel<false><<<sh.grid, red::kBlock, 0, s>>>(x, n, sink, match);
     return (int)hipGetLastError();
 }

@@ -209,6 +209,101 @@ __device__ __forceinline__ void stream_chunk(const float* __restrict__ x,
     }
 }
 
+// ---------------------------------------------------------------------------
+// Streaming one long vector region by region.
+//
+// MI355X dispatches the workgroups of a grid to its kXcds XCDs round-robin
+// by linear index, each XCD with its own L2.  Here the vector's sweeps are
+// cut into kXcds contiguous regions of equal length (the last one shorter),
+// workgroup b serves region b mod kXcds, and the gridDim.x / kXcds
+// workgroups of one region take its sweeps in grid-stride order.  So each
+// XCD streams one contiguous stretch of the vector.  The partial last
+// sweep goes to the workgroup whose turn it is; the scalars before the
+// first 16-byte boundary and after the last whole vector go to thread 0 of
+// workgroup 0.  gridDim.x must be a multiple of kXcds.  (Measured on MI355X
+// with a read-only sink, 4 GiB: one workgroup per CU, 8 loads in flight,
+// regions 577 us = 7.44 TB/s; the same grid in plain grid-stride order 589
+// us; two workgroups per CU in grid-stride order 600 us.  1 GiB 145.5
+// against 153.6 us, 256 MiB 38.7 against 39.9 us; at 64 MiB plain order on
+// two workgroups per CU stays faster, 11.0 against 11.5 us.)
+// ---------------------------------------------------------------------------
+constexpr uint32_t kXcds = 8;
+
+template <class AccT>
+__device__ __forceinline__ void stream_regions(const float* __restrict__ x,
+                                               uint64_t n, AccT& acc)
+{
+    const uint32_t head = head_count(x, n);
+    const uint64_t nvec = (n - head) / 4;
+    const float4* __restrict__ xv = reinterpret_cast<const float4*>(x + head);
+    const uint64_t per = gridDim.x / kXcds;   // workgroups per region
+    const uint64_t region = blockIdx.x % kXcds;
+    const uint64_t sweeps = (nvec + kSweep - 1) / kSweep;
+    const uint64_t full = nvec / kSweep;      // sweeps of kSweep whole vectors
+    const uint64_t len = (sweeps + kXcds - 1) / kXcds;
+    const uint64_t first = region * len + blockIdx.x / kXcds;
+    const uint64_t end = (region + 1) * len < sweeps ? (region + 1) * len : sweeps;
+    const uint64_t stop = end < full ? end : full;
+
+    uint64_t s = first;
+    for (; s < stop; s += per) {
+        const uint64_t i = s * kSweep + threadIdx.x;
+        float4 v[kStreamUnroll];
+#pragma unroll
+        for (int u = 0; u < kStreamUnroll; ++u)
+            v[u] = load_stream(xv + i + (uint64_t)u * kBlock);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int u = 0; u < kStreamUnroll; u += 2)
+            acc.fold2(v[u], v[u + 1]);
+    }
+    // The partial last sweep (index `full`, present when nvec is not a
+    // multiple of kSweep), if it lies in this region and is this
+    // workgroup's turn.
+    if (s == full && full < end)
+        for (uint64_t i = full * kSweep + threadIdx.x; i < nvec; i += kBlock)
+            acc.fold1(load_stream(xv + i));
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+        for (uint32_t k = 0; k < head; ++k)
+            acc.fold_scalar(x[k]);
+        for (uint64_t k = head + 4 * nvec; k < n; ++k)
+            acc.fold_scalar(x[k]);
+    }
+}
+
+// Launch shape of a kernel that streams one vector: vectors of at least
+// kRegionalMinBytes on a device whose CU count is a multiple of kXcds run
+// one workgroup per CU region by region (stream_regions); shorter ones run
+// kStreamWgPerCu per CU, at most one per sweep, in plain grid-stride order
+// (stream_chunk).
+#ifndef RED_REGIONAL_MIN_BYTES
+#define RED_REGIONAL_MIN_BYTES (128ull << 20)
+#endif
+constexpr uint64_t kRegionalMinBytes = RED_REGIONAL_MIN_BYTES;
+
+struct StreamShape {
+    unsigned grid = 1;
+    bool regional = false;
+};
+
+inline StreamShape stream_shape(const float* x, uint64_t n, int cus, int wg_per_cu)
+{
+    StreamShape sh;
+    const uint64_t sweeps = sweep_count(x, n);
+    if (n * sizeof(float) >= kRegionalMinBytes && cus % (int)kXcds == 0 &&
+        sweeps >= (uint64_t)cus) {
+        sh.grid = (unsigned)cus;
+        sh.regional = true;
+        return sh;
+    }
+    uint64_t g = sweeps;
+    const uint64_t cap = (uint64_t)cus * (uint64_t)wg_per_cu;
+    if (g > cap)
+        g = cap;
+    sh.grid = (unsigned)(g < 1 ? 1 : g);
+    return sh;
+}
+
 // Folding, in index order, the values v[t], v[t + kBlock], v[t + 2 kBlock],
 // ... (t = threadIdx.x, indices below count >= 1) into a starting value,
 // with every load of the first kFinishBatch rounds issued before the first

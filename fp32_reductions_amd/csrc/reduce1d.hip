@@ -28,12 +28,24 @@
 namespace red {
 namespace {
 
-template <class Op>
+// The workgroup's share of x, in grid-stride order over the whole vector
+// or region by region (long vectors).
+template <bool REGIONAL, class AccT>
+__device__ __forceinline__ void stream_share(const float* __restrict__ x, uint64_t n,
+                                             AccT& acc)
+{
+    if constexpr (REGIONAL)
+        stream_regions(x, n, acc);
+    else
+        stream_chunk(x, n, blockIdx.x, gridDim.x, acc);
+}
+
+template <class Op, bool REGIONAL>
 __device__ __forceinline__ float thread_part(const float* __restrict__ x,
                                              uint64_t n)
 {
     Acc<Op> acc(Op::identity());
-    stream_chunk(x, n, blockIdx.x, gridDim.x, acc);
+    stream_share<REGIONAL>(x, n, acc);
     return acc.collapse();
 }
 
@@ -102,13 +114,13 @@ __device__ __forceinline__ void block_reduce_sum_max_min(float vs, float vx,
 // one workgroup (short vectors) is the whole call: it writes *out itself,
 // with the old value folded first under accum, exactly as the finish
 // kernel would, and no second kernel is launched.
-template <class Op>
+template <class Op, bool REGIONAL>
 __global__ __launch_bounds__(kBlock) void reduce1d_stream_kernel(
     const float* __restrict__ x, uint64_t n, float* __restrict__ partials,
     float* __restrict__ out, int accum)
 {
     __shared__ float lds[kWaves];
-    const float r = block_reduce<Op>(thread_part<Op>(x, n), lds);
+    const float r = block_reduce<Op>(thread_part<Op, REGIONAL>(x, n), lds);
     if (threadIdx.x == 0) {
         if (gridDim.x == 1)
             *out = accum ? Op::apply(*out, r) : r;
@@ -138,13 +150,14 @@ __global__ __launch_bounds__(kBlock) void reduce1d_finish_kernel(
 
 // Fused first pass: partials[b], partials[G + b], partials[2G + b] receive
 // workgroup b's sum, max and min.
+template <bool REGIONAL>
 __global__ __launch_bounds__(kBlock) void reduce1d_summaxmin_stream_kernel(
     const float* __restrict__ x, uint64_t n, float* __restrict__ partials,
     float* __restrict__ out, int accum)
 {
     __shared__ float lds[3][kWaves];
     AccSumMaxMin acc;
-    stream_chunk(x, n, blockIdx.x, gridDim.x, acc);
+    stream_share<REGIONAL>(x, n, acc);
     float r[3];
     block_reduce_sum_max_min(acc.sum.collapse(), acc.max.collapse(),
                              acc.min.collapse(), lds, r);
@@ -239,12 +252,12 @@ __device__ void atomic_fold_extreme(float* out, float r)
     }
 }
 
-template <class Op>
+template <class Op, bool REGIONAL>
 __global__ __launch_bounds__(kBlock) void reduce1d_atomic_kernel(
     const float* __restrict__ x, uint64_t n, float* __restrict__ out)
 {
     __shared__ float lds[kWaves];
-    const float r = block_reduce<Op>(thread_part<Op>(x, n), lds);
+    const float r = block_reduce<Op>(thread_part<Op, REGIONAL>(x, n), lds);
     if (threadIdx.x == 0) {
         if constexpr (__is_same(Op, OpSum))
             unsafeAtomicAdd(out, r); // hardware global_atomic_add_f32
@@ -263,10 +276,14 @@ __global__ void fill_u32_kernel(unsigned* __restrict__ p, uint64_t count,
 
 template <class Op>
 hipError_t launch_det(const float* x, size_t n, float* out, int accum,
-                      unsigned grid, const Workspace& ws, hipStream_t stream)
+                      StreamShape sh, const Workspace& ws, hipStream_t stream)
 {
     float* partials = static_cast<float*>(ws.partials);
-    reduce1d_stream_kernel<Op><<<grid, kBlock, 0, stream>>>(x, n, partials, out, accum);
+    const unsigned grid = sh.grid;
+    if (sh.regional)
+        reduce1d_stream_kernel<Op, true><<<grid, kBlock, 0, stream>>>(x, n, partials, out, accum);
+    else
+        reduce1d_stream_kernel<Op, false><<<grid, kBlock, 0, stream>>>(x, n, partials, out, accum);
     if (grid > 1)
         reduce1d_finish_kernel<Op><<<1, kBlock, 0, stream>>>(partials, grid, out, accum);
     return hipGetLastError();
@@ -274,7 +291,7 @@ hipError_t launch_det(const float* x, size_t n, float* out, int accum,
 
 template <class Op>
 hipError_t launch_atomic(const float* x, size_t n, float* out, int accum,
-                         unsigned grid, hipStream_t stream)
+                         StreamShape sh, hipStream_t stream)
 {
     if (!accum) {
         // -0.0 for the sum; for max / min the NaN that loses every
@@ -283,21 +300,36 @@ hipError_t launch_atomic(const float* x, size_t n, float* out, int accum,
         fill_u32_kernel<<<1, 64, 0, stream>>>(
             reinterpret_cast<unsigned*>(out), 1, ident);
     }
-    reduce1d_atomic_kernel<Op><<<grid, kBlock, 0, stream>>>(x, n, out);
+    if (sh.regional)
+        reduce1d_atomic_kernel<Op, true><<<sh.grid, kBlock, 0, stream>>>(x, n, out);
+    else
+        reduce1d_atomic_kernel<Op, false><<<sh.grid, kBlock, 0, stream>>>(x, n, out);
     return hipGetLastError();
 }
 
 } // namespace
 
+// Launch shape of the deterministic 1-D kernels for x[0, n).
+StreamShape reduce1d_shape(const float* x, size_t n, const DeviceInfo& dev)
+{
+    return stream_shape(x, n, dev.cus, kStreamWgPerCu);
+}
+
 hipError_t launch_reduce1d_summaxmin(const float* x, size_t n, float* out,
                                      int accum, const DeviceInfo& dev,
                                      const Workspace& ws, hipStream_t stream)
 {
-    const unsigned grid = reduce1d_grid(x, n, dev);
+    const StreamShape sh = reduce1d_shape(x, n, dev);
+    const unsigned grid = sh.grid;
     if ((size_t)grid * 3 * sizeof(float) > ws.partial_bytes)
         return hipErrorInvalidValue;
     float* partials = static_cast<float*>(ws.partials);
-    reduce1d_summaxmin_stream_kernel<<<grid, kBlock, 0, stream>>>(x, n, partials, out, accum);
+    if (sh.regional)
+        reduce1d_summaxmin_stream_kernel<true><<<grid, kBlock, 0, stream>>>(x, n, partials, out,
+                                                                           accum);
+    else
+        reduce1d_summaxmin_stream_kernel<false><<<grid, kBlock, 0, stream>>>(x, n, partials, out,
+                                                                            accum);
     if (grid > 1)
         reduce1d_summaxmin_finish_kernel<<<1, kBlock, 0, stream>>>(partials, grid, out, accum);
     return hipGetLastError();
@@ -305,26 +337,20 @@ hipError_t launch_reduce1d_summaxmin(const float* x, size_t n, float* out,
 
 unsigned reduce1d_grid(const float* x, size_t n, const DeviceInfo& dev)
 {
-    uint64_t g = sweep_count(x, n);
-    const uint64_t cap = (uint64_t)dev.cus * kStreamWgPerCu;
-    if (g > cap)
-        g = cap;
-    if (g < 1)
-        g = 1;
-    return (unsigned)g;
+    return reduce1d_shape(x, n, dev).grid;
 }
 
 hipError_t launch_reduce1d(OpKind op, const float* x, size_t n, float* out,
                            int accum, const DeviceInfo& dev,
                            const Workspace& ws, hipStream_t stream)
 {
-    const unsigned grid = reduce1d_grid(x, n, dev);
-    if ((size_t)grid * sizeof(float) > ws.partial_bytes)
+    const StreamShape sh = reduce1d_shape(x, n, dev);
+    if ((size_t)sh.grid * sizeof(float) > ws.partial_bytes)
         return hipErrorInvalidValue;
     switch (op) {
-    case OpKind::Sum: return launch_det<OpSum>(x, n, out, accum, grid, ws, stream);
-    case OpKind::Max: return launch_det<OpMax>(x, n, out, accum, grid, ws, stream);
-    case OpKind::Min: return launch_det<OpMin>(x, n, out, accum, grid, ws, stream);
+    case OpKind::Sum: return launch_det<OpSum>(x, n, out, accum, sh, ws, stream);
+    case OpKind::Max: return launch_det<OpMax>(x, n, out, accum, sh, ws, stream);
+    case OpKind::Min: return launch_det<OpMin>(x, n, out, accum, sh, ws, stream);
     }
     return hipErrorInvalidValue;
 }
@@ -339,13 +365,11 @@ hipError_t launch_reduce1d_atomic(OpKind op, const float* x, size_t n,
     // MI355X, 64 MiB, median per call: sum with accum 16.7 -> 13.9 us,
     // without 20.8 -> 18.2 us; max without accum 20.3 -> 18.1 us; max with
     // accum, whose workgroups mostly skip their atomic, 11.8 -> 12.1 us.)
-    unsigned grid = reduce1d_grid(x, n, dev);
-    if (grid > (unsigned)dev.cus * kAtomicWgPerCu)
-        grid = (unsigned)dev.cus * kAtomicWgPerCu;
+    const StreamShape sh = stream_shape(x, n, dev.cus, kAtomicWgPerCu);
     switch (op) {
-    case OpKind::Sum: return launch_atomic<OpSum>(x, n, out, accum, grid, stream);
-    case OpKind::Max: return launch_atomic<OpMax>(x, n, out, accum, grid, stream);
-    case OpKind::Min: return launch_atomic<OpMin>(x, n, out, accum, grid, stream);
+    case OpKind::Sum: return launch_atomic<OpSum>(x, n, out, accum, sh, stream);
+    case OpKind::Max: return launch_atomic<OpMax>(x, n, out, accum, sh, stream);
+    case OpKind::Min: return launch_atomic<OpMin>(x, n, out, accum, sh, stream);
     }
     return hipErrorInvalidValue;
 }

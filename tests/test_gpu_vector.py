@@ -138,6 +138,34 @@ def test_extreme_positions(red, orc, n):
         assert run(red, "min", dev(x)) == np.float32(-5.0), where
 
 
+# Vectors of 128 MiB and more are streamed region by region (one contiguous
+# eighth of the sweeps per XCD): lengths that leave a partial last sweep in
+# the last region, odd element counts and misaligned starts.
+REGIONAL = [((1 << 25), 0), ((1 << 25) + 7, 1), ((1 << 25) + 3 * 8192 + 5, 3),
+            ((1 << 25) + 12345678, 2), ((1 << 26) - 1, 1)]
+
+
+@pytest.fixture(scope="module")
+def regional_base():
+    say("generate the base vector of the regional cases")
+    x = workloads.uniform_f32(41, (1 << 26) + 16, -3.0, 3.0)
+    return x, dev(x)
+
+
+@pytest.mark.parametrize("n,off", REGIONAL)
+def test_regional_lengths(red, orc, regional_base, n, off):
+    base, bd = regional_base
+    x, xd = base[off:off + n], bd[off:off + n]
+    say("regional n=%d off=%d" % (n, off))
+    for op in OPS:
+        for atomic in (False, True):
+            for accum, old in ((False, 0.0), (True, -1.5)):
+                got = run(red, op, xd, accum, old, atomic)
+                check(orc, op, x, got, accum, old,
+                      "regional n=%d off=%d %s atomic=%s accum=%s" % (n, off, op, atomic, accum))
+    check_fused(red, orc, x, xd, True, (2.0, -7.0, 7.0), "regional n=%d off=%d" % (n, off))
+
+
 def test_integer_sums_are_exact(red):
     """Integers in [-8, 8]: every partial sum is an integer below 2^24, so
     every order is exact and the fp32 result equals the exact sum."""

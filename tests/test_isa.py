@@ -154,9 +154,9 @@ def test_streaming_loads_are_nontemporal_dwordx4(code):
 
 
 def test_max_min_fold_three_at_a_time(code):
-    for name, txt in kernels(code, r"reduce1d_stream_kernel<red_dev::OpMax>").items():
+    for name, txt in kernels(code, r"reduce1d_stream_kernel<red_dev::OpMax, (true|false)>").items():
         assert txt.count("v_max3_f32") >= 8, name
-    for name, txt in kernels(code, r"reduce1d_stream_kernel<red_dev::OpMin>").items():
+    for name, txt in kernels(code, r"reduce1d_stream_kernel<red_dev::OpMin, (true|false)>").items():
         assert txt.count("v_min3_f32") >= 8, name
 
 
@@ -168,9 +168,9 @@ def test_wave_reduction_uses_dpp(code):
 
 
 def test_atomic_sum_uses_hardware_float_add(code):
-    for name, txt in kernels(code, r"reduce1d_atomic_kernel<red_dev::OpSum>").items():
+    for name, txt in kernels(code, r"reduce1d_atomic_kernel<red_dev::OpSum, (true|false)>").items():
         assert "global_atomic_add_f32" in txt, name
-    for name, txt in kernels(code, r"reduce1d_atomic_kernel<red_dev::OpMax>").items():
+    for name, txt in kernels(code, r"reduce1d_atomic_kernel<red_dev::OpMax, (true|false)>").items():
         assert "global_atomic_smax" in txt and "global_atomic_umin" in txt, name
-    for name, txt in kernels(code, r"reduce1d_atomic_kernel<red_dev::OpMin>").items():
+    for name, txt in kernels(code, r"reduce1d_atomic_kernel<red_dev::OpMin, (true|false)>").items():
         assert "global_atomic_smin" in txt and "global_atomic_umax" in txt, name
