@@ -226,7 +226,8 @@ def wl_vec16m(torch, red, orc, steps):
         def accum(k, op=op, j=j):
             return red.plan(op + "_f32", xs.next(), accs[k, j:j + 1], accum=True)
 
-        kern = "reduce1d_stream_kernel<Op{0}> + reduce1d_finish_kernel<Op{0}>".format(op.capitalize())
+        kern = "reduce1d_stream_kernel<Op{0}, false> + reduce1d_finish_kernel<Op{0}>".format(
+            op.capitalize())
         calls.append(Call(op, kern, 4 * n + 4, plain))
         calls.append(Call(op + "_accum", kern, 4 * n + 8, accum))
     calls = [calls[0], calls[2], calls[4], calls[1], calls[3], calls[5]]
@@ -255,7 +256,7 @@ def wl_vec16m_atomic(torch, red, orc, steps):
         def accum(k, op=op, j=j):
             return red.plan(op + "_f32_atomic", xs.next(), accs[k, j:j + 1], accum=True)
 
-        kern = "reduce1d_atomic_kernel<Op{0}>".format(op.capitalize())
+        kern = "reduce1d_atomic_kernel<Op{0}, false>".format(op.capitalize())
         calls.append(Call(op, "fill_u32_kernel + " + kern, 4 * n + 4, plain))
         calls.append(Call(op + "_accum", kern, 4 * n + 8, accum))
     calls = [calls[0], calls[2], calls[4], calls[1], calls[3], calls[5]]
@@ -276,7 +277,7 @@ def wl_vec16m_fused(torch, red, orc, steps):
     outs = torch.zeros((steps, 3), dtype=torch.float32, device="cuda")
     accs = torch.full((steps, 3), workloads.ACCUM_PRESET, dtype=torch.float32,
                       device="cuda")
-    kern = "reduce1d_summaxmin_stream_kernel + reduce1d_summaxmin_finish_kernel"
+    kern = "reduce1d_summaxmin_stream_kernel<false> + reduce1d_summaxmin_finish_kernel"
     calls = [Call("sum_max_min", kern, 4 * n + 12,
                   lambda k: red.plan("sum_max_min_f32", xs.next(), outs[k])),
              Call("sum_max_min_accum", kern, 4 * n + 24,
@@ -307,7 +308,7 @@ def wl_vec1g(torch, red, orc, steps):
     outs = torch.zeros((steps, 3), dtype=torch.float32, device="cuda")
     calls = []
     for j, op in enumerate(("sum", "max", "min")):
-        kern = ("reduce1d_stream_kernel<Op{0}> (+ reduce1d_finish_kernel<Op{0}>, one "
+        kern = ("reduce1d_stream_kernel<Op{0}, true> (+ reduce1d_finish_kernel<Op{0}>, one "
                 "workgroup)".format(op.capitalize()))
         calls.append(Call(op, kern, 4 * n + 4,
                           lambda k, op=op, j=j: red.plan(op + "_f32", xd, outs[k, j:j + 1])))
