@@ -213,24 +213,31 @@ struct OpMul {
 // dst[j] is folded in first.
 //
 // A column block is kCols = 16 * V columns (256 bytes of each row).  A
-// workgroup's 256 threads form 16 row groups of 16 lanes, GPB row groups
-// per column block, so that it owns 16 / GPB adjacent column blocks: row
-// group gr of a block reads rows gr, gr + GPB, gr + 2 GPB, ... of each of
-// its chunks of GPB * kRowsInFlight rows, each lane one 16-byte vector per
-// row, with kRowsInFlight rows in flight.  The GPB partial products of a block are
-// combined in LDS in row-group order (GPB = 1 stores straight from the
-// lanes).  GPB = 16 (one block per workgroup, a wave reading 256 bytes of
-// four rows) serves tiles of many rows; GPB = 4 and 1 give short, wide
-// tiles fewer and longer-lived workgroups, a wave reading 1 KiB of a row.
-// (Measured on MI355X for a 4096 x 16384 fp32 tile read from HBM: 40.6 us
-// per call with 256 workgroups of GPB = 16 and no second pass, against
-// 44.1 us for workgroups of 256 columns whose waves each read 1 KiB of a
-// row, split four ways over the rows and finished by a second kernel.)
+// workgroup's THREADS threads form THREADS / 16 row groups of 16 lanes, GPB
+// row groups per column block, so that it owns THREADS / 16 / GPB adjacent
+// column blocks: row group gr of a block reads rows gr, gr + GPB,
+// gr + 2 GPB, ... of each of its chunks of GPB * RIF rows, each lane one
+// 16-byte vector per row, with RIF = kRowsInFlight * 256 / THREADS rows in
+// flight (32 KiB in flight per workgroup whatever its size).  The GPB
+// partial products of a block are combined in LDS in row-group order
+// (GPB = 1 stores straight from the lanes).  One block per workgroup (512
+// threads, GPB = 32, 4 rows in flight; a wave reading 256 bytes of four
+// rows) serves tiles of many rows; GPB = 4 and 1 (256 threads) give short,
+// wide tiles fewer and longer-lived workgroups, a wave reading 1 KiB of a
+// row.  Every layout walks the rows in chunks of 128.  (Measured on MI355X
+// for a 4096 x 16384 fp32 tile read from HBM: 40.6 us per call with 256
+// workgroups of one block and no second pass, against 44.1 us for
+// workgroups of 256 columns whose waves each read 1 KiB of a row, split
+// four ways over the rows and finished by a second kernel.  One block per
+// workgroup as 512 threads with 4 rows in flight against 256 threads with
+// 8, interleaved on one box: fp32 42.4 -> 41.3 us, int32 42.1 -> 41.3, bf16
+// 2048 x 32768 21.6 -> 21.2, fp16 21.6 -> 21.4; 1024 threads with 2 rows in
+// flight 42.3 / 42.3 / 22.1 / 22.3; 256 threads with 4 rows 44.5.)
 // The work of workgroup `wg` along the columns and `s` of S along the rows.
-// The rows are walked in chunks of GPB * kRowsInFlight (each row group's
-// rows in flight at once); with S > 1 workgroup s takes chunks s, s + S,
-// s + 2S, ... (grid-stride along the rows).
-template <class Tr, class Op, bool VEC, int GPB>
+// The rows are walked in chunks of GPB * RIF (each row group's rows in
+// flight at once); with S > 1 workgroup s takes chunks s, s + S, s + 2S, ...
+// (grid-stride along the rows).
+template <class Tr, class Op, bool VEC, int GPB, int THREADS = kBlock>
 __device__ __forceinline__ void colred_blocks(
     const typename Tr::T* __restrict__ src, uint64_t R, uint64_t C,
     uint64_t ld, typename Tr::T* __restrict__ dst,
@@ -240,10 +247,12 @@ __device__ __forceinline__ void colred_blocks(
     using T = typename Tr::T;
     using A = typename Tr::A;
     constexpr int V = Tr::V;
-    constexpr int kCols = kLanesPerRow * V;         // columns per block
-    constexpr int kGroups = kBlock / kLanesPerRow;  // row groups per workgroup
+    constexpr int kCols = kLanesPerRow * V;          // columns per block
+    constexpr int kGroups = THREADS / kLanesPerRow;  // row groups per workgroup
     constexpr int kBlocksPerWg = kGroups / GPB;
+    constexpr int RIF = kRowsInFlight * kBlock / THREADS; // rows in flight per lane
     static_assert(kGroups % GPB == 0, "row groups split evenly over blocks");
+    static_assert(RIF >= 1 && RIF * THREADS == kRowsInFlight * kBlock, "same bytes in flight");
 
     __shared__ A lds[GPB > 1 ? kGroups : 1][kCols];
 
@@ -252,7 +261,7 @@ __device__ __forceinline__ void colred_blocks(
     const uint32_t gr = g % GPB;                      // row group within the block
     const uint64_t cb = wg * kBlocksPerWg + g / GPB;
     const uint64_t jb = cb * kCols; // first column of the block
-    constexpr uint64_t kChunk = (uint64_t)GPB * kRowsInFlight;
+    constexpr uint64_t kChunk = (uint64_t)GPB * RIF;
     const uint64_t step = (uint64_t)S * kChunk;
     const bool full = VEC && jb + kCols <= C;
 
@@ -271,14 +280,14 @@ __device__ __forceinline__ void colred_blocks(
         // Lane q owns columns jb + qV .. jb + qV + V - 1: one 16-byte vector
         // per row.
         const T* __restrict__ col = src + jb + (uint64_t)q * V;
-        for (; r + (uint64_t)GPB * (kRowsInFlight - 1) < R; r += step) {
-            uint4 v[kRowsInFlight];
+        for (; r + (uint64_t)GPB * (RIF - 1) < R; r += step) {
+            uint4 v[RIF];
 #pragma unroll
-            for (int u = 0; u < kRowsInFlight; ++u)
+            for (int u = 0; u < RIF; ++u)
                 v[u] = load_stream(reinterpret_cast<const uint4*>(
                     col + (r + (uint64_t)u * GPB) * ld));
 #pragma unroll
-            for (int u = 0; u < kRowsInFlight; ++u) {
+            for (int u = 0; u < RIF; ++u) {
                 A a[V];
                 Tr::unpack(v[u], a);
 #pragma unroll
@@ -297,7 +306,7 @@ __device__ __forceinline__ void colred_blocks(
         // Rows not 16-byte aligned, or the ragged last column block:
         // element loads, lane q owning columns jb + q + 16k, so that each
         // load instruction of a row group reads 16 consecutive elements.
-        // kRowsInFlight rows are requested before any is folded; columns
+        // RIF rows are requested before any is folded; columns
         // at or past C reload column jb (always valid) and are not folded.
         const T* __restrict__ blk = src + jb;
         uint32_t off[V];
@@ -308,16 +317,16 @@ __device__ __forceinline__ void colred_blocks(
             ok[k] = jb + c < C;
             off[k] = ok[k] ? c : 0u;
         }
-        for (; r + (uint64_t)GPB * (kRowsInFlight - 1) < R; r += step) {
-            T v[kRowsInFlight][V];
+        for (; r + (uint64_t)GPB * (RIF - 1) < R; r += step) {
+            T v[RIF][V];
 #pragma unroll
-            for (int u = 0; u < kRowsInFlight; ++u)
+            for (int u = 0; u < RIF; ++u)
 #pragma unroll
                 for (int k = 0; k < V; ++k)
                     v[u][k] = blk[(r + (uint64_t)u * GPB) * ld + off[k]];
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int u = 0; u < kRowsInFlight; ++u)
+            for (int u = 0; u < RIF; ++u)
 #pragma unroll
                 for (int k = 0; k < V; ++k)
                     if (ok[k])
@@ -356,7 +365,7 @@ __device__ __forceinline__ void colred_blocks(
         }
         // Combine each block's row groups' partial rows in row-group order.
         __syncthreads();
-        for (uint32_t i = threadIdx.x; i < (uint32_t)(kBlocksPerWg * kCols); i += kBlock) {
+        for (uint32_t i = threadIdx.x; i < (uint32_t)(kBlocksPerWg * kCols); i += THREADS) {
             const uint32_t b = i / kCols;
             const uint32_t c = i % kCols;
             A p = lds[b * GPB][c];
@@ -402,15 +411,16 @@ __device__ __forceinline__ void column_workgroup(int xcd_contiguous, uint64_t& w
     s = f / nx;
 }
 
-template <class Tr, class Op, bool VEC, int GPB>
-__global__ __launch_bounds__(kBlock) void colred_kernel(
+template <class Tr, class Op, bool VEC, int GPB, int THREADS>
+__global__ __launch_bounds__(THREADS) void colred_kernel(
     const typename Tr::T* __restrict__ src, uint64_t R, uint64_t C,
     uint64_t ld, typename Tr::T* __restrict__ dst,
     typename Tr::A* __restrict__ partials, int accum, int xcd_contiguous)
 {
     uint64_t wg, s;
     column_workgroup(xcd_contiguous, wg, s);
-    colred_blocks<Tr, Op, VEC, GPB>(src, R, C, ld, dst, partials, accum, wg, s, gridDim.y);
+    colred_blocks<Tr, Op, VEC, GPB, THREADS>(src, R, C, ld, dst, partials, accum, wg, s,
+                                             gridDim.y);
 }
 
 // Short, wide tiles with so many column blocks that a workgroup can own a
@@ -711,18 +721,36 @@ hipError_t launch_typed(const void* src, size_t R, size_t C, size_t ld,
         else
             go(colred_wide_kernel<Tr, Op, 2>);
     } else {
+        // group_rows is counted in row groups of a 256-thread workgroup: 1
+        // or 4 run as such.  16 (one block per workgroup) runs as one block
+        // of 32 row groups on 512 threads, with the same 128-row chunks,
+        // when the workgroup walks its block's whole column (S = 1) or the
+        // rows are not 16-byte aligned (element loads); aligned rows shared
+        // by several workgroups keep 256 threads.  (Measured on MI355X,
+        // interleaved A/B, 256 threads -> 512: 4096 x 16384 fp32 41.5 ->
+        // 41.2 us, 4096 x 16383 fp32 50.6 -> 42.0, one element past
+        // alignment 51.0 -> 49.2, 2048 x 32767 bf16 27.7 -> 23.0; with the
+        // rows shared, 8192 x 8192 44.1 -> 43.2 and 16384 x 4096 45.6 ->
+        // 44.7 but 65536 x 1024 41.8 -> 43.8 and 257 blocks split 6 ways
+        // 44.0 -> 44.6.)
+        const bool wide_wg = plan.splits == 1 || !vec;
         const unsigned per_wg = kBlock / kLanesPerRow / plan.group_rows;
         const dim3 grid((plan.col_blocks + per_wg - 1) / per_wg, plan.splits);
         const int xcd = (((uintptr_t)src & 127u) != 0) || ((ld * sizeof(T)) % 128 != 0);
-        auto go = [&](auto kern) {
-            kern<<<grid, kBlock, 0, stream>>>(s, R, C, ld, d, part, accum, xcd);
+        auto go = [&](auto kern, unsigned threads) {
+            kern<<<grid, threads, 0, stream>>>(s, R, C, ld, d, part, accum, xcd);
         };
         if (plan.group_rows == 1)
-            vec ? go(colred_kernel<Tr, Op, true, 1>) : go(colred_kernel<Tr, Op, false, 1>);
+            vec ? go(colred_kernel<Tr, Op, true, 1, kBlock>, kBlock)
+                : go(colred_kernel<Tr, Op, false, 1, kBlock>, kBlock);
         else if (plan.group_rows == 4)
-            vec ? go(colred_kernel<Tr, Op, true, 4>) : go(colred_kernel<Tr, Op, false, 4>);
+            vec ? go(colred_kernel<Tr, Op, true, 4, kBlock>, kBlock)
+                : go(colred_kernel<Tr, Op, false, 4, kBlock>, kBlock);
+        else if (!wide_wg)
+            go(colred_kernel<Tr, Op, true, 16, kBlock>, kBlock);
         else
-            vec ? go(colred_kernel<Tr, Op, true, 16>) : go(colred_kernel<Tr, Op, false, 16>);
+            vec ? go(colred_kernel<Tr, Op, true, 32, 2 * kBlock>, 2 * kBlock)
+                : go(colred_kernel<Tr, Op, false, 32, 2 * kBlock>, 2 * kBlock);
     }
     if (plan.splits > 1)
         colred_finish_kernel<Tr, Op><<<plan.finish_blocks, kBlock, 0, stream>>>(

@@ -147,7 +147,7 @@ def test_fp32_subnormals_preserved(code):
 
 def test_streaming_loads_are_nontemporal_dwordx4(code):
     for pat in (r"reduce1d_stream_kernel<", r"reduce1d_summaxmin_stream_kernel",
-                r"rows_seg_kernel<", r"rows_split_kernel<", r"colred_kernel<.*, true, \d+>",
+                r"rows_seg_kernel<", r"rows_split_kernel<", r"colred_kernel<.*, true, \d+, \d+>",
                 r"colred_narrow_kernel<.*, true>", r"colred_wide_kernel<"):
         for name, txt in kernels(code, pat).items():
             assert re.search(r"global_load_dwordx4 .* nt\b", txt), name
