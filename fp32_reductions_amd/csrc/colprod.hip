@@ -254,7 +254,13 @@ __device__ __forceinline__ void colred_blocks(
     static_assert(kGroups % GPB == 0, "row groups split evenly over blocks");
     static_assert(RIF >= 1 && RIF * THREADS == kRowsInFlight * kBlock, "same bytes in flight");
 
-    __shared__ A lds[GPB > 1 ? kGroups : 1][kCols];
+    // Row g of the LDS combine holds row group g's partial products, column
+    // c of the block at index (c mod V) * 16 + c / V for 16-byte vector
+    // lanes and c for element lanes (lane q's k-th value at k * 16 + q
+    // either way), each row padded by 16: one store instruction of a wave
+    // (four row groups) then hits 64 distinct banks.
+    constexpr int kLdsRow = kCols + kLanesPerRow;
+    __shared__ A lds[GPB > 1 ? kGroups : 1][GPB > 1 ? kLdsRow : 1];
 
     const uint32_t g = threadIdx.x / kLanesPerRow;
     const uint32_t q = threadIdx.x % kLanesPerRow;
@@ -357,21 +363,18 @@ __device__ __forceinline__ void colred_blocks(
         }
     } else {
 #pragma unroll
-        for (int k = 0; k < V; ++k) {
-            if (full)
-                lds[g][q * V + k] = acc[k];
-            else
-                lds[g][q + kLanesPerRow * k] = acc[k];
-        }
+        for (int k = 0; k < V; ++k)
+            lds[g][k * kLanesPerRow + q] = acc[k];
         // Combine each block's row groups' partial rows in row-group order.
         __syncthreads();
         for (uint32_t i = threadIdx.x; i < (uint32_t)(kBlocksPerWg * kCols); i += THREADS) {
             const uint32_t b = i / kCols;
-            const uint32_t c = i % kCols;
-            A p = lds[b * GPB][c];
+            const uint32_t e = i % kCols; // LDS index: value e / 16 of lane e % 16
+            A p = lds[b * GPB][e];
 #pragma unroll
             for (int w = 1; w < GPB; ++w)
-                p = Op::apply(p, lds[b * GPB + w][c]);
+                p = Op::apply(p, lds[b * GPB + w][e]);
+            const uint32_t c = full ? (e % kLanesPerRow) * V + e / kLanesPerRow : e;
             const uint64_t j = (wg * kBlocksPerWg + b) * kCols + c;
             if (j < C) {
                 if (S == 1)
