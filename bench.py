@@ -585,7 +585,7 @@ def read_ceiling(torch, hev, stream_handle, x_dev, copies, steps, warmup, cus):
     vecs = [x_dev] + list(copies)
     n = x_dev.numel()
     grid = max(lib.calib_read_grid(v.data_ptr(), n, cus) for v in vecs)
-    sink = torch.zeros(grid * 256, dtype=torch.int32, device="cuda")
+    sink = torch.zeros(grid * 512, dtype=torch.int32, device="cuda")
     match = 0x5EED1E55  # a thread stores its XOR only if it equals this
 
     def launch(k):

@@ -36,7 +36,7 @@ struct AccXor {
 };
 
 template <bool REGIONAL>
-__global__ __launch_bounds__(kBlock) void read_sink_kernel(const float* __restrict__ x,
+__global__ __launch_bounds__(REGIONAL ? kBlock : kWideBlock) void read_sink_kernel(const float* __restrict__ x,
                                                            uint64_t n,
                                                            uint32_t* __restrict__ sink,
                                                            uint32_t match)
@@ -45,9 +45,9 @@ __global__ __launch_bounds__(kBlock) void read_sink_kernel(const float* __restri
     if constexpr (REGIONAL)
         stream_regions(x, n, acc);
     else
-        stream_chunk(x, n, blockIdx.x, gridDim.x, acc);
+        stream_chunk<kWideBlock, kWideUnroll>(x, n, blockIdx.x, gridDim.x, acc);
     if (acc.w == match)
-        sink[(uint64_t)blockIdx.x * kBlock + threadIdx.x] = acc.w;
+        sink[(uint64_t)blockIdx.x * blockDim.x + threadIdx.x] = acc.w;
 }
 
 } // namespace
@@ -56,10 +56,10 @@ __global__ __launch_bounds__(kBlock) void read_sink_kernel(const float* __restri
 // The stream kernel's grid for x[0, n).
 extern "C" int calib_read_grid(const float* x, size_t n, int cus)
 {
-    return (int)red::stream_shape(x, n, cus, red::kStreamWgPerCu).grid;
+    return (int)red::stream_shape(x, n, cus).grid;
 }
 
-// Streams x[0, n) once on `stream`.  sink must hold grid * 256 words, grid
+// Streams x[0, n) once on `stream`.  sink must hold grid * 512 words, grid
 // as returned by calib_read_grid.  Returns a hipError_t value.
 
 extern "C" int calib_read_f32(const float* x, size_t n, unsigned* sink,
@@ -67,11 +67,11 @@ extern "C" int calib_read_f32(const float* x, size_t n, unsigned* sink,
 {
     if (n == 0)
         return 0;
-    const red::StreamShape sh = red::stream_shape(x, n, cus, red::kStreamWgPerCu);
+    const red::StreamShape sh = red::stream_shape(x, n, cus);
     const hipStream_t s = static_cast<hipStream_t>(stream);
     if (sh.regional)
         red::read_sink_kernel<true><<<sh.grid, red::kBlock, 0, s>>>(x, n, sink, match);
     else
-        red::read_sink_kernel<false><<<sh.grid, red::kBlock, 0, s>>>(x, n, sink, match);
+        red::read_sink_kernel<false><<<sh.grid, red::kWideBlock, 0, s>>>(x, n, sink, match);
     return (int)hipGetLastError();
 }

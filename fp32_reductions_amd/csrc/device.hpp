@@ -173,33 +173,36 @@ __host__ __device__ inline uint64_t sweep_count(const float* x, uint64_t n)
     return ((n - head_count(x, n)) / 4 + kSweep - 1) / kSweep;
 }
 
-template <class AccT>
+// TH threads per workgroup with U loads in flight each cover one sweep
+// (TH * U == kSweep): 256 threads with 8 loads (the default) or 512 with 4.
+template <int TH = kBlock, int U = kStreamUnroll, class AccT>
 __device__ __forceinline__ void stream_chunk(const float* __restrict__ x,
                                              uint64_t n, uint64_t chunk,
                                              uint64_t chunks, AccT& acc)
 {
+    static_assert((uint64_t)TH * U == kSweep && U % 2 == 0, "one sweep per step, loads in pairs");
     const uint32_t head = head_count(x, n);
     const uint64_t nvec = (n - head) / 4;
     const float4* __restrict__ xv = reinterpret_cast<const float4*>(x + head);
     const uint64_t step = chunks * kSweep;
 
     uint64_t i = chunk * kSweep + threadIdx.x;
-    for (; i + (uint64_t)(kStreamUnroll - 1) * kBlock < nvec; i += step) {
-        float4 v[kStreamUnroll];
+    for (; i + (uint64_t)(U - 1) * TH < nvec; i += step) {
+        float4 v[U];
 #pragma unroll
-        for (int u = 0; u < kStreamUnroll; ++u)
-            v[u] = load_stream(xv + i + (uint64_t)u * kBlock);
+        for (int u = 0; u < U; ++u)
+            v[u] = load_stream(xv + i + (uint64_t)u * TH);
         // All loads of the sweep are issued before the first fold (left to
         // itself the scheduler interleaves max3 / min3 folds with the loads
         // and waits for the first load before issuing the rest).
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int u = 0; u < kStreamUnroll; u += 2)
+        for (int u = 0; u < U; u += 2)
             acc.fold2(v[u], v[u + 1]);
     }
     // The partial last sweep, if it is this workgroup's turn (otherwise i is
     // already past the end).
-    for (; i < nvec; i += kBlock)
+    for (; i < nvec; i += TH)
         acc.fold1(load_stream(xv + i));
     if (chunk == 0 && threadIdx.x == 0) {
         for (uint32_t k = 0; k < head; ++k)
@@ -271,22 +274,33 @@ __device__ __forceinline__ void stream_regions(const float* __restrict__ x,
     }
 }
 
-// Launch shape of a kernel that streams one vector: vectors of at least
-// kRegionalMinBytes on a device whose CU count is a multiple of kXcds run
-// one workgroup per CU region by region (stream_regions); shorter ones run
-// kStreamWgPerCu per CU, at most one per sweep, in plain grid-stride order
-// (stream_chunk).
+// Launch shape of a kernel that streams one vector, one workgroup per CU
+// at most: vectors of at least kRegionalMinBytes on a device whose CU count
+// is a multiple of kXcds run workgroups of kBlock threads with
+// kStreamUnroll loads in flight, region by region (stream_regions);
+// shorter ones run workgroups of kWideBlock threads with kWideUnroll loads
+// in flight, at most one per sweep, in plain grid-stride order
+// (stream_chunk<kWideBlock, kWideUnroll>).  Both keep 32 KiB in flight per
+// CU.  (Measured on MI355X with a read-only sink, µs per read, plain order
+// on 512-thread workgroups / plain order on two 256-thread workgroups per
+// CU / regions: 32 MiB 6.5 / 6.6 / 7.0, 64 MiB 11.0 / 11.2 / 11.4, 128 MiB
+// 20.2 / 20.8 / 21.0, 256 MiB 39.1 / 40.3 / 38.5, 1 GiB 151 / 155 / 146,
+// 4 GiB 596 / 604 / 580.)
 #ifndef RED_REGIONAL_MIN_BYTES
-#define RED_REGIONAL_MIN_BYTES (128ull << 20)
+#define RED_REGIONAL_MIN_BYTES (256ull << 20)
 #endif
 constexpr uint64_t kRegionalMinBytes = RED_REGIONAL_MIN_BYTES;
+constexpr int kWideBlock = 512;  // threads per workgroup of the plain 1-D stream
+constexpr int kWideUnroll = 4;   // its loads in flight per thread
+static_assert((uint64_t)kWideBlock * kWideUnroll == kSweep, "one sweep per step");
 
 struct StreamShape {
     unsigned grid = 1;
     bool regional = false;
+    unsigned threads() const { return regional ? (unsigned)kBlock : (unsigned)kWideBlock; }
 };
 
-inline StreamShape stream_shape(const float* x, uint64_t n, int cus, int wg_per_cu)
+inline StreamShape stream_shape(const float* x, uint64_t n, int cus)
 {
     StreamShape sh;
     const uint64_t sweeps = sweep_count(x, n);
@@ -296,10 +310,7 @@ inline StreamShape stream_shape(const float* x, uint64_t n, int cus, int wg_per_
         sh.regional = true;
         return sh;
     }
-    uint64_t g = sweeps;
-    const uint64_t cap = (uint64_t)cus * (uint64_t)wg_per_cu;
-    if (g > cap)
-        g = cap;
+    const uint64_t g = sweeps < (uint64_t)cus ? sweeps : (uint64_t)cus;
     sh.grid = (unsigned)(g < 1 ? 1 : g);
     return sh;
 }

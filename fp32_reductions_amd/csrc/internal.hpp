@@ -23,9 +23,10 @@ struct DeviceInfo {
     int cus = 0;                   // compute units
 };
 
-// Workgroups per compute unit for the 1-D streaming kernel and for the
-// column product (measured on MI355X: fewer, longer-lived workgroups stream
-// HBM faster than a full-occupancy grid).
+// Workgroups per compute unit that the split-row kernel aims at, and that
+// the column product plans for (measured on MI355X: fewer, longer-lived
+// workgroups stream HBM faster than a full-occupancy grid).  The 1-D
+// kernels take their launch shape from stream_shape (device.hpp).
 #ifndef RED_STREAM_WG_PER_CU
 #define RED_STREAM_WG_PER_CU 2
 #endif
@@ -33,8 +34,6 @@ struct DeviceInfo {
 #define RED_COLPROD_WG_PER_CU 1
 #endif
 constexpr int kStreamWgPerCu = RED_STREAM_WG_PER_CU;
-// Workgroups per compute unit for the single-pass atomic variant.
-constexpr int kAtomicWgPerCu = 1;
 constexpr int kColprodWgPerCu = RED_COLPROD_WG_PER_CU;
 // Row count from which the row kernels use one wave per row whatever n is.
 constexpr int kRowsWavePerCu = 8;

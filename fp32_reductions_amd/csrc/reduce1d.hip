@@ -1,10 +1,13 @@
 // reduce1d.hip -- 1-D fp32 vector -> scalar (sum / max / min, accum).
 //
-// Two workgroups per compute unit share the vector's 32 KiB sweeps in
-// grid-stride order; each thread streams its share with eight
-// non-temporal 16-byte (dwordx4) loads in flight into a per-thread
-// multi-wide accumulator, which collapses along a fixed tree; the wave
-// reduces with DPP and the workgroup through LDS.
+// One workgroup per compute unit streams the vector's 32 KiB sweeps with
+// non-temporal 16-byte (dwordx4) loads: under 256 MiB, 512-thread
+// workgroups with four loads in flight per thread take the sweeps in
+// grid-stride order over the whole vector; from 256 MiB, 256-thread
+// workgroups with eight take them region by region, one contiguous region
+// per XCD (stream_shape, device.hpp).  Each thread folds its loads into a
+// per-thread multi-wide accumulator, which collapses along a fixed tree;
+// the wave reduces with DPP and the workgroup through LDS.
 //
 // The cross-workgroup step takes one of three forms:
 //  * deterministic (default): every workgroup stores its partial; a second,
@@ -28,8 +31,12 @@
 namespace red {
 namespace {
 
-// The workgroup's share of x, in grid-stride order over the whole vector
-// or region by region (long vectors).
+// The workgroup's share of x: region by region on kBlock threads (long
+// vectors), else in grid-stride order over the whole vector on kWideBlock
+// threads (stream_shape decides).
+template <bool REGIONAL>
+constexpr int kStreamThreads = REGIONAL ? kBlock : kWideBlock;
+
 template <bool REGIONAL, class AccT>
 __device__ __forceinline__ void stream_share(const float* __restrict__ x, uint64_t n,
                                              AccT& acc)
@@ -37,7 +44,7 @@ __device__ __forceinline__ void stream_share(const float* __restrict__ x, uint64
     if constexpr (REGIONAL)
         stream_regions(x, n, acc);
     else
-        stream_chunk(x, n, blockIdx.x, gridDim.x, acc);
+        stream_chunk<kWideBlock, kWideUnroll>(x, n, blockIdx.x, gridDim.x, acc);
 }
 
 template <class Op, bool REGIONAL>
@@ -84,9 +91,10 @@ struct AccSumMaxMin {
 // is folded exactly as block_reduce folds it (DPP within the wave, then the
 // waves in order), so the results equal three block_reduce calls bit for
 // bit.  Only thread 0's results are meaningful.
+template <int WAVES>
 __device__ __forceinline__ void block_reduce_sum_max_min(float vs, float vx,
                                                          float vn,
-                                                         float (*lds)[kWaves],
+                                                         float (*lds)[WAVES],
                                                          float* r)
 {
     const float ws = wave_reduce<OpSum>(vs);
@@ -102,7 +110,7 @@ __device__ __forceinline__ void block_reduce_sum_max_min(float vs, float vx,
     r[1] = lds[1][0];
     r[2] = lds[2][0];
 #pragma unroll
-    for (int k = 1; k < kWaves; ++k) {
+    for (int k = 1; k < WAVES; ++k) {
         r[0] = OpSum::apply(r[0], lds[0][k]);
         r[1] = OpMax::apply(r[1], lds[1][k]);
         r[2] = OpMin::apply(r[2], lds[2][k]);
@@ -115,12 +123,13 @@ __device__ __forceinline__ void block_reduce_sum_max_min(float vs, float vx,
 // with the old value folded first under accum, exactly as the finish
 // kernel would, and no second kernel is launched.
 template <class Op, bool REGIONAL>
-__global__ __launch_bounds__(kBlock) void reduce1d_stream_kernel(
+__global__ __launch_bounds__(kStreamThreads<REGIONAL>) void reduce1d_stream_kernel(
     const float* __restrict__ x, uint64_t n, float* __restrict__ partials,
     float* __restrict__ out, int accum)
 {
-    __shared__ float lds[kWaves];
-    const float r = block_reduce<Op>(thread_part<Op, REGIONAL>(x, n), lds);
+    constexpr int kW = kStreamThreads<REGIONAL> / kWave;
+    __shared__ float lds[kW];
+    const float r = red_dev::block_reduce<Op, kW>(thread_part<Op, REGIONAL>(x, n), lds);
     if (threadIdx.x == 0) {
         if (gridDim.x == 1)
             *out = accum ? Op::apply(*out, r) : r;
@@ -151,16 +160,17 @@ __global__ __launch_bounds__(kBlock) void reduce1d_finish_kernel(
 // Fused first pass: partials[b], partials[G + b], partials[2G + b] receive
 // workgroup b's sum, max and min.
 template <bool REGIONAL>
-__global__ __launch_bounds__(kBlock) void reduce1d_summaxmin_stream_kernel(
+__global__ __launch_bounds__(kStreamThreads<REGIONAL>) void reduce1d_summaxmin_stream_kernel(
     const float* __restrict__ x, uint64_t n, float* __restrict__ partials,
     float* __restrict__ out, int accum)
 {
-    __shared__ float lds[3][kWaves];
+    constexpr int kW = kStreamThreads<REGIONAL> / kWave;
+    __shared__ float lds[3][kW];
     AccSumMaxMin acc;
     stream_share<REGIONAL>(x, n, acc);
     float r[3];
-    block_reduce_sum_max_min(acc.sum.collapse(), acc.max.collapse(),
-                             acc.min.collapse(), lds, r);
+    block_reduce_sum_max_min<kW>(acc.sum.collapse(), acc.max.collapse(),
+                                 acc.min.collapse(), lds, r);
     if (threadIdx.x == 0) {
         if (gridDim.x == 1) { // the whole call, as for the single operations
             out[0] = accum ? OpSum::apply(out[0], r[0]) : r[0];
@@ -192,7 +202,7 @@ __global__ __launch_bounds__(kBlock) void reduce1d_summaxmin_finish_kernel(
     const float vx = fold_loaded<OpMax>(first ? ox : OpMax::identity(), px, partials + G, G);
     const float vn = fold_loaded<OpMin>(first ? on : OpMin::identity(), pn, partials + 2 * G, G);
     float t[3];
-    block_reduce_sum_max_min(vs, vx, vn, lds, t);
+    block_reduce_sum_max_min<kWaves>(vs, vx, vn, lds, t);
     if (threadIdx.x == 0) {
         out[0] = t[0];
         out[1] = t[1];
@@ -253,11 +263,12 @@ __device__ void atomic_fold_extreme(float* out, float r)
 }
 
 template <class Op, bool REGIONAL>
-__global__ __launch_bounds__(kBlock) void reduce1d_atomic_kernel(
+__global__ __launch_bounds__(kStreamThreads<REGIONAL>) void reduce1d_atomic_kernel(
     const float* __restrict__ x, uint64_t n, float* __restrict__ out)
 {
-    __shared__ float lds[kWaves];
-    const float r = block_reduce<Op>(thread_part<Op, REGIONAL>(x, n), lds);
+    constexpr int kW = kStreamThreads<REGIONAL> / kWave;
+    __shared__ float lds[kW];
+    const float r = red_dev::block_reduce<Op, kW>(thread_part<Op, REGIONAL>(x, n), lds);
     if (threadIdx.x == 0) {
         if constexpr (__is_same(Op, OpSum))
             unsafeAtomicAdd(out, r); // hardware global_atomic_add_f32
@@ -283,7 +294,8 @@ hipError_t launch_det(const float* x, size_t n, float* out, int accum,
     if (sh.regional)
         reduce1d_stream_kernel<Op, true><<<grid, kBlock, 0, stream>>>(x, n, partials, out, accum);
     else
-        reduce1d_stream_kernel<Op, false><<<grid, kBlock, 0, stream>>>(x, n, partials, out, accum);
+        reduce1d_stream_kernel<Op, false><<<grid, kWideBlock, 0, stream>>>(x, n, partials, out,
+                                                                          accum);
     if (grid > 1)
         reduce1d_finish_kernel<Op><<<1, kBlock, 0, stream>>>(partials, grid, out, accum);
     return hipGetLastError();
@@ -303,7 +315,7 @@ hipError_t launch_atomic(const float* x, size_t n, float* out, int accum,
     if (sh.regional)
         reduce1d_atomic_kernel<Op, true><<<sh.grid, kBlock, 0, stream>>>(x, n, out);
     else
-        reduce1d_atomic_kernel<Op, false><<<sh.grid, kBlock, 0, stream>>>(x, n, out);
+        reduce1d_atomic_kernel<Op, false><<<sh.grid, kWideBlock, 0, stream>>>(x, n, out);
     return hipGetLastError();
 }
 
@@ -312,7 +324,7 @@ hipError_t launch_atomic(const float* x, size_t n, float* out, int accum,
 // Launch shape of the deterministic 1-D kernels for x[0, n).
 StreamShape reduce1d_shape(const float* x, size_t n, const DeviceInfo& dev)
 {
-    return stream_shape(x, n, dev.cus, kStreamWgPerCu);
+    return stream_shape(x, n, dev.cus);
 }
 
 hipError_t launch_reduce1d_summaxmin(const float* x, size_t n, float* out,
@@ -328,8 +340,8 @@ hipError_t launch_reduce1d_summaxmin(const float* x, size_t n, float* out,
         reduce1d_summaxmin_stream_kernel<true><<<grid, kBlock, 0, stream>>>(x, n, partials, out,
                                                                            accum);
     else
-        reduce1d_summaxmin_stream_kernel<false><<<grid, kBlock, 0, stream>>>(x, n, partials, out,
-                                                                            accum);
+        reduce1d_summaxmin_stream_kernel<false><<<grid, kWideBlock, 0, stream>>>(x, n, partials,
+                                                                                out, accum);
     if (grid > 1)
         reduce1d_summaxmin_finish_kernel<<<1, kBlock, 0, stream>>>(partials, grid, out, accum);
     return hipGetLastError();
@@ -359,13 +371,12 @@ hipError_t launch_reduce1d_atomic(OpKind op, const float* x, size_t n,
                                   float* out, int accum, const DeviceInfo& dev,
                                   hipStream_t stream)
 {
-    // One workgroup per CU rather than the stream kernel's two: the
-    // workgroups' atomics on the one destination serialize (~9 ns each), so
-    // halving them gains more than the narrower stream loses.  (Measured on
-    // MI355X, 64 MiB, median per call: sum with accum 16.7 -> 13.9 us,
-    // without 20.8 -> 18.2 us; max without accum 20.3 -> 18.1 us; max with
-    // accum, whose workgroups mostly skip their atomic, 11.8 -> 12.1 us.)
-    const StreamShape sh = stream_shape(x, n, dev.cus, kAtomicWgPerCu);
+    // The stream kernels' launch shape: one workgroup per CU at most, so
+    // at most one same-address atomic per CU (they serialize, ~9 ns each).
+    // (Measured on MI355X, 64 MiB, median per call, one 256-thread
+    // workgroup per CU against two: sum with accum 16.7 -> 13.9 us, without
+    // 20.8 -> 18.2 us; max without accum 20.3 -> 18.1 us.)
+    const StreamShape sh = stream_shape(x, n, dev.cus);
     switch (op) {
     case OpKind::Sum: return launch_atomic<OpSum>(x, n, out, accum, sh, stream);
     case OpKind::Max: return launch_atomic<OpMax>(x, n, out, accum, sh, stream);

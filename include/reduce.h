@@ -131,11 +131,11 @@ int red_sum_max_min_f32(const float* x, size_t n, float* out, int accum,
  * serving loops, harnesses that forbid hipMalloc): red_sum_max_min_f32
  * without any device or host allocation.  Same arguments, results (bit for
  * bit) and errors, and the same two kernels, but the per-workgroup partials
- * (12 bytes per workgroup of the first pass, at most 2 workgroups per
+ * (12 bytes per workgroup of the first pass, at most one workgroup per
  * compute unit) live in a 16 KiB static device buffer that the library
  * declares and that each GPU it runs on holds until the process ends.
  * Calls whose grid would need more than 16 KiB of partials (devices of
- * more than 682 compute units) return RED_ERR_SCRATCH and enqueue nothing.
+ * more than 1365 compute units) return RED_ERR_SCRATCH and enqueue nothing.
  * Nothing in the buffer has to start at zero: the first kernel writes
  * every partial the second reads.  Every call on one GPU shares that GPU's
  * buffer, whatever its stream or host thread: calls that overlap in time

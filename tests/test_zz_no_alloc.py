@@ -94,8 +94,9 @@ def test_noalloc_short_and_misaligned(lib):
 
 def test_noalloc_rejects_a_grid_beyond_the_scratch(lib, monkeypatch):
     """With the scratch limit lowered from the host to 1 KiB (room for the
-    partials of 85 workgroups), a 512-workgroup grid is refused and the
-    destination is left untouched; an 8-workgroup grid still runs."""
+    partials of 85 workgroups), a full grid (one workgroup per CU) is
+    refused and the destination is left untouched; an 8-workgroup grid
+    still runs."""
     say("noalloc scratch limit")
     monkeypatch.setenv("RED_TEST_SCRATCH_LIMIT", "1024")
     x = workloads.uniform_f32(603, 1 << 24)
