@@ -180,9 +180,9 @@ class Rotor:
         return len(self.copies)
 
 
-# The column kernel (16 row groups per 256-byte column block at these
-# shapes); a second kernel runs only when the plan splits the rows.
-COLRED = "colred_kernel<{0}, true, 16> (+ colred_finish_kernel<{0}> if rows are split)"
+# The column kernel (one 256-byte column block per 512-thread workgroup at
+# these shapes); a second kernel runs only when the plan splits the rows.
+COLRED = "colred_kernel<{0}, true, 32, 512> (+ colred_finish_kernel<{0}> if rows are split)"
 
 
 def up(torch, a):

@@ -226,9 +226,9 @@ __device__ __forceinline__ void stream_chunk(const float* __restrict__ x,
 // workgroup 0.  gridDim.x must be a multiple of kXcds.  (Measured on MI355X
 // with a read-only sink, 4 GiB: one workgroup per CU, 8 loads in flight,
 // regions 577 us = 7.44 TB/s; the same grid in plain grid-stride order 589
-// us; two workgroups per CU in grid-stride order 600 us.  1 GiB 145.5
-// against 153.6 us, 256 MiB 38.7 against 39.9 us; at 64 MiB plain order on
-// two workgroups per CU stays faster, 11.0 against 11.5 us.)
+// us; two workgroups per CU in grid-stride order 600 us; 16, 32 or 256
+// regions 582, 589, 598 us.  1 GiB 145.5 against 153.6 us, 256 MiB 38.7
+// against 39.9 us.  Shorter vectors run the plain walk: see stream_shape.)
 // ---------------------------------------------------------------------------
 constexpr uint32_t kXcds = 8;
 

@@ -153,7 +153,9 @@ int red_sum_max_min_f32_noalloc(const float* x, size_t n, float* out, int accum,
  * accum == 0 the library first sets *out to the identity (-0.0 for sum, a
  * quiet NaN for max / min) on `stream`.  sum uses the hardware fp32 atomic
  * add, so its rounding order -- and its last bits -- vary from run to run
- * (same error bound); max / min fold each workgroup's result with one
+ * (same error bound); on gfx950 that atomic keeps subnormal operands and
+ * results and the sign of zero, as the other entry points do (a zero sum
+ * is -0 only when every term is -0); max / min fold each workgroup's result with one
  * integer atomic max / min on the fp32 bit pattern and are exact (an old
  * NaN under accum is replaced first by compare-and-swap; equal zeros of
  * both signs give +0 for max and -0 for min).  No workspace is used. */
