@@ -21,7 +21,8 @@ microseconds per call, GB/s, the fraction of the 8 TB/s peak and, when a
 counter summary for that call and source is committed, its HBM traffic.
 ``read_ceiling`` gives the same figures for a read-only streaming kernel
 (the 1-D stream kernel with its reduction replaced by a trivial sink) over
-the 2^30 + 7 and the 2^24 vectors.
+the 2^30 + 7 and the 2^24 vectors, and over 128 MiB and 256 MiB, the byte
+counts of the 16-bit and the fp32 tiles.
 
 Cold cache: MI355X's 256 MB Infinity Cache would hold a 64 MiB vector
 between calls, so a small input exists as several identical copies in HBM
@@ -788,6 +789,16 @@ def main(argv=None) -> int:
         ceiling["vec16m"] = read_ceiling(torch, hev, sh, small, copies, ks, ws,
                                          props.multi_processor_count)
         del copies
+        # The sizes of the column and row tiles: 128 MiB (the 16-bit tiles)
+        # and 256 MiB (the fp32 tiles and the 65536 x 1000 rows), each read
+        # from disjoint slices of the long vector in turn so that no call
+        # finds its bytes in the 256 MB last-level cache.
+        for label, lg, nslices in (("128MiB", 25, 8), ("256MiB", 26, 4)):
+            m = 1 << lg
+            parts = [x_dev[k * m:(k + 1) * m] for k in range(nslices)]
+            log("read-only ceiling over %s (%d disjoint slices)" % (label, nslices))
+            ceiling[label] = read_ceiling(torch, hev, sh, parts[0], parts[1:], ks, ws,
+                                          props.multi_processor_count)
         line["read_ceiling"] = ceiling
         per_config = {}
         for name in PER_CONFIG:
