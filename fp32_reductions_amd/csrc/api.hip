@@ -343,9 +343,12 @@ int check_cols(ColType t, const void* src, size_t R, size_t C, size_t ld,
     if (!src || !dst || ld < C || !extent_ok(R, ld, C, es) ||
         C > SIZE_MAX / sizeof(float))
         return RED_ERR_INVALID;
-    // A launch holds at most 2^32 - 1 work-items per grid dimension: the
-    // column kernel's workgroups of 256 threads each cover 16 lanes x
-    // (16 / es) columns.
+    // A launch holds at most 2^32 - 1 work-items per grid dimension.  Each
+    // column workgroup covers at least one block of 16 lanes x (16 / es)
+    // columns on 256 threads; the 512-thread layout runs only when the
+    // blocks are too few to give every compute unit a workgroup of 4 row
+    // groups (fewer than 4 per CU).  So fewer than 2^24 blocks keep every
+    // grid under the limit.
     const size_t cols_per_wg = 16 * (16 / es);
     if ((C + cols_per_wg - 1) / cols_per_wg >= (size_t(1) << 24))
         return RED_ERR_INVALID;

@@ -12,8 +12,10 @@
 //    f32 / i32, 8 for f16 / bf16), so one 16-byte load per row feeds all of
 //    them; 16 lanes cover 256 contiguous bytes of a row and a wave reads
 //    four rows per load;
-//  * a workgroup (256 threads = 16 row groups of 16 lanes) covers one block
-//    of 16*V columns and its share of the rows; its row groups take
+//  * a workgroup covers one block of 16*V columns and its share of the
+//    rows: 512 threads (32 row groups of 16 lanes, 4 rows in flight per
+//    lane) when the rows are not split or not 16-byte aligned, else 256
+//    threads (16 row groups, 8 rows in flight); its row groups take
 //    interleaved rows and combine their partial products in LDS in
 //    row-group order.  Short, wide tiles, whose blocks alone would give
 //    thousands of short-lived workgroups, put 4 or 16 adjacent blocks in a

@@ -141,7 +141,9 @@ int red_sum_max_min_f32(const float* x, size_t n, float* out, int accum,
  * buffer, whatever its stream or host thread: calls that overlap in time
  * on one GPU race and give wrong results, so the caller must order them
  * (for example, issue them all on one stream).  The first call on a device
- * looks up the buffer's device address once (hipGetSymbolAddress). */
+ * looks up the buffer's device address once (hipGetSymbolAddress) and
+ * keeps it in a fixed table of 64 devices: on a device of index 64 or more
+ * the call returns RED_ERR_HIP and enqueues nothing. */
 int red_sum_max_min_f32_noalloc(const float* x, size_t n, float* out, int accum,
                                 red_stream_t stream);
 
