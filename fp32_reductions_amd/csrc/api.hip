@@ -82,26 +82,44 @@ bool extent_ok(size_t count, size_t stride, size_t width, size_t elem)
     return !__builtin_mul_overflow(span, elem, &span);
 }
 
-int current_device(int* dev, DeviceInfo* info)
+int device_info(int dev, DeviceInfo* info)
 {
-    if (hipGetDevice(dev) != hipSuccess || *dev < 0)
-        return RED_ERR_HIP;
-    const bool cached = *dev < kMaxDevices;
+    const bool cached = dev < kMaxDevices;
     if (cached) {
         std::lock_guard<std::mutex> lock(g_mu);
-        if (g_dev[*dev].cus > 0) {
-            *info = g_dev[*dev];
+        if (g_dev[dev].cus > 0) {
+            *info = g_dev[dev];
             return RED_OK;
         }
     }
     int cus = 0;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, *dev) !=
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) !=
             hipSuccess || cus <= 0)
         return RED_ERR_HIP;
     info->cus = cus;
     if (cached) {
         std::lock_guard<std::mutex> lock(g_mu);
-        g_dev[*dev] = *info;
+        g_dev[dev] = *info;
+    }
+    return RED_OK;
+}
+
+// The current device and the figures the launch plans use.  Test hook:
+// RED_TEST_CUS (a count from 1 to 65536), when set, replaces the compute-
+// unit count in every plan, so that tests run the planning of other device
+// sizes (a partitioned GPU, a smaller or larger part) on this one.
+int current_device(int* dev, DeviceInfo* info)
+{
+    if (hipGetDevice(dev) != hipSuccess || *dev < 0)
+        return RED_ERR_HIP;
+    const int st = device_info(*dev, info);
+    if (st != RED_OK)
+        return st;
+    const char* t = std::getenv("RED_TEST_CUS");
+    if (t && *t) {
+        const long v = std::strtol(t, nullptr, 10);
+        if (v >= 1 && v <= 65536)
+            info->cus = (int)v;
     }
     return RED_OK;
 }
