@@ -376,8 +376,14 @@ __device__ __forceinline__ void colred_blocks(
 #pragma unroll
             for (int w = 1; w < GPB; ++w)
                 p = Op::apply(p, lds[b * GPB + w][e]);
-            const uint32_t c = full ? (e % kLanesPerRow) * V + e / kLanesPerRow : e;
-            const uint64_t j = (wg * kBlocksPerWg + b) * kCols + c;
+            // Block b's own layout decides the column of index e: with several
+            // blocks per workgroup, the thread combining it need not be one of
+            // the block's readers, and a ragged last block is read in elements
+            // while its neighbours are read in vectors.
+            const uint64_t jb_b = (wg * kBlocksPerWg + b) * kCols;
+            const bool full_b = VEC && jb_b + kCols <= C;
+            const uint32_t c = full_b ? (e % kLanesPerRow) * V + e / kLanesPerRow : e;
+            const uint64_t j = jb_b + c;
             if (j < C) {
                 if (S == 1)
                     dst[j] = Tr::narrow(accum ? Op::apply(Tr::widen(dst[j]), p) : p);

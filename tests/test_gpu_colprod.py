@@ -256,6 +256,23 @@ def test_int_shapes(red, orc, kind, R, C, ld, off):
     assert bad.size == 0, "%s: column %d got %d want %d" % (kind, bad[0], got[bad[0]], want[bad[0]])
 
 
+# Short, wide 16-bit tiles of 4 row groups per block with a ragged last
+# block beside whole ones in the last workgroup (the 2-byte layout whose
+# combine places most values of a block from threads that read another).
+@pytest.mark.parametrize("kind", ["i16", "u16"])
+@pytest.mark.parametrize("R,C,ld", [(2, 236_272, 236_272), (5, 256_356, 256_360),
+                                    (1, 518_552, 518_552)])
+def test_int_wide_ragged(red, orc, kind, R, C, ld):
+    say("colprod int wide ragged %s R=%d C=%d ld=%d" % (kind, R, C, ld))
+    rng = np.random.default_rng(51)
+    src = (rng.integers(0, 1 << 16, (R, ld), dtype=np.uint64) | 1).astype(np.uint16)
+    src = src.view(INT_KINDS[kind][0])
+    got = run_int(red, kind, src, C)
+    want = want_int(orc, kind, src, C)
+    bad = np.nonzero(got != want)[0]
+    assert bad.size == 0, "%s: column %d got %d want %d" % (kind, bad[0], got[bad[0]], want[bad[0]])
+
+
 @pytest.mark.parametrize("kind,R,C", [("u32", 4096, 16384), ("i16", 2048, 32768),
                                       ("u16", 2048, 32768)])
 def test_int_large(red, orc, kind, R, C):

@@ -147,7 +147,8 @@ def factors(seed, shape):
 # blocks per workgroup, wide strips, unaligned rows, narrow rows.
 COLS = [("f32", 4096, 4096, 4096), ("f32", 64, 65536, 65536), ("f32", 1500, 1000, 1003),
         ("f32", 20_000, 12, 12), ("bf16", 2048, 2048, 2048), ("f16", 777, 3000, 3000),
-        ("i32", 1000, 1000, 1003), ("i32", 3000, 8192, 8192)]
+        ("i32", 1000, 1000, 1003), ("i32", 3000, 8192, 8192),
+        ("f16", 10, 1_187_589, 1_187_592), ("bf16", 3, 300_100, 300_104)]
 
 
 @pytest.mark.parametrize("kind,R,C,ld", COLS)

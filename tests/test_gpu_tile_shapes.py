@@ -248,16 +248,36 @@ def test_wide_4byte(red, orc, kind, R, C, ld):
     colprod_case(red, orc, kind, R, C, ld, 1000 + R)
 
 
-# 2-byte elements: 2041 or more blocks of 128 columns give 4 row groups
-# per block, 8161 or more give 1 (and the wide-strip kernel as above).
+# 2-byte elements: the same block counts, of 128 columns: 1021 or more
+# give 4 row groups per block, 4081 or more give 1, and 256 strips of
+# 32, 64 or 128 whole blocks (8 K, 16 K or 32 K blocks) the wide-strip
+# kernel.
 WIDE16 = [(20, 262_144, 262_144), (6, 270_000, 270_003), (4, 1_100_000, 1_100_008),
-          (11, 1_050_001, 1_050_001), (3, 4_200_005, 4_200_008), (2, 2_400_000, 2_400_000)]
+          (11, 1_050_001, 1_050_001), (3, 4_200_005, 4_200_008), (2, 2_400_000, 2_400_000),
+          (5, 600_000, 600_000)]
+
+# 4 row groups per block on 16-byte aligned rows with a ragged last block
+# (read in elements) in a workgroup whose other blocks are whole (read in
+# vectors).  A workgroup of 2-byte elements combines 4 x 128 values on 256
+# threads, so most of a block's values are combined by threads that read
+# another block; each must place them by that block's layout.  (Block
+# counts 1846, 4052, 2003, 1094, 3002: 2, 4, 3, 2 and 2 blocks in the last
+# workgroup.)
+WIDE16_RAGGED = [(2, 236_272, 236_272), (1, 518_552, 518_552), (7, 256_356, 256_360),
+                 (33, 140_000, 140_000), (3, 384_192, 384_192)]
 
 
 @pytest.mark.parametrize("R,C,ld", WIDE16)
 @pytest.mark.parametrize("kind", ["f16", "bf16"])
 def test_wide_2byte(red, orc, kind, R, C, ld):
     colprod_case(red, orc, kind, R, C, ld, 1100 + R)
+
+
+@pytest.mark.parametrize("R,C,ld", WIDE16_RAGGED)
+@pytest.mark.parametrize("kind", ["f16", "bf16"])
+@pytest.mark.parametrize("dst_off", [0, 2])
+def test_wide_2byte_ragged(red, orc, kind, R, C, ld, dst_off):
+    colprod_case(red, orc, kind, R, C, ld, 1150 + R, 0, dst_off)
 
 
 @pytest.mark.parametrize("R,C,ld", [(37, 65536, 65536), (7, 70001, 70002),
