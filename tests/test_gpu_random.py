@@ -205,6 +205,19 @@ def column_case(red, orc, rng, kind, R, C, ld, off, doff, what):
         out = torch.zeros(C + doff, dtype=torch.int32, device="cuda")[doff:]
         red.colprod_i32(_at(src, off), out, C=C)
         assert (host(out) == orc.colprod_i32(src, R, C, ld)).all(), what
+    elif kind in ("i16", "u16", "u32"):
+        # odd values: the products modulo 2^16 / 2^32 stay odd, so every row counts
+        w = 32 if kind == "u32" else 16
+        bits = (rng.integers(0, 1 << w, (R, ld), dtype=np.uint64) | 1).astype(
+            np.uint32 if w == 32 else np.uint16)
+        signed = np.int32 if w == 32 else np.int16
+        out = torch.zeros(C + doff, dtype=torch.int32 if w == 32 else torch.int16,
+                          device="cuda")[doff:]
+        getattr(red, "colprod_" + kind)(_at(bits.view(signed), off), out, C=C)
+        got = host(out).view(np.uint32 if w == 32 else np.uint16)
+        want = (orc.colprod_u32 if w == 32 else orc.colprod_u16)(bits, R, C, ld)
+        bad = np.nonzero(got != want)[0]
+        assert bad.size == 0, "%s: column %d" % (what, bad[0])
     elif kind in ("sum", "max", "min"):
         x = rng.uniform(-1, 1, (R, ld)).astype(np.float32)
         x[:, C:] = np.nan
@@ -291,3 +304,178 @@ def test_random_overrun_tiles(red, orc):
             case, kind, R, C, blocks, ld, off, doff)
         say(what)
         column_case(red, orc, rng, kind, R, C, ld, off, doff, what)
+
+
+def test_random_multiblock_tiles(red, orc):
+    """Short, wide tiles on 16-byte aligned rows whose workgroups hold
+    several column blocks (4 row groups each), a row group per block, or
+    wide strips, with a ragged last block for every element type: the
+    block counts are drawn from 1021 to 20000 (the 4-row-group layout
+    below 4081 at 256 CUs), so the last workgroup often holds whole blocks
+    beside the ragged one."""
+    rng = np.random.default_rng(9006)
+    kinds = ["f32", "i32", "bf16", "f16", "i16", "u16", "u32", "sum", "max", "min"]
+    for case in range(60):
+        kind = kinds[case % len(kinds)]
+        es = 2 if kind in ("bf16", "f16", "i16", "u16") else 4
+        cols = 256 // es
+        blocks = log_uniform(rng, 1021, 20000)
+        C = (blocks - 1) * cols + int(rng.integers(1, cols))      # ragged last block
+        vec = 16 // es
+        ld = -(-C // vec) * vec + vec * int(rng.integers(0, 2))    # rows on 16-byte boundaries
+        R = max(1, min(log_uniform(rng, 1, 24), 8_000_000 // ld))
+        off = vec * int(rng.integers(0, 2))
+        doff = int(rng.integers(0, 2)) * int(rng.integers(0, 3))
+        what = "multiblock case %d kind=%s R=%d C=%d (%d blocks) ld=%d off=%d doff=%d" % (
+            case, kind, R, C, blocks, ld, off, doff)
+        say(what)
+        column_case(red, orc, rng, kind, R, C, ld, off, doff, what)
+
+
+SPECIALS = np.array([0.0, -0.0, np.nan, np.inf, -np.inf, 2.0 ** -140, -(2.0 ** -140), 1e30, -1e30],
+                    np.float32)
+
+
+def _special_values(rng, shape, p):
+    """Uniform values with a fraction p replaced by NaN, infinities, zeros of
+    both signs, subnormals and large values; or zeros only, of random signs;
+    or -0 only with a few of those specials."""
+    kind = int(rng.integers(0, 3))
+    if kind == 1:
+        return np.where(rng.random(shape) < 0.5, np.float32(0.0), np.float32(-0.0)).astype(np.float32)
+    x = (np.full(shape, -0.0, np.float32) if kind == 2
+         else rng.uniform(-1, 1, shape).astype(np.float32))
+    m = rng.random(shape) < p
+    x[m] = SPECIALS[rng.integers(0, SPECIALS.size, int(m.sum()))]
+    return x
+
+
+def test_random_special_values(red, orc, monkeypatch):
+    """Special values through random shapes of the row and column
+    reductions, the column products and every 1-D entry point, under the
+    launch plans of random device sizes (RED_TEST_CUS from 1 to 4096, or
+    the device's own count), each checked strictly: NaN for NaN, the same
+    infinity, the sign of every zero (sums: -0 only when every term is -0;
+    products: the XOR of the factors' signs; max / min: either zero only
+    when both occur)."""
+    rng = np.random.default_rng(9007)
+    for case in range(90):
+        if rng.random() < 0.5:
+            monkeypatch.delenv("RED_TEST_CUS", raising=False)
+            cus = 0
+        else:
+            cus = log_uniform(rng, 1, 4096)
+            monkeypatch.setenv("RED_TEST_CUS", str(cus))
+        p = float(np.exp(rng.uniform(np.log(1e-5), np.log(0.05))))
+        part = case % 3
+        if part == 0:  # rows
+            op = ("sum", "max", "min")[(case // 3) % 3]
+            n = log_uniform(rng, 1, 5000)
+            ld = n + int(rng.integers(0, 2)) * int(rng.integers(0, 9))
+            rows = max(1, min(log_uniform(rng, 1, 200_000), 4_000_000 // ld))
+            off = int(rng.integers(0, 4))
+            accum = bool(rng.integers(0, 2))
+            x = np.full((rows, ld), np.nan, np.float32)
+            x[:, :n] = _special_values(rng, (rows, n), p)
+            old = _special_values(rng, rows, 0.2)
+            what = "special rows case %d %s rows=%d n=%d ld=%d off=%d accum=%d p=%.1e cus=%d" % (
+                case, op, rows, n, ld, off, accum, p, cus)
+            say(what)
+            out = dev(old.copy())
+            getattr(red, op + "_rows_f32")(upload_padded(x, off), out, n=n, accum=accum)
+            got = host(out)
+            if op == "sum":
+                s, a = orc.rows_sum_f32(x, rows, n, ld, accum, old)
+                check_sums(got, s, a, what)
+            else:
+                want = getattr(orc, "rows_%s_f32" % op)(x, rows, n, ld, accum, old)
+                both = has_both_zeros(valid_region(x, rows, n, ld), old, accum, axis=1)
+                check_extremes(got, want, both, what)
+        elif part == 1:  # columns
+            kind = ("f32", "bf16", "f16", "sum", "max", "min")[(case // 3) % 6]
+            C = log_uniform(rng, 1, 300_000)
+            ld = C + int(rng.integers(0, 2)) * int(rng.integers(0, 9))
+            R = max(1, min(log_uniform(rng, 1, 4000), 4_000_000 // ld))
+            off = int(rng.integers(0, 2)) * int(rng.integers(0, 4))
+            what = "special cols case %d %s R=%d C=%d ld=%d off=%d p=%.1e cus=%d" % (
+                case, kind, R, C, ld, off, p, cus)
+            say(what)
+            if kind in ("sum", "max", "min"):
+                x = _special_values(rng, (R, ld), p)
+                accum = bool(rng.integers(0, 2))
+                old = _special_values(rng, C, 0.2)
+                out = dev(old.copy())
+                getattr(red, kind + "_cols_f32")(_at(x, off), out, C=C, accum=accum)
+                got = host(out)
+                if kind == "sum":
+                    s, a = orc.cols_sum_f32(x, R, C, ld, accum, old)
+                    check_sums(got, s, a, what)
+                else:
+                    want = getattr(orc, "cols_%s_f32" % kind)(x, R, C, ld, accum, old)
+                    both = has_both_zeros(valid_region(x, R, C, ld), old, accum, axis=0)
+                    check_extremes(got, want, both, what)
+            else:
+                # +-1 with rare +-2 / +-0.5, and +-0, NaN, +-inf: every order
+                # gives the same product, bit for bit
+                u = rng.random((R, ld))
+                x = np.where(u < 2e-4, 2.0, np.where(u < 4e-4, 0.5, 1.0))
+                x = (x * np.where(rng.random((R, ld)) < 0.5, -1.0, 1.0)).astype(np.float32)
+                m = rng.random((R, ld)) < p
+                sp = np.array([0.0, -0.0, np.nan, np.inf, -np.inf], np.float32)
+                x[m] = sp[rng.integers(0, sp.size, int(m.sum()))]
+                if kind == "f32":
+                    out = torch.zeros(C, dtype=torch.float32, device="cuda")
+                    red.colprod_f32(_at(x, off), out, C=C)
+                    got, want = host(out), orc.colprod_f32(x, R, C, ld)
+                else:
+                    tdt = torch.bfloat16 if kind == "bf16" else torch.float16
+                    bits = torch.from_numpy(x).to(tdt).view(torch.int16).numpy().view(np.uint16)
+                    out = torch.zeros(C, dtype=tdt, device="cuda")
+                    getattr(red, "colprod_" + kind)(_at(bits.view(np.int16), off).view(tdt), out, C=C)
+                    got = host(out.float())
+                    want = np.asarray(getattr(orc, "colprod_" + kind)(bits, R, C, ld), np.float32)
+                g, w = np.asarray(got, np.float32), np.asarray(want, np.float32)
+                same = (g.view(np.uint32) == w.view(np.uint32)) | (np.isnan(g) & np.isnan(w))
+                assert same.all(), "%s: column %d got %r want %r" % (
+                    what, int(np.nonzero(~same)[0][0]), g[~same][0], w[~same][0])
+        else:  # 1-D
+            n = log_uniform(rng, 1, 4_000_000)
+            off = int(rng.integers(0, 4))
+            accum = bool(rng.integers(0, 2))
+            x = _special_values(rng, n, p)
+            old = np.float32(SPECIALS[rng.integers(0, SPECIALS.size)] if rng.random() < 0.3
+                             else rng.uniform(-3, 3))
+            what = "special 1-D case %d n=%d off=%d accum=%d p=%.1e old=%r cus=%d" % (
+                case, n, off, accum, p, float(old), cus)
+            say(what)
+            xd = upload_padded(x.reshape(1, n), off).view(n)
+            s, a = orc.sum_f32(x, accum, float(old))
+            both = bool(has_both_zeros(x, np.array([old]), accum))
+            res = {}
+            for op in ("sum", "max", "min"):
+                out = dev(np.array([old], np.float32))
+                getattr(red, op + "_f32")(xd, out, accum=accum)
+                res[op] = host(out)[0]
+            check_sum(res["sum"], s, a, what + " sum")
+            check_exact(res["max"], orc.max_f32(x, accum, float(old)), what + " max", both)
+            check_exact(res["min"], orc.min_f32(x, accum, float(old)), what + " min", both)
+            want3 = np.array([res["sum"], res["max"], res["min"]], np.float32)
+            for fn in ("sum_max_min_f32", "sum_max_min_f32_noalloc"):
+                out3 = dev(np.array([old, old, old], np.float32))
+                try:
+                    getattr(red, fn)(xd, out3, accum=accum)
+                except red.ReduceError as e:  # partials past the static buffer
+                    assert fn.endswith("noalloc") and e.status == red.RED_ERR_SCRATCH and cus > 1365, what
+                    continue
+                g = host(out3)
+                same = (g.view(np.uint32) == want3.view(np.uint32)) | (np.isnan(g) & np.isnan(want3))
+                assert same.all(), (what, fn, g, want3)
+            for op in ("sum", "max", "min"):
+                out = dev(np.array([old], np.float32))
+                getattr(red, op + "_f32_atomic")(xd, out, accum=accum)
+                got = host(out)[0]
+                if op == "sum":
+                    check_sum(got, s, a, what + " atomic sum")
+                else:
+                    check_exact(got, getattr(orc, op + "_f32")(x, accum, float(old)),
+                                what + " atomic " + op, both)
