@@ -22,7 +22,9 @@ counter summary for that call and source is committed, its HBM traffic.
 ``read_ceiling`` gives the same figures for a read-only streaming kernel
 (the 1-D stream kernel with its reduction replaced by a trivial sink) over
 the 2^30 + 7 and the 2^24 vectors, and over 128 MiB and 256 MiB, the byte
-counts of the 16-bit and the fp32 tiles.
+counts of the 16-bit and the fp32 tiles.  A call whose byte count is within
+3 % of a ceiling's also reports its rate over that ceiling
+(``of_read_ceiling``).
 
 Cold cache: MI355X's 256 MB Infinity Cache would hold a 64 MiB vector
 between calls, so a small input exists as several identical copies in HBM
@@ -558,6 +560,22 @@ def call_entry(call, durs, traffic=None):
     return entry
 
 
+def against_ceiling(entry, ceiling, within=0.03):
+    """Add to a per-call entry its rate over the read-only ceiling measured
+    on the same byte count (to within `within`), when there is one: how
+    close the call comes to a plain read of its bytes with the same launch
+    style."""
+    best = None
+    for label, c in ceiling.items():
+        rel = abs(c["bytes"] - entry["bytes"]) / entry["bytes"]
+        if rel <= within and (best is None or rel < best[0]):
+            best = (rel, label, c)
+    if best is not None:
+        entry["read_ceiling"] = best[1]
+        entry["of_read_ceiling"] = round(entry["gbs_mean"] / best[2]["gbs_mean"], 4)
+    return entry
+
+
 def measure_workload(torch, red, orc, name, steps, warmup, hev, stream_handle):
     """Per-call event timings of one workload (for per_config)."""
     wl = WORKLOADS[name](torch, red, orc, steps + warmup)
@@ -805,6 +823,11 @@ def main(argv=None) -> int:
             log("per_config: %s" % name)
             per_config[name] = measure_workload(torch, red, orc, name, ks, ws, hev, sh)
             torch.cuda.empty_cache()
+        for entry in per_call.values():
+            against_ceiling(entry, ceiling)
+        for cfg in per_config.values():
+            for entry in cfg["calls"].values():
+                against_ceiling(entry, ceiling)
         line["per_config"] = per_config
 
     if args.cpu_seconds > 0:

@@ -102,3 +102,15 @@ def test_cpu_baseline_reports_threads_and_single_core():
     b = bench.cpu_baseline(wl, 0.05)
     assert b["kind"] == "oracle" and b["value"] > 0
     assert b["single_core"] is None or (b["single_core"]["cores"] == 1 and b["cores"] >= 2)
+
+
+def test_against_ceiling_picks_the_same_byte_count():
+    ceiling = {"big": {"bytes": 4 << 30, "gbs_mean": 7400.0},
+               "128MiB": {"bytes": 128 << 20, "gbs_mean": 6700.0},
+               "256MiB": {"bytes": 256 << 20, "gbs_mean": 6900.0}}
+    e = bench.against_ceiling({"bytes": 134283264, "gbs_mean": 6300.0}, ceiling)
+    assert e["read_ceiling"] == "128MiB" and abs(e["of_read_ceiling"] - 6300 / 6700) < 1e-4
+    e = bench.against_ceiling({"bytes": 262406144, "gbs_mean": 6660.0}, ceiling)
+    assert e["read_ceiling"] == "256MiB"
+    e = bench.against_ceiling({"bytes": 540672, "gbs_mean": 100.0}, ceiling)
+    assert "read_ceiling" not in e and "of_read_ceiling" not in e
