@@ -4,7 +4,9 @@ kernels and grid, partials in the static scratch instead of a workspace)
 and match the oracle, on two calls in a row, the second with a smaller
 input, and with accum; a grid that would need more scratch than the
 buffer holds is refused (forced from the host with the library's
-RED_TEST_SCRATCH_LIMIT hook), with nothing enqueued."""
+RED_TEST_SCRATCH_LIMIT hook), with nothing enqueued; and calls captured
+into a HIP graph on a stream without a workspace replay to the eager
+results."""
 import ctypes
 import os
 
@@ -109,3 +111,48 @@ def test_noalloc_rejects_a_grid_beyond_the_scratch(lib, monkeypatch):
     small = xd[: 8 * 2048 * 4]            # 8 sweeps of 32 KiB: 8 workgroups
     got = call(lib, "red_sum_max_min_f32_noalloc", small, (0.0, 0.0, 0.0), False)
     check_oracle(x[: 8 * 2048 * 4], got, False, (0.0, 0.0, 0.0), "noalloc under the limit")
+
+
+def test_noalloc_graph_replay(lib):
+    """The use the entry point exists for: two calls captured into a HIP
+    graph on a stream that has never made a library call (they need no
+    workspace), the second smaller and with accum, after one eager call on
+    the device (which looks up the scratch address), then replayed four
+    times with new inputs copied in between and an eager fused call on
+    another stream in between; every replay equals the eager fused call
+    bit for bit."""
+    say("noalloc graph capture and 4 replays")
+    n1, n2 = (1 << 22) + 5, 100003
+    x1 = torch.empty(n1, dtype=torch.float32, device="cuda")
+    x2 = torch.empty(n2, dtype=torch.float32, device="cuda")
+    o1 = torch.zeros(3, dtype=torch.float32, device="cuda")
+    o2 = torch.zeros(3, dtype=torch.float32, device="cuda")
+    old2 = (1.0, -5.0, 5.0)
+    call(lib, "red_sum_max_min_f32_noalloc", x2[:8], (0.0, 0.0, 0.0), False)  # set-up
+    cap = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g, stream=cap):
+        h = torch.cuda.current_stream().cuda_stream
+        rc1 = lib.red_sum_max_min_f32_noalloc(x1.data_ptr(), n1, o1.data_ptr(), 0, h)
+        rc2 = lib.red_sum_max_min_f32_noalloc(x2.data_ptr(), n2, o2.data_ptr(), 1, h)
+    assert rc1 == RED_OK and rc2 == RED_OK, (rc1, rc2)
+    torch.cuda.synchronize()
+    eager_stream = torch.cuda.Stream()
+    for rep in range(4):
+        a = workloads.uniform_f32(610 + rep, n1, -2.0, 2.0)
+        b = workloads.uniform_f32(620 + rep, n2, -2.0, 2.0)
+        x1.copy_(torch.from_numpy(a))
+        x2.copy_(torch.from_numpy(b))
+        o2.copy_(torch.tensor(old2, dtype=torch.float32))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        with torch.cuda.stream(eager_stream):
+            w1 = call(lib, "red_sum_max_min_f32", x1, (0.0, 0.0, 0.0), False)
+            w2 = call(lib, "red_sum_max_min_f32", x2, old2, True)
+        g1, g2 = host(o1), host(o2)
+        assert g1.tobytes() == w1.tobytes(), ("replay", rep, g1, w1)
+        assert g2.tobytes() == w2.tobytes(), ("replay", rep, g2, w2)
+        check_oracle(a, g1, False, (0.0, 0.0, 0.0), "noalloc graph replay %d" % rep)
+        check_oracle(b, g2, True, old2, "noalloc graph replay %d accum" % rep)
