@@ -1,7 +1,8 @@
 """Benchmark of libreduce on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                    [--cpu-seconds S] [--no-configs]
+                    [--variant twopass|fused|atomic] [--cpu-seconds S]
+                    [--no-configs]
 
 Prints ONE JSON line on stdout.  A step is one pass of the workload's calls
 over its input.  The default workload is ``vec1g``: one fp32 vector of
@@ -48,9 +49,11 @@ point only.
 
 Other workloads (--workload): vec16m, vec16m_fused (sum / max / min from
 one read per call), vec16m_atomic (the vec16m step through the single-pass
-atomic variant), colprod4k, rows1000, rows32, colprod_int (int16 and
-uint32 column products), cols4k (column sum / max / min of a
-4096 x 16384 tile), copycal (a plain device copy, for counter calibration).
+atomic variant), vec1g_fused and vec1g_atomic (the same for the 2^30 + 7
+vector), colprod4k, rows1000, rows32, colprod_int (int16 and uint32 column
+products), cols4k (column sum / max / min of a 4096 x 16384 tile), copycal
+(a plain device copy, for counter calibration).  --variant fused / atomic
+selects the <workload>_fused / <workload>_atomic form of vec1g or vec16m.
 """
 from __future__ import annotations
 
@@ -324,6 +327,53 @@ def wl_vec1g(torch, red, orc, steps):
         calls, ["sum"], SOURCES_1D, cpu, device_inputs=[xd])
 
 
+def wl_vec1g_fused(torch, red, orc, steps):
+    """The vec1g step as one fused call: sum, max and min from one read."""
+    log("generating 2^30+7 vector")
+    x = workloads.vec1g()
+    n = x.size
+    xd = up(torch, x)
+    outs = torch.zeros((steps, 3), dtype=torch.float32, device="cuda")
+    kern = "reduce1d_summaxmin_stream_kernel<true> + reduce1d_summaxmin_finish_kernel"
+    calls = [Call("sum_max_min", kern, 4 * n + 12,
+                  lambda k: red.plan("sum_max_min_f32", xd, outs[k]))]
+
+    def oracle_all(t=None):
+        if t is None:
+            return orc.sum_f32(x), orc.max_f32(x), orc.min_f32(x)
+        return orc.sum_f32_mt(x, t), orc.max_f32_mt(x, t), orc.min_f32_mt(x, t)
+    cpu = [(4 * n + 12, lambda: oracle_all(), lambda t: oracle_all(t))]
+    return Workload(
+        "vec1g_fused",
+        "one fp32 vector of 2^30+7 elements, normal(0,1) with 1% of entries "
+        "scaled by 1e6, seed 3; sum, max and min from one read (fused call)",
+        {"n": n, "calls_per_step": 1, "cold_copies": 1},
+        calls, ["sum_max_min"], SOURCES_1D, cpu, device_inputs=[xd])
+
+
+def wl_vec1g_atomic(torch, red, orc, steps):
+    """The vec1g step through the single-pass atomic variant."""
+    log("generating 2^30+7 vector")
+    x = workloads.vec1g()
+    n = x.size
+    xd = up(torch, x)
+    outs = torch.zeros((steps, 3), dtype=torch.float32, device="cuda")
+    calls = []
+    for j, op in enumerate(("sum", "max", "min")):
+        kern = "fill_u32_kernel + reduce1d_atomic_kernel<Op{0}, true>".format(op.capitalize())
+        calls.append(Call(op, kern, 4 * n + 4,
+                          lambda k, op=op, j=j: red.plan(op + "_f32_atomic", xd,
+                                                         outs[k, j:j + 1])))
+    cpu = vector_cpu(orc, x, (False,))
+    return Workload(
+        "vec1g_atomic",
+        "one fp32 vector of 2^30+7 elements, normal(0,1) with 1% of entries "
+        "scaled by 1e6, seed 3; sum, max, min, each as one pass with one "
+        "device-scope atomic per workgroup",
+        {"n": n, "calls_per_step": 3, "cold_copies": 1},
+        calls, ["sum"], SOURCES_1D, cpu, device_inputs=[xd])
+
+
 def wl_colprod4k(torch, red, orc, steps):
     log("generating 4096 x 16384 f32 / i32 tiles")
     f, i = workloads.colprod4k_f32_i32()
@@ -475,7 +525,8 @@ def wl_copycal(torch, red, orc, steps):
                     calls, ["copy"], [], [])
 
 
-WORKLOADS = {"vec16m": wl_vec16m, "vec16m_fused": wl_vec16m_fused, "vec16m_atomic": wl_vec16m_atomic, "vec1g": wl_vec1g, "colprod4k": wl_colprod4k,
+WORKLOADS = {"vec16m": wl_vec16m, "vec16m_fused": wl_vec16m_fused, "vec16m_atomic": wl_vec16m_atomic, "vec1g": wl_vec1g,
+             "vec1g_fused": wl_vec1g_fused, "vec1g_atomic": wl_vec1g_atomic, "colprod4k": wl_colprod4k,
              "rows1000": wl_rows1000, "colprod_int": wl_colprod_int, "cols4k": wl_cols4k, "rows32": wl_rows32, "copycal": wl_copycal}
 
 
@@ -701,7 +752,20 @@ def main(argv=None) -> int:
                     help="time budget of each CPU-oracle baseline (0: skip)")
     ap.add_argument("--no-configs", action="store_true",
                     help="skip the per_config and read_ceiling blocks")
+    ap.add_argument("--variant", default="twopass", choices=["twopass", "fused", "atomic"],
+                    help="the 1-D calls of the workload: the deterministic two-kernel "
+                         "calls (default), the fused sum+max+min call, or the single-pass "
+                         "atomic variant")
     args = ap.parse_args(argv)
+    name = args.workload
+    if args.variant != "twopass":
+        name = "%s_%s" % (args.workload, args.variant)
+        if name not in WORKLOADS:
+            print("workload %s has no %s variant (variants exist for: %s)" % (
+                args.workload, args.variant,
+                ", ".join(sorted(w.rsplit("_", 1)[0] for w in WORKLOADS
+                                 if w.endswith("_" + args.variant)))), file=sys.stderr)
+            return 2
 
     if args.gpus != 1:
         print("bench.py measures one GPU only: multi-GPU runs are not part of "
@@ -717,7 +781,7 @@ def main(argv=None) -> int:
     torch.cuda.set_device(0)
     props = torch.cuda.get_device_properties(0)
     K, W = args.steps, args.warmup
-    wl = WORKLOADS[args.workload](torch, red, orc, K + W)
+    wl = WORKLOADS[name](torch, red, orc, K + W)
     stream = torch.cuda.current_stream()
 
     log("workload %s: %d calls/step, warmup %d, steps %d" % (wl.name, len(wl.calls), W, K))
@@ -794,7 +858,7 @@ def main(argv=None) -> int:
     }
     del plans
 
-    if args.workload == "vec1g" and not args.no_configs:
+    if name == "vec1g" and not args.no_configs:
         ks, ws = min(K, 30), min(W, 5)
         x_dev = wl.device_inputs[0]
         log("read-only ceiling over the 2^30 + 7 vector")

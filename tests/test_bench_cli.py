@@ -114,3 +114,17 @@ def test_against_ceiling_picks_the_same_byte_count():
     assert e["read_ceiling"] == "256MiB"
     e = bench.against_ceiling({"bytes": 540672, "gbs_mean": 100.0}, ceiling)
     assert "read_ceiling" not in e and "of_read_ceiling" not in e
+
+
+def test_variant_without_a_workload_is_refused():
+    proc = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--workload", "rows32",
+                           "--variant", "atomic"], capture_output=True, text=True, timeout=120)
+    assert proc.returncode == 2
+    assert "no atomic variant" in proc.stderr and "vec1g" in proc.stderr
+    assert proc.stdout == ""
+
+
+def test_every_variant_names_a_workload():
+    for base in ("vec1g", "vec16m"):
+        for v in ("fused", "atomic"):
+            assert "%s_%s" % (base, v) in bench.WORKLOADS
