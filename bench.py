@@ -854,7 +854,10 @@ def main(argv=None) -> int:
                      "traffic": traffic,
                      "bytes_per_launch": dom_bytes, "mean_launch_us": round(dom_us, 3)},
         "per_call": per_call,
-        "device": {"name": props.name, "cus": props.multi_processor_count},
+        "device": {"name": props.name, "cus": props.multi_processor_count,
+                   "arch": getattr(props, "gcnArchName", None),
+                   "hbm_gib": round(props.total_memory / 2**30, 1),
+                   "hip": getattr(torch.version, "hip", None), "torch": torch.__version__},
     }
     del plans
 
