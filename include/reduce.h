@@ -67,9 +67,9 @@
  *     on the capture stream does this), and must end before that stream's
  *     workspace is released.
  *   - Thread safety: any host thread may call any entry point.
- *   - Test hooks, read from the environment at every call and meant to be
- *     left unset outside tests: RED_TEST_FAIL_ALLOC=1 makes a workspace
- *     allocation fail (RED_ERR_NOMEM); RED_TEST_SCRATCH_LIMIT=<bytes>
+ *   - Test hooks, read from the environment and meant to be left unset
+ *     outside tests: RED_TEST_FAIL_ALLOC=1 makes the creation of a workspace
+ *     fail (RED_ERR_NOMEM); RED_TEST_SCRATCH_LIMIT=<bytes>
  *     lowers the static scratch limit of red_sum_max_min_f32_noalloc;
  *     RED_TEST_CUS=<1..65536> replaces the compute-unit count the launch
  *     plans start from (results then stay correct but may differ in their
