@@ -282,8 +282,9 @@ __device__ __forceinline__ void colred_blocks(
     // one: its remaining rows are read one at a time.
     uint64_t r = s * kChunk + gr;
     if (jb >= C) {
-        // A block past the last column (the workgroup's last blocks when
-        // 16 / GPB does not divide the block count): nothing to read.
+        // A block past the last column (the last workgroup's last blocks
+        // when its kBlocksPerWg blocks do not divide the block count):
+        // nothing to read; its row groups combine the identity.
     } else if (full) {
         // Lane q owns columns jb + qV .. jb + qV + V - 1: one 16-byte vector
         // per row.
