@@ -274,8 +274,62 @@ __device__ __forceinline__ void stream_regions(const float* __restrict__ x,
     }
 }
 
+// ---------------------------------------------------------------------------
+// Short vectors in one workgroup, every load in flight at once.
+//
+// Up to kShortVecs whole 16-byte vectors (128 KiB): thread t loads vectors
+// t, t + kShortBlock, ..., t + (kShortUnroll - 1) kShortBlock, all requested
+// before the first fold (indices past the end load the last vector again and
+// are not folded, which keeps the loads unconditional), then folds its valid
+// ones in pairs in that order.  The scalars before the first 16-byte
+// boundary and after the last whole vector go to thread 0.  One CU streams
+// 128 KiB within the launch latency of a one-kernel call, so such a vector
+// costs no more than a 32 KiB one and needs no second kernel.  (Measured on
+// MI355X, one workgroup of 1024 threads against the two-kernel call, event
+// per call, cold copies: 64 KiB 4.44 against 6.26 us, 128 KiB 4.40 against
+// 6.28 us; 256 KiB took 6.5 us and 512 KiB 10.8 us in one workgroup, so
+// longer vectors keep the grid.)
+// ---------------------------------------------------------------------------
+constexpr int kShortBlock = 1024;
+constexpr int kShortUnroll = 8;
+constexpr uint64_t kShortVecs = (uint64_t)kShortBlock * kShortUnroll;
+
+template <class AccT>
+__device__ __forceinline__ void stream_short(const float* __restrict__ x, uint64_t n,
+                                             AccT& acc)
+{
+    const uint32_t head = head_count(x, n);
+    const uint32_t nvec = (uint32_t)((n - head) / 4); // at most kShortVecs
+    const float4* __restrict__ xv = reinterpret_cast<const float4*>(x + head);
+    if (nvec > 0) {
+        float4 v[kShortUnroll];
+#pragma unroll
+        for (int u = 0; u < kShortUnroll; ++u) {
+            const uint32_t i = threadIdx.x + (uint32_t)u * kShortBlock;
+            v[u] = load_stream(xv + (i < nvec ? i : nvec - 1));
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int u = 0; u < kShortUnroll; u += 2) {
+            const uint32_t i = threadIdx.x + (uint32_t)u * kShortBlock;
+            if (i + kShortBlock < nvec)
+                acc.fold2(v[u], v[u + 1]);
+            else if (i < nvec)
+                acc.fold1(v[u]);
+        }
+    }
+    if (threadIdx.x == 0) {
+        for (uint32_t k = 0; k < head; ++k)
+            acc.fold_scalar(x[k]);
+        for (uint64_t k = head + 4 * (uint64_t)nvec; k < n; ++k)
+            acc.fold_scalar(x[k]);
+    }
+}
+
 // Launch shape of a kernel that streams one vector, one workgroup per CU
-// at most: vectors of at least kRegionalMinBytes on a device whose CU count
+// at most: vectors of at most kShortVecs whole 16-byte vectors run one
+// workgroup of kShortBlock threads (stream_short); vectors of at least
+// kRegionalMinBytes on a device whose CU count
 // is a multiple of kXcds run workgroups of kBlock threads with
 // kStreamUnroll loads in flight, region by region (stream_regions);
 // shorter ones run workgroups of kWideBlock threads with kWideUnroll loads
@@ -297,12 +351,20 @@ static_assert((uint64_t)kWideBlock * kWideUnroll == kSweep, "one sweep per step"
 struct StreamShape {
     unsigned grid = 1;
     bool regional = false;
-    unsigned threads() const { return regional ? (unsigned)kBlock : (unsigned)kWideBlock; }
+    bool one_shot = false; // one workgroup of kShortBlock threads (stream_short)
+    unsigned threads() const
+    {
+        return one_shot ? (unsigned)kShortBlock : regional ? (unsigned)kBlock : (unsigned)kWideBlock;
+    }
 };
 
 inline StreamShape stream_shape(const float* x, uint64_t n, int cus)
 {
     StreamShape sh;
+    if ((n - head_count(x, n)) / 4 <= kShortVecs) {
+        sh.one_shot = true;
+        return sh;
+    }
     const uint64_t sweeps = sweep_count(x, n);
     if (n * sizeof(float) >= kRegionalMinBytes && cus % (int)kXcds == 0 &&
         sweeps >= (uint64_t)cus) {

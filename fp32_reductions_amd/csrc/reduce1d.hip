@@ -138,6 +138,21 @@ __global__ __launch_bounds__(kStreamThreads<REGIONAL>) void reduce1d_stream_kern
     }
 }
 
+// A short vector in one workgroup (stream_short): the whole call, writing
+// *out itself with the old value folded first under accum.
+template <class Op>
+__global__ __launch_bounds__(kShortBlock) void reduce1d_short_kernel(
+    const float* __restrict__ x, uint64_t n, float* __restrict__ out, int accum)
+{
+    constexpr int kW = kShortBlock / kWave;
+    __shared__ float lds[kW];
+    Acc<Op> acc(Op::identity());
+    stream_short(x, n, acc);
+    const float r = red_dev::block_reduce<Op, kW>(acc.collapse(), lds);
+    if (threadIdx.x == 0)
+        *out = accum ? Op::apply(*out, r) : r;
+}
+
 // Second pass, one workgroup: combine the G partials in index order (each
 // thread folds partials t, t + 256, ..., then the workgroup tree), with the
 // old destination in the first slot under accum.  The old value and the
@@ -181,6 +196,25 @@ __global__ __launch_bounds__(kStreamThreads<REGIONAL>) void reduce1d_summaxmin_s
             partials[gridDim.x + blockIdx.x] = r[1];
             partials[2 * gridDim.x + blockIdx.x] = r[2];
         }
+    }
+}
+
+// Fused short vector in one workgroup: each result as the single-operation
+// short kernel computes it.
+__global__ __launch_bounds__(kShortBlock) void reduce1d_summaxmin_short_kernel(
+    const float* __restrict__ x, uint64_t n, float* __restrict__ out, int accum)
+{
+    constexpr int kW = kShortBlock / kWave;
+    __shared__ float lds[3][kW];
+    AccSumMaxMin acc;
+    stream_short(x, n, acc);
+    float r[3];
+    block_reduce_sum_max_min<kW>(acc.sum.collapse(), acc.max.collapse(),
+                                 acc.min.collapse(), lds, r);
+    if (threadIdx.x == 0) {
+        out[0] = accum ? OpSum::apply(out[0], r[0]) : r[0];
+        out[1] = accum ? OpMax::apply(out[1], r[1]) : r[1];
+        out[2] = accum ? OpMin::apply(out[2], r[2]) : r[2];
     }
 }
 
@@ -277,6 +311,25 @@ __global__ __launch_bounds__(kStreamThreads<REGIONAL>) void reduce1d_atomic_kern
     }
 }
 
+// The single-pass variant on a short vector: one workgroup (stream_short)
+// and its one atomic.
+template <class Op>
+__global__ __launch_bounds__(kShortBlock) void reduce1d_atomic_short_kernel(
+    const float* __restrict__ x, uint64_t n, float* __restrict__ out)
+{
+    constexpr int kW = kShortBlock / kWave;
+    __shared__ float lds[kW];
+    Acc<Op> acc(Op::identity());
+    stream_short(x, n, acc);
+    const float r = red_dev::block_reduce<Op, kW>(acc.collapse(), lds);
+    if (threadIdx.x == 0) {
+        if constexpr (__is_same(Op, OpSum))
+            unsafeAtomicAdd(out, r);
+        else
+            atomic_fold_extreme<Op>(out, r);
+    }
+}
+
 __global__ void fill_u32_kernel(unsigned* __restrict__ p, uint64_t count,
                                 unsigned value)
 {
@@ -289,6 +342,10 @@ template <class Op>
 hipError_t launch_det(const float* x, size_t n, float* out, int accum,
                       StreamShape sh, const Workspace& ws, hipStream_t stream)
 {
+    if (sh.one_shot) {
+        reduce1d_short_kernel<Op><<<1, kShortBlock, 0, stream>>>(x, n, out, accum);
+        return hipGetLastError();
+    }
     float* partials = static_cast<float*>(ws.partials);
     const unsigned grid = sh.grid;
     if (sh.regional)
@@ -312,7 +369,9 @@ hipError_t launch_atomic(const float* x, size_t n, float* out, int accum,
         fill_u32_kernel<<<1, 64, 0, stream>>>(
             reinterpret_cast<unsigned*>(out), 1, ident);
     }
-    if (sh.regional)
+    if (sh.one_shot)
+        reduce1d_atomic_short_kernel<Op><<<1, kShortBlock, 0, stream>>>(x, n, out);
+    else if (sh.regional)
         reduce1d_atomic_kernel<Op, true><<<sh.grid, kBlock, 0, stream>>>(x, n, out);
     else
         reduce1d_atomic_kernel<Op, false><<<sh.grid, kWideBlock, 0, stream>>>(x, n, out);
@@ -333,6 +392,10 @@ hipError_t launch_reduce1d_summaxmin(const float* x, size_t n, float* out,
 {
     const StreamShape sh = reduce1d_shape(x, n, dev);
     const unsigned grid = sh.grid;
+    if (sh.one_shot) {
+        reduce1d_summaxmin_short_kernel<<<1, kShortBlock, 0, stream>>>(x, n, out, accum);
+        return hipGetLastError();
+    }
     if ((size_t)grid * 3 * sizeof(float) > ws.partial_bytes)
         return hipErrorInvalidValue;
     float* partials = static_cast<float*>(ws.partials);

@@ -101,8 +101,11 @@ def test_vec1g_atomic(red, orc, vec1g, op):
 # small and ragged lengths, every misalignment
 # ---------------------------------------------------------------------------
 
+# (up to 4 x 8192 + 3 elements, the whole vector is one workgroup's loads in
+# flight at once; the cases straddle that bound at every offset)
 SIZES = (list(range(1, 18)) + [31, 32, 33, 63, 64, 65, 255, 256, 257, 1000,
-                               4095, 4096, 4097, 65537]
+                               4095, 4096, 4097, 8195, 8196, 32767, 32768, 32771,
+                               32772, 32775, 65537]
          + [(1 << 20) + k for k in range(8)])
 
 
@@ -311,7 +314,7 @@ def test_fused_vec1g(red, orc, vec1g):
     check_fused(red, orc, x, xd, False, (0.0, 0.0, 0.0), "vec1g")
 
 
-@pytest.mark.parametrize("n", [1, 3, 7, 8, 9, 33, 257, 4097, (1 << 20) + 5])
+@pytest.mark.parametrize("n", [1, 3, 7, 8, 9, 33, 257, 4097, 32771, 32772, (1 << 20) + 5])
 def test_fused_lengths(red, orc, base, n):
     x, xd = base
     say("fused lengths n=%d" % n)
